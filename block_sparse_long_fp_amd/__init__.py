@@ -1,0 +1,250 @@
+"""Python binding of libfpv2.so: mean-corrected block-sparse causal prefill on MI355X.
+
+Argument marshalling only: every step of the computation runs in the library's
+HIP kernels. PyTorch supplies device memory and the current HIP stream. If the
+library has not been built, importing the compute functions raises at call
+time with a message that says so; there is no fallback path.
+
+Entry points mirror the C ABI in include/fpv2.h:
+  pool_blocks, select_blocks, sparse_prefill, dense_prefill
+plus the convenience ``prefill`` that allocates outputs and runs all three
+stages, and the host-only ``index_shape`` / ``select_workspace_bytes`` /
+``validate``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfpv2.so")
+
+FP_BF16, FP_FP8_E4M3 = 0, 1
+FP_KV_CONTIGUOUS, FP_KV_PAGED = 0, 1
+FP_MAX_SEQS = 128
+FP_MAX_BLOCKS_PER_SEQ = 32768
+
+STATUS_NAMES = {
+    0: "FP_OK", 1: "FP_ERR_NULL", 2: "FP_ERR_SHAPE", 3: "FP_ERR_GQA", 4: "FP_ERR_BLOCK", 5: "FP_ERR_DTYPE",
+    6: "FP_ERR_LAYOUT", 7: "FP_ERR_CAPACITY", 8: "FP_ERR_WORKSPACE", 9: "FP_ERR_ARG", 10: "FP_ERR_UNSUPPORTED",
+    11: "FP_ERR_HIP",
+}
+
+
+class FpError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(code, code)}: {message}")
+        self.code = code
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("cu_seqlens", ctypes.POINTER(ctypes.c_int32)),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("descale_q", ctypes.c_void_p),
+        ("descale_k", ctypes.c_void_p),
+        ("descale_v", ctypes.c_void_p),
+        ("kv_layout", ctypes.c_int32),
+        ("page_table", ctypes.c_void_p),
+        ("page_size", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+    ]
+
+
+class _SelectArgs(ctypes.Structure):
+    _fields_ = [("alpha", ctypes.c_float), ("sel_scale", ctypes.c_float), ("min_sparse_len", ctypes.c_int32)]
+
+
+class _AttnArgs(ctypes.Structure):
+    _fields_ = [("sm_scale", ctypes.c_float), ("mean_correction", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libfpv2.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m block_sparse_long_fp_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(_Problem)
+        vp, i64p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64)
+        L.fp_index_shape.argtypes = [P, i64p, i64p, i64p]
+        L.fp_select_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+        L.fp_validate.argtypes = [P, ctypes.POINTER(_SelectArgs), ctypes.POINTER(_AttnArgs)]
+        L.fp_pool_blocks.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+        L.fp_select_blocks.argtypes = [P, ctypes.POINTER(_SelectArgs), vp, vp, vp, vp, ctypes.c_int64, vp,
+                                       ctypes.c_size_t, vp]
+        L.fp_sparse_prefill.argtypes = [P, ctypes.POINTER(_AttnArgs), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.fp_dense_prefill.argtypes = [P, ctypes.POINTER(_AttnArgs), vp, vp, vp, vp, vp, vp]
+        for f in ("fp_index_shape", "fp_select_workspace_bytes", "fp_validate", "fp_pool_blocks", "fp_select_blocks",
+                  "fp_sparse_prefill", "fp_dense_prefill"):
+            getattr(L, f).restype = ctypes.c_int32
+        L.fp_status_string.argtypes = [ctypes.c_int32]
+        L.fp_status_string.restype = ctypes.c_char_p
+        L.fp_last_error.argtypes = []
+        L.fp_last_error.restype = ctypes.c_char_p
+        L.fp_abi_version.argtypes = []
+        L.fp_abi_version.restype = ctypes.c_int32
+        _lib = L
+    return _lib
+
+
+def _check(code: int):
+    if code != 0:
+        raise FpError(code, lib().fp_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class Problem:
+    """Holds an fp_problem and keeps its host arrays alive."""
+
+    def __init__(self, cu_seqlens: Sequence[int], num_q_heads: int, num_kv_heads: int, block_size: int,
+                 head_dim: int = 128, dtype: int = FP_BF16, descales: Optional[Sequence[torch.Tensor]] = None,
+                 page_table: Optional[torch.Tensor] = None, page_size: int = 0, num_pages: int = 0):
+        cu = [int(x) for x in cu_seqlens]
+        self.cu_seqlens = cu
+        self._cu = (ctypes.c_int32 * len(cu))(*cu)
+        self._keep = []
+        s = _Problem()
+        s.num_seqs = len(cu) - 1
+        s.cu_seqlens = ctypes.cast(self._cu, ctypes.POINTER(ctypes.c_int32))
+        s.num_q_heads, s.num_kv_heads, s.head_dim, s.block_size = num_q_heads, num_kv_heads, head_dim, block_size
+        s.dtype = dtype
+        if descales is not None:
+            self._keep.extend(descales)
+            s.descale_q, s.descale_k, s.descale_v = (t.data_ptr() for t in descales)
+        if page_table is not None:
+            self._keep.append(page_table)
+            s.kv_layout = FP_KV_PAGED
+            s.page_table = page_table.data_ptr()
+            s.page_size = page_size
+            s.max_pages_per_seq = page_table.shape[1]
+            s.num_pages = num_pages
+        else:
+            s.kv_layout = FP_KV_CONTIGUOUS
+        self.s = s
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.s)
+
+
+def index_shape(prob: Problem):
+    rows, nnz, nb = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().fp_index_shape(prob.ref, ctypes.byref(rows), ctypes.byref(nnz), ctypes.byref(nb)))
+    return rows.value, nnz.value, nb.value
+
+
+def select_workspace_bytes(prob: Problem) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().fp_select_workspace_bytes(prob.ref, ctypes.byref(n)))
+    return n.value
+
+
+def select_args(alpha: float, sel_scale: float = 1.0, min_sparse_len: int = 0) -> _SelectArgs:
+    return _SelectArgs(alpha, sel_scale, min_sparse_len)
+
+
+def attn_args(sm_scale: float = 0.0, mean_correction: bool = True) -> _AttnArgs:
+    return _AttnArgs(sm_scale, 1 if mean_correction else 0)
+
+
+def validate(prob: Problem, sel: Optional[_SelectArgs] = None, attn: Optional[_AttnArgs] = None):
+    _check(lib().fp_validate(prob.ref, ctypes.byref(sel) if sel is not None else None,
+                             ctypes.byref(attn) if attn is not None else None))
+
+
+def pool_blocks(prob: Problem, q, k, v, q_bar, k_bar, v_bar, stream=None):
+    _check(lib().fp_pool_blocks(prob.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(q_bar), _ptr(k_bar), _ptr(v_bar),
+                                _stream(stream)))
+
+
+def select_blocks(prob: Problem, sel: _SelectArgs, q_bar, k_bar, row_ptr, col_idx, workspace, stream=None):
+    _check(lib().fp_select_blocks(prob.ref, ctypes.byref(sel), _ptr(q_bar), _ptr(k_bar), _ptr(row_ptr),
+                                  _ptr(col_idx), col_idx.numel(), _ptr(workspace), workspace.numel(),
+                                  _stream(stream)))
+
+
+def sparse_prefill(prob: Problem, attn: _AttnArgs, q, k, v, k_bar, v_bar, row_ptr, col_idx, out, lse=None,
+                   stream=None):
+    _check(lib().fp_sparse_prefill(prob.ref, ctypes.byref(attn), _ptr(q), _ptr(k), _ptr(v), _ptr(k_bar),
+                                   _ptr(v_bar), _ptr(row_ptr), _ptr(col_idx), _ptr(out), _ptr(lse),
+                                   _stream(stream)))
+
+
+def dense_prefill(prob: Problem, attn: _AttnArgs, q, k, v, out, lse=None, stream=None):
+    _check(lib().fp_dense_prefill(prob.ref, ctypes.byref(attn), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                  _stream(stream)))
+
+
+class Buffers:
+    """Device buffers of one prefill problem (allocated with torch)."""
+
+    def __init__(self, prob: Problem, device, head_dim: int = 128):
+        rows, nnz, nb = index_shape(prob)
+        Hkv = prob.s.num_kv_heads
+        T = prob.cu_seqlens[-1]
+        Hq = prob.s.num_q_heads
+        f32 = dict(dtype=torch.float32, device=device)
+        self.q_bar = torch.empty((Hkv, nb, head_dim), **f32)
+        self.k_bar = torch.empty((Hkv, nb, head_dim), **f32)
+        self.v_bar = torch.empty((Hkv, nb, head_dim), **f32)
+        self.row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=device)
+        self.col_idx = torch.empty(max(nnz, 1), dtype=torch.int32, device=device)
+        self.workspace = torch.empty(select_workspace_bytes(prob), dtype=torch.uint8, device=device)
+        self.out = torch.empty((T, Hq, head_dim), dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty((Hq, T), **f32)
+
+
+def run_prefill(prob: Problem, bufs: Buffers, q, k, v, alpha: float, sel_scale: float = 1.0,
+                min_sparse_len: int = 0, sm_scale: float = 0.0, mean_correction: bool = True, stream=None):
+    """All three stages on preallocated buffers (nothing allocated here)."""
+    pool_blocks(prob, q, k, v, bufs.q_bar, bufs.k_bar, bufs.v_bar, stream)
+    select_blocks(prob, select_args(alpha, sel_scale, min_sparse_len), bufs.q_bar, bufs.k_bar, bufs.row_ptr,
+                  bufs.col_idx, bufs.workspace, stream)
+    sparse_prefill(prob, attn_args(sm_scale, mean_correction), q, k, v, bufs.k_bar, bufs.v_bar, bufs.row_ptr,
+                   bufs.col_idx, bufs.out, bufs.lse, stream)
+    return bufs
+
+
+def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: Sequence[int], block_size: int,
+            alpha: float, sel_scale: float = 1.0, min_sparse_len: int = 0, sm_scale: float = 0.0,
+            mean_correction: bool = True, descales: Optional[Sequence[torch.Tensor]] = None,
+            page_table: Optional[torch.Tensor] = None, page_size: int = 0):
+    """Mean-corrected block-sparse causal prefill of a ragged batch.
+
+    q [T, Hq, 128]; k, v [T, Hkv, 128] (contiguous) or page pools
+    [num_pages, page_size, Hkv, 128] with ``page_table`` [R, max_pages]
+    (int32, device). bf16, or float8_e4m3fn with ``descales`` = three
+    one-element fp32 device tensors. Returns a ``Buffers`` with out, lse,
+    row_ptr, col_idx and the pooled statistics.
+    """
+    Hq = q.shape[1]
+    Hkv = k.shape[-2]
+    dtype = FP_FP8_E4M3 if q.dtype == torch.float8_e4m3fn else FP_BF16
+    prob = Problem(cu_seqlens, Hq, Hkv, block_size, q.shape[-1], dtype, descales, page_table, page_size,
+                   k.shape[0] if page_table is not None else 0)
+    bufs = Buffers(prob, q.device, q.shape[-1])
+    return run_prefill(prob, bufs, q, k, v, alpha, sel_scale, min_sparse_len, sm_scale, mean_correction)

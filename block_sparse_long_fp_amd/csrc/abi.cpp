@@ -1,0 +1,305 @@
+// C ABI of libfpv2.so: argument validation, sizing and kernel launches.
+//
+// Every entry point validates on the host first and enqueues nothing on
+// failure; the library never allocates device memory and never synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/fpv2.h"
+#include "launch.h"
+
+using namespace fpv2;
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+fp_status fail(fp_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+fp_status ok() {
+  g_last_error[0] = '\0';
+  return FP_OK;
+}
+
+// Host-side shape facts derived from a validated problem.
+struct Shape {
+  int R;
+  int64_t T;
+  int64_t NB_tot;
+  int64_t pairs;  // sum_r NB_r (NB_r + 1) / 2
+  int nb_max;
+};
+
+fp_status check_problem(const fp_problem* p, Shape* sh) {
+  if (!p) return fail(FP_ERR_NULL, "problem is NULL");
+  if (p->num_seqs < 1 || p->num_seqs > FP_MAX_SEQS)
+    return fail(p->num_seqs < 1 ? FP_ERR_SHAPE : FP_ERR_UNSUPPORTED, "num_seqs=%d outside [1, %d]", p->num_seqs,
+                FP_MAX_SEQS);
+  if (!p->cu_seqlens) return fail(FP_ERR_NULL, "cu_seqlens (host) is NULL");
+  if (p->num_q_heads < 1 || p->num_kv_heads < 1)
+    return fail(FP_ERR_SHAPE, "num_q_heads=%d num_kv_heads=%d must be >= 1", p->num_q_heads, p->num_kv_heads);
+  if (p->num_q_heads % p->num_kv_heads != 0)
+    return fail(FP_ERR_GQA, "num_q_heads=%d is not a multiple of num_kv_heads=%d", p->num_q_heads, p->num_kv_heads);
+  if (p->head_dim != FP_HEAD_DIM) return fail(FP_ERR_UNSUPPORTED, "head_dim=%d (only %d)", p->head_dim, FP_HEAD_DIM);
+  if (p->block_size != 64 && p->block_size != 128)
+    return fail(FP_ERR_BLOCK, "block_size=%d (64 or 128)", p->block_size);
+  if (p->dtype != FP_BF16 && p->dtype != FP_FP8_E4M3) return fail(FP_ERR_DTYPE, "dtype=%d unknown", p->dtype);
+  if (p->dtype == FP_FP8_E4M3 && (!p->descale_q || !p->descale_k || !p->descale_v))
+    return fail(FP_ERR_DTYPE, "FP8 needs descale_q, descale_k and descale_v");
+  if (p->cu_seqlens[0] != 0) return fail(FP_ERR_SHAPE, "cu_seqlens[0]=%d must be 0", p->cu_seqlens[0]);
+  Shape s{};
+  s.R = p->num_seqs;
+  int64_t nb_tot = 0, pairs = 0;
+  int nb_max = 0, len_max = 0;
+  for (int r = 0; r < p->num_seqs; ++r) {
+    const int64_t L = (int64_t)p->cu_seqlens[r + 1] - p->cu_seqlens[r];
+    if (L < 1) return fail(FP_ERR_SHAPE, "request %d has length %lld (cu_seqlens must increase)", r, (long long)L);
+    const int64_t nb = (L + p->block_size - 1) / p->block_size;
+    if (nb > FP_MAX_BLOCKS_PER_SEQ)
+      return fail(FP_ERR_UNSUPPORTED, "request %d has %lld blocks (max %d)", r, (long long)nb, FP_MAX_BLOCKS_PER_SEQ);
+    nb_tot += nb;
+    pairs += nb * (nb + 1) / 2;
+    if (nb > nb_max) nb_max = (int)nb;
+    if (L > len_max) len_max = (int)L;
+  }
+  s.T = p->cu_seqlens[p->num_seqs];
+  if ((int64_t)p->num_kv_heads * pairs > INT32_MAX)
+    return fail(FP_ERR_UNSUPPORTED, "worst-case nnz %lld exceeds int32 CSR offsets",
+                (long long)((int64_t)p->num_kv_heads * pairs));
+  if (s.T * p->num_q_heads > INT32_MAX)
+    return fail(FP_ERR_UNSUPPORTED, "T * num_q_heads = %lld exceeds int32 LSE indexing",
+                (long long)(s.T * p->num_q_heads));
+  if (p->kv_layout == FP_KV_PAGED) {
+    if (!p->page_table) return fail(FP_ERR_NULL, "paged layout needs page_table");
+    if (p->page_size < 1) return fail(FP_ERR_LAYOUT, "page_size=%d must be >= 1", p->page_size);
+    if (p->num_pages < 1) return fail(FP_ERR_LAYOUT, "num_pages=%d must be >= 1", p->num_pages);
+    const int64_t need = ((int64_t)len_max + p->page_size - 1) / p->page_size;
+    if (p->max_pages_per_seq < need)
+      return fail(FP_ERR_LAYOUT, "max_pages_per_seq=%d < %lld pages of the longest request", p->max_pages_per_seq,
+                  (long long)need);
+  } else if (p->kv_layout != FP_KV_CONTIGUOUS) {
+    return fail(FP_ERR_LAYOUT, "kv_layout=%d unknown", p->kv_layout);
+  }
+  s.NB_tot = nb_tot;
+  s.pairs = pairs;
+  s.nb_max = nb_max;
+  if (sh) *sh = s;
+  return FP_OK;
+}
+
+fp_status check_select(const fp_select_args* a) {
+  if (!a) return fail(FP_ERR_NULL, "select args are NULL");
+  if (std::isnan(a->alpha)) return fail(FP_ERR_ARG, "alpha is NaN");
+  if (!std::isfinite(a->sel_scale)) return fail(FP_ERR_ARG, "sel_scale must be finite");
+  if (a->min_sparse_len < 0) return fail(FP_ERR_ARG, "min_sparse_len=%d must be >= 0", a->min_sparse_len);
+  return FP_OK;
+}
+
+fp_status check_attn(const fp_attn_args* a) {
+  if (!a) return fail(FP_ERR_NULL, "attention args are NULL");
+  if (!std::isfinite(a->sm_scale) || a->sm_scale < 0.f) return fail(FP_ERR_ARG, "sm_scale must be finite and >= 0");
+  if (a->mean_correction != 0 && a->mean_correction != 1)
+    return fail(FP_ERR_ARG, "mean_correction=%d must be 0 or 1", a->mean_correction);
+  return FP_OK;
+}
+
+ReqTable make_table(const fp_problem* p, const Shape& s) {
+  ReqTable t{};
+  t.R = s.R;
+  t.nb_max = s.nb_max;
+  t.blk_off[0] = 0;
+  for (int r = 0; r <= s.R; ++r) t.tok_off[r] = p->cu_seqlens[r];
+  for (int r = 0; r < s.R; ++r) {
+    const int L = p->cu_seqlens[r + 1] - p->cu_seqlens[r];
+    t.blk_off[r + 1] = t.blk_off[r] + (L + p->block_size - 1) / p->block_size;
+  }
+  return t;
+}
+
+KVAddr make_kv(const fp_problem* p) {
+  KVAddr a{};
+  a.paged = p->kv_layout == FP_KV_PAGED;
+  a.page_table = a.paged ? p->page_table : nullptr;
+  a.page_size = a.paged ? p->page_size : 1;
+  a.max_pages = a.paged ? p->max_pages_per_seq : 0;
+  return a;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct WsLayout {
+  size_t z, rowmax, counts, total;
+};
+
+WsLayout ws_layout(const fp_problem* p, const Shape& s) {
+  WsLayout w{};
+  const int64_t rows = (int64_t)p->num_kv_heads * s.NB_tot;
+  w.z = 0;
+  w.rowmax = align256((size_t)p->num_kv_heads * s.pairs * sizeof(float));
+  w.counts = w.rowmax + align256((size_t)rows * sizeof(float));
+  w.total = w.counts + align256((size_t)rows * sizeof(int32_t));
+  return w;
+}
+
+fp_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(FP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+int rows_per_wg() { return 256; }
+
+}  // namespace
+
+extern "C" {
+
+fp_status fp_index_shape(const fp_problem* p, int64_t* num_rows, int64_t* max_nnz, int64_t* num_blocks) {
+  Shape s;
+  fp_status st = check_problem(p, &s);
+  if (st) return st;
+  if (num_rows) *num_rows = (int64_t)p->num_kv_heads * s.NB_tot;
+  if (max_nnz) *max_nnz = (int64_t)p->num_kv_heads * s.pairs;
+  if (num_blocks) *num_blocks = s.NB_tot;
+  return ok();
+}
+
+fp_status fp_select_workspace_bytes(const fp_problem* p, size_t* bytes) {
+  Shape s;
+  fp_status st = check_problem(p, &s);
+  if (st) return st;
+  if (!bytes) return fail(FP_ERR_NULL, "bytes is NULL");
+  *bytes = ws_layout(p, s).total;
+  return ok();
+}
+
+fp_status fp_validate(const fp_problem* p, const fp_select_args* sel, const fp_attn_args* attn) {
+  fp_status st = check_problem(p, nullptr);
+  if (st) return st;
+  if (sel && (st = check_select(sel))) return st;
+  if (attn && (st = check_attn(attn))) return st;
+  return ok();
+}
+
+fp_status fp_pool_blocks(const fp_problem* p, const void* q, const void* k, const void* v, float* q_bar,
+                         float* k_bar, float* v_bar, void* stream) {
+  Shape s;
+  fp_status st = check_problem(p, &s);
+  if (st) return st;
+  if (!q || !k || !v || !q_bar || !k_bar || !v_bar) return fail(FP_ERR_NULL, "fp_pool_blocks: NULL buffer");
+  PoolParams pp{};
+  pp.q = q; pp.k = k; pp.v = v;
+  pp.q_bar = q_bar; pp.k_bar = k_bar; pp.v_bar = v_bar;
+  pp.descale_q = p->descale_q; pp.descale_k = p->descale_k; pp.descale_v = p->descale_v;
+  pp.Hq = p->num_q_heads; pp.Hkv = p->num_kv_heads; pp.G = p->num_q_heads / p->num_kv_heads;
+  pp.B = p->block_size; pp.NB_tot = (int32_t)s.NB_tot; pp.fp8 = p->dtype == FP_FP8_E4M3;
+  pp.kv = make_kv(p);
+  pp.rt = make_table(p, s);
+  if (pool_lds_bytes(pp.G) > 64 * 1024) return fail(FP_ERR_UNSUPPORTED, "GQA ratio %d too large for pooling", pp.G);
+  return hip_status(launch_pool(pp, (hipStream_t)stream), "pool launch");
+}
+
+fp_status fp_select_blocks(const fp_problem* p, const fp_select_args* sel, const float* q_bar, const float* k_bar,
+                           int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  Shape s;
+  fp_status st = check_problem(p, &s);
+  if (st) return st;
+  if ((st = check_select(sel))) return st;
+  if (!q_bar || !k_bar || !row_ptr || !col_idx) return fail(FP_ERR_NULL, "fp_select_blocks: NULL buffer");
+  const int64_t max_nnz = (int64_t)p->num_kv_heads * s.pairs;
+  if (col_capacity < max_nnz)
+    return fail(FP_ERR_CAPACITY, "col_capacity=%lld < max_nnz=%lld", (long long)col_capacity, (long long)max_nnz);
+  const WsLayout wl = ws_layout(p, s);
+  if (!workspace || workspace_bytes < wl.total)
+    return fail(FP_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace ? workspace_bytes : (size_t)0,
+                wl.total);
+  SelectParams sp{};
+  sp.q_bar = q_bar; sp.k_bar = k_bar; sp.row_ptr = row_ptr; sp.col_idx = col_idx;
+  char* ws = static_cast<char*>(workspace);
+  sp.zbuf = reinterpret_cast<float*>(ws + wl.z);
+  sp.rowmax = reinterpret_cast<float*>(ws + wl.rowmax);
+  sp.counts = reinterpret_cast<int32_t*>(ws + wl.counts);
+  sp.pairs_tot = s.pairs;
+  sp.sel_scale = sel->sel_scale;
+  sp.all_keep = sel->alpha <= 0.f;
+  sp.log_alpha = sel->alpha > 0.f ? (float)std::log((double)sel->alpha) : 0.f;
+  sp.min_sparse_len = sel->min_sparse_len;
+  sp.Hkv = p->num_kv_heads; sp.NB_tot = (int32_t)s.NB_tot; sp.B = p->block_size;
+  sp.rt = make_table(p, s);
+  return hip_status(launch_select(sp, (hipStream_t)stream), "select launch");
+}
+
+static fp_status run_attention(const fp_problem* p, const fp_attn_args* attn, const void* q, const void* k,
+                               const void* v, const float* k_bar, const float* v_bar, const int32_t* row_ptr,
+                               const int32_t* col_idx, void* out, float* lse, void* stream, bool dense) {
+  Shape s;
+  fp_status st = check_problem(p, &s);
+  if (st) return st;
+  if ((st = check_attn(attn))) return st;
+  if (!q || !k || !v || !out) return fail(FP_ERR_NULL, "attention: NULL q/k/v/out");
+  if (!dense) {
+    if (!row_ptr || !col_idx) return fail(FP_ERR_NULL, "fp_sparse_prefill: NULL CSR");
+    if (attn->mean_correction && (!k_bar || !v_bar))
+      return fail(FP_ERR_NULL, "fp_sparse_prefill: mean correction needs k_bar and v_bar");
+  }
+  AttnParams ap{};
+  ap.q = q; ap.k = k; ap.v = v;
+  ap.k_bar = k_bar; ap.v_bar = v_bar; ap.row_ptr = row_ptr; ap.col_idx = col_idx;
+  ap.out = static_cast<uint16_t*>(out);
+  ap.lse = lse;
+  ap.descale_q = p->descale_q; ap.descale_k = p->descale_k; ap.descale_v = p->descale_v;
+  ap.sm_scale = attn->sm_scale > 0.f ? attn->sm_scale : 1.0f / std::sqrt((float)p->head_dim);
+  ap.Hq = p->num_q_heads; ap.Hkv = p->num_kv_heads; ap.G = p->num_q_heads / p->num_kv_heads;
+  ap.B = p->block_size; ap.NB_tot = (int32_t)s.NB_tot; ap.T = (int32_t)s.T;
+  ap.mean_correction = dense ? 0 : attn->mean_correction;
+  ap.dense = dense ? 1 : 0;
+  ap.subs = (ap.G * ap.B + rows_per_wg() - 1) / rows_per_wg();
+  ap.fp8 = p->dtype == FP_FP8_E4M3;
+  ap.kv = make_kv(p);
+  ap.rt = make_table(p, s);
+  return hip_status(launch_attn(ap, (hipStream_t)stream), dense ? "dense attention launch" : "attention launch");
+}
+
+fp_status fp_sparse_prefill(const fp_problem* p, const fp_attn_args* attn, const void* q, const void* k,
+                            const void* v, const float* k_bar, const float* v_bar, const int32_t* row_ptr,
+                            const int32_t* col_idx, void* out, float* lse, void* stream) {
+  return run_attention(p, attn, q, k, v, k_bar, v_bar, row_ptr, col_idx, out, lse, stream, false);
+}
+
+fp_status fp_dense_prefill(const fp_problem* p, const fp_attn_args* attn, const void* q, const void* k,
+                           const void* v, void* out, float* lse, void* stream) {
+  return run_attention(p, attn, q, k, v, nullptr, nullptr, nullptr, nullptr, out, lse, stream, true);
+}
+
+const char* fp_status_string(fp_status s) {
+  switch (s) {
+    case FP_OK: return "FP_OK";
+    case FP_ERR_NULL: return "FP_ERR_NULL: a required pointer is NULL";
+    case FP_ERR_SHAPE: return "FP_ERR_SHAPE: bad sequence lengths, head counts or sizes";
+    case FP_ERR_GQA: return "FP_ERR_GQA: num_q_heads is not a multiple of num_kv_heads";
+    case FP_ERR_BLOCK: return "FP_ERR_BLOCK: block_size must be 64 or 128";
+    case FP_ERR_DTYPE: return "FP_ERR_DTYPE: unknown dtype or missing FP8 descales";
+    case FP_ERR_LAYOUT: return "FP_ERR_LAYOUT: bad kv_layout or page arguments";
+    case FP_ERR_CAPACITY: return "FP_ERR_CAPACITY: col_idx capacity below worst-case nnz";
+    case FP_ERR_WORKSPACE: return "FP_ERR_WORKSPACE: workspace missing or too small";
+    case FP_ERR_ARG: return "FP_ERR_ARG: bad scalar argument";
+    case FP_ERR_UNSUPPORTED: return "FP_ERR_UNSUPPORTED: outside what this build implements";
+    case FP_ERR_HIP: return "FP_ERR_HIP: HIP runtime error";
+    default: return "unknown fp_status";
+  }
+}
+
+const char* fp_last_error(void) { return g_last_error; }
+
+int32_t fp_abi_version(void) { return FPV2_ABI_VERSION; }
+
+}  // extern "C"

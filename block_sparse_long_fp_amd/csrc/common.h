@@ -1,0 +1,78 @@
+// Shared device-side definitions of the gfx950 block-sparse prefill kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/fpv2.h"
+
+namespace fpv2 {
+
+constexpr int kHeadDim = FP_HEAD_DIM;   // d
+constexpr int kMaxSeqs = FP_MAX_SEQS;
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Ragged batch description, passed by value as a kernel argument. Built on the
+// host from the host-side cu_seqlens, so no device lookup table is needed.
+struct ReqTable {
+  int32_t R;                         // requests
+  int32_t nb_max;                    // max_r NB_r
+  int32_t tok_off[kMaxSeqs + 1];     // cu_seqlens
+  int32_t blk_off[kMaxSeqs + 1];     // prefix sums of NB_r
+};
+
+// K/V addressing: contiguous [T, Hkv, d] or paged [pages, page_size, Hkv, d].
+struct KVAddr {
+  const int32_t* page_table;  // [R, max_pages] (paged only)
+  int32_t page_size;
+  int32_t max_pages;
+  int32_t paged;
+};
+
+// Element offset of (request r, request-local token t, kv head h, dim 0).
+__device__ __forceinline__ int64_t kv_elem_offset(const KVAddr& a, const ReqTable& rt, int r, int t, int h,
+                                                  int Hkv) {
+  int64_t row;
+  if (a.paged) {
+    const int page = a.page_table[(int64_t)r * a.max_pages + t / a.page_size];
+    row = (int64_t)page * a.page_size + (t % a.page_size);
+  } else {
+    row = (int64_t)rt.tok_off[r] + t;
+  }
+  return (row * Hkv + h) * kHeadDim;
+}
+
+// OCP E4M3 (FN) byte -> float, exact. gfx950 uses the OCP encoding.
+__device__ __forceinline__ float e4m3_to_float(uint32_t c) {
+  const uint32_t s = (c & 0x80u) << 24;
+  const uint32_t e = (c >> 3) & 0xFu;
+  const uint32_t m = c & 0x7u;
+  float v;
+  if (e == 0) {
+    v = (float)m * 0.001953125f;  // m/8 * 2^-6
+  } else {
+    v = __uint_as_float(((e + 120u) << 23) | (m << 20));  // (1+m/8) * 2^(e-7)
+  }
+  return __uint_as_float(__float_as_uint(v) | s);
+}
+
+// bf16 <-> float helpers on raw bits.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f32x2 v = {a, b};
+  bf16x2 r = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+}  // namespace fpv2

@@ -1,0 +1,72 @@
+// Host <-> kernel interface of the gfx950 block-sparse prefill library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace fpv2 {
+
+struct PoolParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* q_bar;
+  float* k_bar;
+  float* v_bar;
+  const float* descale_q;
+  const float* descale_k;
+  const float* descale_v;
+  int32_t Hq, Hkv, G, B, NB_tot, fp8;
+  KVAddr kv;
+  ReqTable rt;
+};
+
+struct SelectParams {
+  const float* q_bar;
+  const float* k_bar;
+  int32_t* row_ptr;
+  int32_t* col_idx;
+  float* zbuf;        // workspace: Hkv * pairs_tot floats
+  float* rowmax;      // workspace: rows floats
+  int32_t* counts;    // workspace: rows ints
+  int64_t pairs_tot;  // sum_r NB_r (NB_r + 1) / 2
+  float sel_scale;
+  float log_alpha;    // ln(alpha), fp32
+  int32_t all_keep;   // alpha <= 0
+  int32_t min_sparse_len;
+  int32_t Hkv, NB_tot, B;
+  ReqTable rt;
+};
+
+struct AttnParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* k_bar;
+  const float* v_bar;
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  uint16_t* out;        // bf16 bits
+  float* lse;
+  const float* descale_q;
+  const float* descale_k;
+  const float* descale_v;
+  float sm_scale;
+  int32_t Hq, Hkv, G, B, NB_tot, T;
+  int32_t mean_correction;
+  int32_t dense;        // 1: ignore the CSR, attend to every causal block
+  int32_t subs;         // workgroups per (h, I) row: ceil(G * B / rows_per_wg)
+  int32_t fp8;
+  KVAddr kv;
+  ReqTable rt;
+};
+
+size_t pool_lds_bytes(int G);
+hipError_t launch_pool(const PoolParams& p, hipStream_t stream);
+hipError_t launch_select(const SelectParams& p, hipStream_t stream);
+hipError_t launch_attn(const AttnParams& p, hipStream_t stream);
+
+}  // namespace fpv2

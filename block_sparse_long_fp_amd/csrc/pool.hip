@@ -1,0 +1,145 @@
+// Stage 1a: block-mean pooling of GQA-packed Q, and of K and V.
+//
+// Method: "FlashPrefill V2: Block-Sparse Prefill Attention for Long-Context LLM
+// Serving" (metallab.ai paper digest), Figure 3 (Stage 1 packs the grouped
+// queries and pools block-mean statistics) and Figure 4 (a pruned block is
+// represented by its mean key and mean value).
+//
+// Work split: one workgroup per (block b of the ragged batch, KV head h). Its
+// threads own "slots" (the G query heads of the group, then K, then V) times
+// 16-byte column chunks of the 128-wide head dim, and split the block's tokens
+// into interleaved groups; every load is a 16-byte (bf16) or 8-byte (fp8)
+// vector whose neighbours in the wave read the neighbouring bytes of the same
+// row, so each wave streams whole 128-byte lines. Partial sums meet in LDS in
+// a fixed order (deterministic), are divided by the element count and written
+// as fp32. The kernel is HBM-bound: it reads every input byte once.
+#include "common.h"
+#include "launch.h"
+
+namespace fpv2 {
+
+namespace {
+
+constexpr int kPoolThreads = 256;
+constexpr int kChunks = kHeadDim / 8;  // 8 elements per chunk
+
+template <bool FP8>
+__device__ __forceinline__ void load_chunk(const void* base, int64_t elem, float (&x)[8]) {
+  if constexpr (FP8) {
+    const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(base) + elem);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = e4m3_to_float((w.x >> (8 * i)) & 0xFFu);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[4 + i] = e4m3_to_float((w.y >> (8 * i)) & 0xFFu);
+  } else {
+    const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + elem);
+    x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x);
+    x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+    x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z);
+    x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+  }
+}
+
+template <bool FP8>
+__global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolParams p) {
+  extern __shared__ float part[];  // [groups][slots*kChunks][8]
+  const int b = blockIdx.x;        // global block id in [0, NB_tot)
+  const int h = blockIdx.y;
+  const ReqTable& rt = p.rt;
+  // request of this block: last r with blk_off[r] <= b
+  int r = 0;
+  while (r + 1 < rt.R && rt.blk_off[r + 1] <= b) ++r;
+  const int J = b - rt.blk_off[r];
+  const int L = rt.tok_off[r + 1] - rt.tok_off[r];
+  const int t0 = J * p.B;
+  const int n = min(p.B, L - t0);
+
+  const int G = p.G;
+  const int slots = G + 2;
+  const int tasks = slots * kChunks;
+  const int groups = tasks >= kPoolThreads ? 1 : kPoolThreads / tasks;
+  const int tid = threadIdx.x;
+
+  for (int tk = tid; tk < groups * tasks; tk += kPoolThreads) {
+    const int task = tk % tasks;
+    const int grp = tk / tasks;
+    const int slot = task / kChunks;
+    const int chunk = task % kChunks;
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    if (slot < G) {
+      const int g = h * G + slot;
+      for (int t = grp; t < n; t += groups) {
+        const int64_t e = ((int64_t)(rt.tok_off[r] + t0 + t) * p.Hq + g) * kHeadDim + chunk * 8;
+        float x[8];
+        load_chunk<FP8>(p.q, e, x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += x[i];
+      }
+    } else {
+      const void* src = (slot == G) ? p.k : p.v;
+      for (int t = grp; t < n; t += groups) {
+        const int64_t e = kv_elem_offset(p.kv, rt, r, t0 + t, h, p.Hkv) + chunk * 8;
+        float x[8];
+        load_chunk<FP8>(src, e, x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += x[i];
+      }
+    }
+    float* dst = part + ((int64_t)grp * tasks + task) * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dst[i] = acc[i];
+  }
+  __syncthreads();
+
+  // Reduce: one thread per (output kind, chunk): kind 0 = q_bar, 1 = k_bar, 2 = v_bar.
+  if (tid < 3 * kChunks) {
+    const int kind = tid / kChunks;
+    const int c = tid % kChunks;
+    float s[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s[i] = 0.f;
+    const int s_lo = (kind == 0) ? 0 : (kind == 1 ? G : G + 1);
+    const int s_hi = (kind == 0) ? G : s_lo + 1;
+    for (int sl = s_lo; sl < s_hi; ++sl) {
+      for (int gr = 0; gr < groups; ++gr) {
+        const float* src = part + ((int64_t)gr * tasks + sl * kChunks + c) * 8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s[i] += src[i];
+      }
+    }
+    float scale;
+    if (kind == 0) {
+      scale = 1.0f / (float)(n * G);
+      if (FP8) scale *= *p.descale_q;
+    } else {
+      scale = 1.0f / (float)n;
+      if (FP8) scale *= (kind == 1) ? *p.descale_k : *p.descale_v;
+    }
+    float* out = (kind == 0) ? p.q_bar : (kind == 1 ? p.k_bar : p.v_bar);
+    float4* o4 = reinterpret_cast<float4*>(out + ((int64_t)h * p.NB_tot + b) * kHeadDim + c * 8);
+    o4[0] = make_float4(s[0] * scale, s[1] * scale, s[2] * scale, s[3] * scale);
+    o4[1] = make_float4(s[4] * scale, s[5] * scale, s[6] * scale, s[7] * scale);
+  }
+}
+
+}  // namespace
+
+size_t pool_lds_bytes(int G) {
+  const int tasks = (G + 2) * kChunks;
+  const int groups = tasks >= kPoolThreads ? 1 : kPoolThreads / tasks;
+  return (size_t)groups * tasks * 8 * sizeof(float);
+}
+
+hipError_t launch_pool(const PoolParams& p, hipStream_t stream) {
+  dim3 grid(p.NB_tot, p.Hkv);
+  const size_t lds = pool_lds_bytes(p.G);
+  if (p.fp8)
+    hipLaunchKernelGGL(pool_kernel<true>, grid, dim3(kPoolThreads), lds, stream, p);
+  else
+    hipLaunchKernelGGL(pool_kernel<false>, grid, dim3(kPoolThreads), lds, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace fpv2

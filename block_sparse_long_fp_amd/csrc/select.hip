@@ -1,0 +1,225 @@
+// Stage 1b: block scoring, max-based dynamic threshold and CSR compaction.
+//
+// Method: "FlashPrefill V2: Block-Sparse Prefill Attention for Long-Context LLM
+// Serving" (metallab.ai paper digest): the abstract's max-based dynamic
+// thresholding, Table 9 (alpha sets how many blocks survive) and Table 7 (the
+// index is a CSR of selected blocks per KV head, int32 block ids). The
+// nestfrontier.com article "128K context now demands Hopper hardware", section
+// "A serving setup you can actually test", names the threshold and the minimum
+// sparse query length knobs.
+//
+// Row (h, I) of request r scores every causal key block J <= I with
+// z_J = tau * q_bar[h,I] . k_bar[h,J] (fp32), takes the row max m, and keeps J
+// iff z_J - m >= ln(alpha) (the same as exp(z_J - m) >= alpha), plus J = I.
+//
+// Three kernels, no host round trip:
+//   score_kernel    one workgroup per (KV head, tile of 32 query blocks of one
+//                   request): q_bar tile and 32-row k_bar chunks staged in LDS,
+//                   each thread owns one row and every 8th column, so its
+//                   running max and its keep count need no other thread until
+//                   an 8-lane shuffle reduction. z goes to the workspace so
+//                   the count and the compaction see the same fp32 values.
+//   scan_kernel     one workgroup: exclusive prefix sum of the row counts
+//                   into row_ptr (wave shuffles, then a carry across chunks).
+//   compact_kernel  one wave per row: ballot of the keep flags of 64 columns,
+//                   mbcnt prefix, ascending column ids written at row_ptr.
+#include "common.h"
+#include "launch.h"
+
+namespace fpv2 {
+
+namespace {
+
+constexpr int kTileI = 32;       // query blocks per score workgroup
+constexpr int kTileJ = 32;       // key blocks per LDS chunk
+constexpr int kScoreThreads = 256;
+constexpr int kPad = kHeadDim + 4;
+
+__device__ __forceinline__ int64_t pair_offset(const ReqTable& rt, int r) {
+  int64_t s = 0;
+  for (int i = 0; i < r; ++i) {
+    const int64_t nb = rt.blk_off[i + 1] - rt.blk_off[i];
+    s += nb * (nb + 1) / 2;
+  }
+  return s;
+}
+
+__device__ __forceinline__ bool request_dense(const SelectParams& p, int r) {
+  const int L = p.rt.tok_off[r + 1] - p.rt.tok_off[r];
+  return p.all_keep || L < p.min_sparse_len;
+}
+
+__global__ __launch_bounds__(kScoreThreads) void score_kernel(SelectParams p) {
+  __shared__ float qs[kTileI][kPad];
+  __shared__ float ks[kTileJ][kPad];
+  const ReqTable& rt = p.rt;
+  const int h = blockIdx.y;
+  // Map blockIdx.x to (request, tile): tiles are numbered request by request.
+  int r = 0, tile = blockIdx.x;
+  for (;;) {
+    const int nb = rt.blk_off[r + 1] - rt.blk_off[r];
+    const int nt = (nb + kTileI - 1) / kTileI;
+    if (tile < nt || r + 1 >= rt.R) break;
+    tile -= nt;
+    ++r;
+  }
+  const int NB = rt.blk_off[r + 1] - rt.blk_off[r];
+  const int I0 = tile * kTileI;
+  if (I0 >= NB) return;
+  const int tid = threadIdx.x;
+  const int ti = tid >> 3;   // row within the tile
+  const int jq = tid & 7;    // column phase
+  const int I = I0 + ti;
+  const bool row_ok = I < NB;
+  const int64_t row = (int64_t)h * p.NB_tot + rt.blk_off[r] + I;
+
+  if (request_dense(p, r)) {
+    if (jq == 0 && row_ok) p.counts[row] = I + 1;
+    return;
+  }
+
+  // q_bar tile -> LDS
+  for (int e = tid; e < kTileI * (kHeadDim / 4); e += kScoreThreads) {
+    const int rr = e / (kHeadDim / 4), c4 = e % (kHeadDim / 4);
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (I0 + rr < NB) v = reinterpret_cast<const float4*>(p.q_bar + ((int64_t)h * p.NB_tot + rt.blk_off[r] + I0 + rr) * kHeadDim)[c4];
+    *reinterpret_cast<float4*>(&qs[rr][c4 * 4]) = v;
+  }
+  float* zrow = p.zbuf + (int64_t)h * p.pairs_tot + pair_offset(rt, r) + (int64_t)I * (I + 1) / 2;
+  const int Jend = min(NB, I0 + kTileI);  // exclusive bound of columns any row needs
+  float m = -INFINITY;
+  for (int J0 = 0; J0 < Jend; J0 += kTileJ) {
+    __syncthreads();
+    for (int e = tid; e < kTileJ * (kHeadDim / 4); e += kScoreThreads) {
+      const int rr = e / (kHeadDim / 4), c4 = e % (kHeadDim / 4);
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (J0 + rr < NB) v = reinterpret_cast<const float4*>(p.k_bar + ((int64_t)h * p.NB_tot + rt.blk_off[r] + J0 + rr) * kHeadDim)[c4];
+      *reinterpret_cast<float4*>(&ks[rr][c4 * 4]) = v;
+    }
+    __syncthreads();
+    if (row_ok) {
+#pragma unroll
+      for (int u = 0; u < kTileJ / 8; ++u) {
+        const int jj = jq + 8 * u;
+        const int J = J0 + jj;
+        if (J <= I) {
+          float acc = 0.f;
+#pragma unroll 8
+          for (int c = 0; c < kHeadDim; c += 4) {
+            const float4 a = *reinterpret_cast<const float4*>(&qs[ti][c]);
+            const float4 b = *reinterpret_cast<const float4*>(&ks[jj][c]);
+            acc = fmaf(a.x, b.x, acc);
+            acc = fmaf(a.y, b.y, acc);
+            acc = fmaf(a.z, b.z, acc);
+            acc = fmaf(a.w, b.w, acc);
+          }
+          const float z = p.sel_scale * acc;
+          zrow[J] = z;
+          m = fmaxf(m, z);
+        }
+      }
+    }
+  }
+  // Row max over the 8 threads of the row (lanes 8k .. 8k+7 of one wave).
+  m = fmaxf(m, __shfl_xor(m, 1));
+  m = fmaxf(m, __shfl_xor(m, 2));
+  m = fmaxf(m, __shfl_xor(m, 4));
+  // Count: each thread re-reads the z values it wrote itself.
+  int cnt = 0;
+  if (row_ok) {
+    for (int J = jq; J <= I; J += 8) cnt += ((zrow[J] - m) >= p.log_alpha) || (J == I);
+  }
+  cnt += __shfl_xor(cnt, 1);
+  cnt += __shfl_xor(cnt, 2);
+  cnt += __shfl_xor(cnt, 4);
+  if (row_ok && jq == 0) {
+    p.counts[row] = cnt;
+    p.rowmax[row] = m;
+  }
+}
+
+constexpr int kScanThreads = 1024;
+
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ row_ptr, int64_t rows) {
+  __shared__ int32_t wsum[kScanThreads / 64];
+  __shared__ int32_t carry_s;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (tid == 0) {
+    carry_s = 0;
+    row_ptr[0] = 0;
+  }
+  __syncthreads();
+  for (int64_t base = 0; base < rows; base += kScanThreads) {
+    const int64_t i = base + tid;
+    int32_t x = i < rows ? counts[i] : 0;
+    // inclusive wave scan
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int32_t y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) wsum[w] = x;
+    __syncthreads();
+    int32_t before = 0;
+    for (int k = 0; k < w; ++k) before += wsum[k];
+    const int32_t carry = carry_s;
+    if (i < rows) row_ptr[i + 1] = carry + before + x;
+    __syncthreads();
+    if (tid == kScanThreads - 1) carry_s = carry + before + x;
+    __syncthreads();
+  }
+}
+
+constexpr int kCompactThreads = 256;
+
+__global__ __launch_bounds__(kCompactThreads) void compact_kernel(SelectParams p) {
+  const ReqTable& rt = p.rt;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * (kCompactThreads / 64) + (threadIdx.x >> 6);
+  const int64_t rows = (int64_t)p.Hkv * p.NB_tot;
+  if (row >= rows) return;
+  const int h = (int)(row / p.NB_tot);
+  const int b = (int)(row % p.NB_tot);
+  int r = 0;
+  while (r + 1 < rt.R && rt.blk_off[r + 1] <= b) ++r;
+  const int I = b - rt.blk_off[r];
+  int32_t* out = p.col_idx + p.row_ptr[row];
+  if (request_dense(p, r)) {
+    for (int J = lane; J <= I; J += 64) out[J] = J;
+    return;
+  }
+  const float* zrow = p.zbuf + (int64_t)h * p.pairs_tot + pair_offset(rt, r) + (int64_t)I * (I + 1) / 2;
+  const float m = p.rowmax[row];
+  int base = 0;
+  for (int J0 = 0; J0 <= I; J0 += 64) {
+    const int J = J0 + lane;
+    const bool keep = (J <= I) && (((zrow[J] - m) >= p.log_alpha) || (J == I));
+    const uint64_t mask = __ballot(keep);
+    const int pre = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+    if (keep) out[base + pre] = J;
+    base += __popcll(mask);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_select(const SelectParams& p, hipStream_t stream) {
+  int tiles = 0;
+  for (int r = 0; r < p.rt.R; ++r) {
+    const int nb = p.rt.blk_off[r + 1] - p.rt.blk_off[r];
+    tiles += (nb + kTileI - 1) / kTileI;
+  }
+  hipLaunchKernelGGL(score_kernel, dim3(tiles, p.Hkv), dim3(kScoreThreads), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t rows = (int64_t)p.Hkv * p.NB_tot;
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, p.counts, p.row_ptr, rows);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t wgs = (rows + (kCompactThreads / 64) - 1) / (kCompactThreads / 64);
+  hipLaunchKernelGGL(compact_kernel, dim3((unsigned)wgs), dim3(kCompactThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace fpv2

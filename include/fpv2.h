@@ -1,0 +1,204 @@
+/*
+ * fpv2.h - C ABI of the MI355X (gfx950) mean-corrected block-sparse causal
+ * prefill library (libfpv2.so).
+ *
+ * The method is FlashPrefill V2 as described in "FlashPrefill V2: Block-Sparse
+ * Prefill Attention for Long-Context LLM Serving" (paper digest on
+ * metallab.ai; cited below as [digest]) and in the nestfrontier.com article
+ * "128K context now demands Hopper hardware" (cited as [article]).
+ *
+ * The prefill runs as three calls, in order, on one HIP stream:
+ *   1. fp_pool_blocks     block-mean statistics of Q (GQA-packed), K and V
+ *                         ([digest] Figure 3, Stage 1; Figure 4 means).
+ *   2. fp_select_blocks   max-based dynamic threshold over pooled scores and a
+ *                         CSR index of kept blocks ([digest] abstract,
+ *                         Table 7 "CSR of selected blocks, per KV head").
+ *   3. fp_sparse_prefill  exact online-softmax attention over the kept blocks,
+ *                         with the mean-correction surrogate of every pruned
+ *                         causal block merged into the same softmax
+ *                         ([digest] Figure 3 Stage 2, Figure 4).
+ * fp_dense_prefill is the dense causal comparator built from the same kernels.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Memory:    every buffer is allocated and freed by the caller. Pointers marked
+ *            DEVICE are HIP device pointers; HOST pointers are read during the
+ *            call only. The library never allocates, never synchronises the
+ *            stream and keeps no pointer after returning.
+ * Streams:   `stream` is a hipStream_t passed as void* (NULL = the null
+ *            stream). All device work is enqueued on it, in call order; a call
+ *            returns before the work runs.
+ * Errors:    every call validates its arguments on the host before enqueuing
+ *            anything; on failure it returns a non-zero fp_status, enqueues no
+ *            work and writes no output. fp_last_error() then holds a message
+ *            (per calling thread). A failed kernel launch returns FP_ERR_HIP.
+ * Layouts:   T = total tokens over the ragged batch, Hq / Hkv query / KV
+ *            heads, G = Hq / Hkv, d = head_dim (128), B = block_size.
+ *            Request r holds tokens [cu_seqlens[r], cu_seqlens[r+1]); its
+ *            blocks restart at its token 0: block J covers request-local
+ *            tokens [J*B, min((J+1)*B, L_r)), NB_r = ceil(L_r / B).
+ *            NB_tot = sum_r NB_r; blk_off[r] = sum_{r'<r} NB_r'.
+ *            Q, O:          [T, Hq, d] row-major; query head g uses KV head g / G.
+ *            K, V contiguous: [T, Hkv, d].
+ *            K, V paged:    [num_pages, page_size, Hkv, d]; token t of request r
+ *                           is slot t % page_size of page
+ *                           page_table[r * max_pages_per_seq + t / page_size]
+ *                           ([digest] "What they did", Fix 3; Table 7: paged KV,
+ *                           arbitrary page size).
+ *            pooled q_bar, k_bar, v_bar: fp32 [Hkv, NB_tot, d], row
+ *                           h * NB_tot + blk_off[r] + J.
+ *            CSR:           one row per (h, r, I), row id h * NB_tot + blk_off[r] + I;
+ *                           row_ptr int32 [Hkv * NB_tot + 1]; col_idx int32
+ *                           request-local key-block ids, strictly ascending in a
+ *                           row, the diagonal I always present.
+ *            LSE:           fp32 [Hq, T], natural log of the full softmax
+ *                           denominator (exact terms plus surrogates).
+ *            O:             bf16 for both input dtypes.
+ */
+#ifndef FPV2_H
+#define FPV2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FPV2_ABI_VERSION 1
+
+/* Status codes. */
+typedef int32_t fp_status;
+enum {
+  FP_OK = 0,
+  FP_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  FP_ERR_SHAPE = 2,       /* bad sequence lengths, head counts or sizes          */
+  FP_ERR_GQA = 3,         /* num_q_heads is not a multiple of num_kv_heads       */
+  FP_ERR_BLOCK = 4,       /* block_size is not 64 or 128                         */
+  FP_ERR_DTYPE = 5,       /* unknown dtype, or FP8 without its three descales    */
+  FP_ERR_LAYOUT = 6,      /* unknown kv_layout or inconsistent page arguments    */
+  FP_ERR_CAPACITY = 7,    /* col_idx capacity below the worst-case nnz           */
+  FP_ERR_WORKSPACE = 8,   /* workspace NULL or smaller than fp_select_workspace_bytes */
+  FP_ERR_ARG = 9,         /* bad scalar argument (NaN alpha, sel_scale, sm_scale) */
+  FP_ERR_UNSUPPORTED = 10,/* valid request outside this build (head_dim != 128,  */
+                          /* more than FP_MAX_SEQS requests, too many blocks)    */
+  FP_ERR_HIP = 11         /* a HIP runtime call or kernel launch failed          */
+};
+
+/* Element type of Q, K and V. FP8 is OCP E4M3 (max 448) with one fp32 descale
+ * per tensor: value = code * descale ([digest] "What they did", Fix 2). */
+enum { FP_BF16 = 0, FP_FP8_E4M3 = 1 };
+
+/* K/V storage. */
+enum { FP_KV_CONTIGUOUS = 0, FP_KV_PAGED = 1 };
+
+/* Limits of this build. */
+#define FP_MAX_SEQS 128               /* requests per call                      */
+#define FP_MAX_BLOCKS_PER_SEQ 32768   /* NB_r; 4M tokens at B = 128             */
+#define FP_HEAD_DIM 128
+
+/* Problem description shared by all calls. */
+typedef struct fp_problem {
+  int32_t num_seqs;              /* R, 1 .. FP_MAX_SEQS                           */
+  const int32_t* cu_seqlens;     /* HOST [R+1]; cu_seqlens[0] = 0, each L_r >= 1  */
+  int32_t num_q_heads;           /* Hq >= 1                                        */
+  int32_t num_kv_heads;          /* Hkv >= 1, Hq % Hkv == 0                        */
+  int32_t head_dim;              /* d, must be 128                                 */
+  int32_t block_size;            /* B in {64, 128}: query block = key block        */
+  int32_t dtype;                 /* FP_BF16 or FP_FP8_E4M3                         */
+  const float* descale_q;        /* DEVICE fp32 scalar; required for FP8, else NULL */
+  const float* descale_k;
+  const float* descale_v;
+  int32_t kv_layout;             /* FP_KV_CONTIGUOUS or FP_KV_PAGED                */
+  const int32_t* page_table;     /* DEVICE int32 [R, max_pages_per_seq] (paged)    */
+  int32_t page_size;             /* tokens per page, >= 1 (paged)                  */
+  int32_t max_pages_per_seq;     /* row pitch of page_table, >= ceil(L_r/page_size) */
+  int32_t num_pages;             /* pages in each of the K and V pools (paged)     */
+} fp_problem;
+
+/* Block selection ([digest] abstract: max-based dynamic thresholding;
+ * [article] flags --flashprefill-abs-threshold and -min-sparse-q-len).
+ * Row (h, I) scores z_J = sel_scale * q_bar[h,I] . k_bar[h,J] for J <= I and
+ * keeps J iff exp(z_J - max_J z_J) >= alpha, plus the diagonal J = I. */
+typedef struct fp_select_args {
+  float alpha;                   /* threshold; alpha <= 0 keeps every causal block */
+  float sel_scale;               /* score temperature tau, finite                  */
+  int32_t min_sparse_len;        /* requests with L_r < this keep every causal block */
+} fp_select_args;
+
+/* Attention ([digest] Figures 3-4). */
+typedef struct fp_attn_args {
+  float sm_scale;                /* softmax scale; 0 means 1/sqrt(head_dim)        */
+  int32_t mean_correction;       /* 1: each pruned causal block J < I adds the     */
+                                 /* logit sm*q.k_bar_J + ln n_J on value v_bar_J;  */
+                                 /* 0: pruned blocks are dropped (the ablation)    */
+} fp_attn_args;
+
+/* Host-only queries (no GPU needed). */
+
+/* Sizes of the index: rows = Hkv * NB_tot, max_nnz = Hkv * sum_r NB_r(NB_r+1)/2
+ * (every causal pair), num_blocks = NB_tot. Any output pointer may be NULL. */
+fp_status fp_index_shape(const fp_problem* p, int64_t* num_rows, int64_t* max_nnz,
+                         int64_t* num_blocks);
+
+/* Bytes of DEVICE workspace fp_select_blocks needs for this problem. */
+fp_status fp_select_workspace_bytes(const fp_problem* p, size_t* bytes);
+
+/* Validate a problem and (optionally, may be NULL) selection/attention args
+ * exactly as the compute calls do, without touching any device pointer. */
+fp_status fp_validate(const fp_problem* p, const fp_select_args* sel, const fp_attn_args* attn);
+
+/* Stage 1a: pooled statistics ([digest] Figure 3: PackGQA packing and
+ * block-mean pooling; Figure 4: mean key/value of a block).
+ *   q_bar[h, b] = mean over the G heads of group h and the n_J tokens of block b,
+ *   k_bar[h, b], v_bar[h, b] = mean over the n_J tokens of block b,
+ * each as dequantised values for FP8, accumulated in fp32.
+ * q, k, v: DEVICE inputs in the layouts above (k, v are the page pools when
+ * paged). q_bar, k_bar, v_bar: DEVICE fp32 [Hkv, NB_tot, d] outputs. */
+fp_status fp_pool_blocks(const fp_problem* p, const void* q, const void* k, const void* v,
+                         float* q_bar, float* k_bar, float* v_bar, void* stream);
+
+/* Stage 1b: scoring, threshold and CSR build ([digest] abstract; Table 7).
+ * q_bar, k_bar: DEVICE outputs of fp_pool_blocks. row_ptr: DEVICE int32
+ * [rows+1] output; row_ptr[rows] = nnz. col_idx: DEVICE int32 output with
+ * room for col_capacity entries; col_capacity must be >= max_nnz of
+ * fp_index_shape (checked before launch, so the kernels cannot overflow).
+ * workspace: DEVICE scratch of at least fp_select_workspace_bytes bytes; its
+ * contents on entry do not matter and are garbage on exit. Decisions are taken
+ * in fp32 as (z_J - max) >= ln(alpha). */
+fp_status fp_select_blocks(const fp_problem* p, const fp_select_args* sel, const float* q_bar,
+                           const float* k_bar, int32_t* row_ptr, int32_t* col_idx,
+                           int64_t col_capacity, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* Stage 2: block-sparse attention with the fused mean correction ([digest]
+ * Figure 3 Stage 2: exact path over CSR blocks and correction path merged in
+ * one online softmax; Figure 4 surrogate |B_J| exp(s_J) (v_bar_J, 1)).
+ * k_bar, v_bar: DEVICE fp32 from fp_pool_blocks (read only when
+ * mean_correction = 1). row_ptr, col_idx: DEVICE CSR from fp_select_blocks
+ * (or any CSR of the same shape with the diagonal in every row).
+ * out: DEVICE bf16 [T, Hq, d]. lse: DEVICE fp32 [Hq, T], or NULL to skip. */
+fp_status fp_sparse_prefill(const fp_problem* p, const fp_attn_args* attn, const void* q,
+                            const void* k, const void* v, const float* k_bar, const float* v_bar,
+                            const int32_t* row_ptr, const int32_t* col_idx, void* out, float* lse,
+                            void* stream);
+
+/* Dense causal attention over every key j <= i of the request (the comparator
+ * for the sparse path; mean_correction is ignored). Same layouts as above. */
+fp_status fp_dense_prefill(const fp_problem* p, const fp_attn_args* attn, const void* q,
+                           const void* k, const void* v, void* out, float* lse, void* stream);
+
+/* Static text for a status code; never NULL. */
+const char* fp_status_string(fp_status s);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char* fp_last_error(void);
+
+/* FPV2_ABI_VERSION of the built library. */
+int32_t fp_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FPV2_H */

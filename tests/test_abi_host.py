@@ -1,0 +1,139 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared
+symbol, and rejects bad arguments before touching any device pointer.
+
+None of these calls launch a kernel, so they run without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_long_fp_amd as fp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fpv2.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(fp.LIB_PATH), reason="libfpv2.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(fp_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"fp_pool_blocks", "fp_select_blocks", "fp_sparse_prefill", "fp_dense_prefill"} <= set(names)
+    L = ctypes.CDLL(fp.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    assert fp.lib().fp_abi_version() == 1
+
+
+def _prob(**kw):
+    base = dict(cu_seqlens=[0, 1000, 3000], num_q_heads=32, num_kv_heads=8, block_size=128)
+    base.update(kw)
+    return fp.Problem(**base)
+
+
+def test_index_shape_and_workspace():
+    p = _prob()
+    rows, nnz, nb = fp.index_shape(p)
+    nbs = [8, 16]
+    assert nb == 24 and rows == 8 * 24
+    assert nnz == 8 * sum(n * (n + 1) // 2 for n in nbs)
+    ws = fp.select_workspace_bytes(p)
+    assert ws >= 4 * (nnz + 2 * rows)
+
+
+def test_index_memory_matches_the_pages_order_of_magnitude():
+    # Table 7 of the digest: at 128K with 32 query / 4 KV heads the CSR of
+    # selected blocks takes about 6 MB at ~5% density, against 32 MB for a
+    # dense per-query-head byte mask of 128-token tiles. Our worst case (every
+    # causal block of 128 tokens, per KV head) times the density gives the
+    # same order: 4 * 1024*1025/2 * 0.05 * 4 B ~ 0.4 MB, far under the mask.
+    p = _prob(cu_seqlens=[0, 131072], num_q_heads=32, num_kv_heads=4, block_size=128)
+    rows, nnz, nb = fp.index_shape(p)
+    mask_bytes = 32 * 1024 * 1024
+    assert mask_bytes == 32 * 2 ** 20
+    assert nnz * 4 * 0.05 < 6e6 < mask_bytes
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(num_kv_heads=5), 3),
+    (dict(block_size=96), 4),
+    (dict(head_dim=64), 10),
+    (dict(cu_seqlens=[0, 10, 5]), 2),
+    (dict(cu_seqlens=[1, 10]), 2),
+    (dict(cu_seqlens=[0] + list(range(1, 130))), 10),
+    (dict(dtype=1), 5),
+    (dict(dtype=7), 5),
+    (dict(num_q_heads=0), 2),
+])
+def test_problem_validation(kw, code):
+    with pytest.raises(fp.FpError) as e:
+        fp.validate(_prob(**kw))
+    assert e.value.code == code
+    assert fp.lib().fp_last_error().decode()
+
+
+def test_paged_validation():
+    class FakeTensor:
+        def __init__(self, shape):
+            self.shape = shape
+
+        def data_ptr(self):
+            return 0x1000
+
+    p = fp.Problem([0, 1000], 8, 2, 128, page_table=FakeTensor((1, 10)), page_size=64, num_pages=100)
+    with pytest.raises(fp.FpError) as e:
+        fp.validate(p)  # 1000 tokens need 16 pages of 64, table has 10
+    assert e.value.code == 6
+    p = fp.Problem([0, 1000], 8, 2, 128, page_table=FakeTensor((1, 16)), page_size=0, num_pages=100)
+    with pytest.raises(fp.FpError) as e:
+        fp.validate(p)
+    assert e.value.code == 6
+    fp.validate(fp.Problem([0, 1000], 8, 2, 128, page_table=FakeTensor((1, 16)), page_size=64, num_pages=100))
+
+
+def test_argument_validation():
+    p = _prob()
+    with pytest.raises(fp.FpError) as e:
+        fp.validate(p, fp.select_args(float("nan")))
+    assert e.value.code == 9
+    with pytest.raises(fp.FpError) as e:
+        fp.validate(p, fp.select_args(0.3, float("inf")))
+    assert e.value.code == 9
+    with pytest.raises(fp.FpError) as e:
+        fp.validate(p, None, fp.attn_args(-1.0))
+    assert e.value.code == 9
+    with pytest.raises(fp.FpError) as e:
+        fp.validate(p, None, fp._AttnArgs(0.1, 2))
+    assert e.value.code == 9
+    fp.validate(p, fp.select_args(0.3), fp.attn_args())
+    fp.validate(p, fp.select_args(-1.0), fp.attn_args(0.0, False))
+
+
+def test_compute_calls_reject_before_launch():
+    """Null buffers, small capacity and small workspace fail on the host."""
+    p = _prob()
+    L = fp.lib()
+    sel = fp.select_args(0.3)
+    attn = fp.attn_args()
+    vp = ctypes.c_void_p
+    fake = vp(0x1000)
+    assert L.fp_pool_blocks(p.ref, None, fake, fake, fake, fake, fake, None) == 1
+    rows, nnz, nb = fp.index_shape(p)
+    ws = fp.select_workspace_bytes(p)
+    assert L.fp_select_blocks(p.ref, ctypes.byref(sel), fake, fake, fake, fake, nnz - 1, fake, ws, None) == 7
+    assert L.fp_select_blocks(p.ref, ctypes.byref(sel), fake, fake, fake, fake, nnz, fake, ws - 1, None) == 8
+    assert L.fp_select_blocks(p.ref, ctypes.byref(sel), fake, fake, fake, fake, nnz, None, ws, None) == 8
+    assert L.fp_sparse_prefill(p.ref, ctypes.byref(attn), fake, fake, fake, None, fake, fake, fake, fake, None,
+                               None) == 1
+    assert L.fp_sparse_prefill(p.ref, ctypes.byref(attn), fake, fake, fake, fake, fake, None, fake, fake, None,
+                               None) == 1
+    assert L.fp_dense_prefill(p.ref, ctypes.byref(attn), fake, fake, fake, None, None, None) == 1
+    for code in range(12):
+        assert L.fp_status_string(code)

@@ -1,0 +1,139 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Sizes are small enough for the oracle to finish in seconds, yet span several
+key blocks, several workgroups per (KV head, query block) and ragged tails.
+Bar: bit-exact CSR outside the near-threshold band; O max-abs <= 2e-2 (bf16)
+or 6e-2 (fp8); LSE |error| <= 1e-3 * max(1, |LSE|).
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_common import (O_TOL, compare_csr, compare_outputs, compare_pooled, run_gpu, run_oracle,
+                        sets_from_csr, host_values)
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_full(wl, alpha=None, mean_correction=True, paged=None, min_sparse_len=None):
+    print(f"[parity] {wl.name} L={wl.seqlens} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} B={wl.block_size} "
+          f"dtype={wl.dtype} alpha={alpha if alpha is not None else wl.alpha} mc={mean_correction} "
+          f"paged={paged if paged is not None else wl.paged}", flush=True)
+    gpu = run_gpu(wl, alpha, mean_correction, paged, min_sparse_len=min_sparse_len)
+    orc = run_oracle(wl, alpha, mean_correction, do_attend=False, paged=paged, min_sparse_len=min_sparse_len)
+    compare_pooled(gpu, orc)
+    n_near = compare_csr(gpu, orc)
+    # Attention on the CSR the GPU chose (identical to the oracle's outside the band).
+    Q, K, V = host_values(wl)
+    sets = sets_from_csr(gpu["row_ptr"], gpu["col_idx"], orc.blk_off, wl.num_kv_heads)
+    O = np.full_like(Q, np.nan)
+    LSE = np.full((wl.num_q_heads, Q.shape[0]), np.nan)
+    import math
+    G = wl.num_q_heads // wl.num_kv_heads
+    for r in range(len(wl.seqlens)):
+        s, e = wl.cu_seqlens[r], wl.cu_seqlens[r + 1]
+        a, b = orc.blk_off[r], orc.blk_off[r + 1]
+        o, l = oracle.attend(Q[s:e], K[s:e], V[s:e], orc.kbar[:, a:b], orc.vbar[:, a:b], sets[r], wl.block_size, G,
+                             1.0 / math.sqrt(wl.head_dim), mean_correction)
+        O[s:e], LSE[:, s:e] = o, l
+    o_err, l_err = compare_outputs(gpu["out"], gpu["lse"], O, LSE, O_TOL[wl.dtype])
+    print(f"[parity] ok: nnz={gpu['row_ptr'][-1]} near_rows={n_near} O_err={o_err:.2e} LSE_err={l_err:.2e}",
+          flush=True)
+    return gpu
+
+
+def test_tiny_needle_full():
+    _check_full(synth.make_workload("tiny_4k"))
+
+
+def test_gqa4_block128_ragged():
+    wl = synth.make_workload("llama_32k", L=3000, Hq=8, Hkv=2, n_planted=6)
+    _check_full(wl)
+
+
+def test_gqa8_block64_ragged():
+    wl = synth.make_workload("llama_32k", L=2500, Hq=16, Hkv=2, B=64, n_planted=8, alpha=0.4)
+    _check_full(wl)
+
+
+def test_gqa1_block128():
+    wl = synth.make_workload("llama_32k", L=1500, Hq=2, Hkv=2, n_planted=3)
+    _check_full(wl)
+
+
+def test_mean_correction_off():
+    wl = synth.make_workload("llama_32k", L=2200, Hq=8, Hkv=2, n_planted=5)
+    _check_full(wl, mean_correction=False)
+
+
+def test_fp8_gqa8():
+    wl = synth.make_workload("qwen30b_128k_fp8", L=3000, Hq=16, Hkv=2, n_planted=6)
+    _check_full(wl)
+
+
+def test_varlen_paged_min_sparse_len():
+    wl = synth.make_workload("qwen4b_varlen_paged", lengths=[300, 1000, 2100, 129], Hq=8, Hkv=2,
+                             min_sparse_len=1000, page_size=64)
+    _check_full(wl)
+
+
+def test_varlen_paged_odd_page_size():
+    wl = synth.make_workload("qwen4b_varlen_paged", lengths=[700, 1333], Hq=4, Hkv=1, min_sparse_len=0,
+                             page_size=48, n_planted=3)
+    _check_full(wl)
+
+
+def test_paged_equals_contiguous_bitwise():
+    wl = synth.make_workload("qwen4b_varlen_paged", lengths=[900, 1700], Hq=8, Hkv=2, min_sparse_len=0,
+                             page_size=64, n_planted=4)
+    a = run_gpu(wl, paged=True)
+    b = run_gpu(wl, paged=False)
+    for key in ("q_bar", "k_bar", "v_bar", "row_ptr", "col_idx", "out", "lse"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+def test_alpha_zero_sparse_equals_dense_kernel_and_oracle():
+    wl = synth.make_workload("llama_32k", L=1800, Hq=8, Hkv=2, n_planted=4)
+    sp = run_gpu(wl, alpha=0.0)
+    dn = run_gpu(wl, dense=True)
+    nb = -(-1800 // 128)
+    assert sp["row_ptr"][-1] == 2 * nb * (nb + 1) // 2
+    assert np.array_equal(sp["out"], dn["out"]) and np.array_equal(sp["lse"], dn["lse"])
+    orc = run_oracle(wl, alpha=0.0)
+    compare_outputs(dn["out"], dn["lse"], orc.O, orc.LSE, O_TOL["bf16"])
+
+
+def test_dense_kernel_fp8_and_varlen():
+    wl = synth.make_workload("qwen30b_128k_fp8", L=1300, Hq=8, Hkv=1, n_planted=3)
+    dn = run_gpu(wl, dense=True)
+    orc = run_oracle(wl, alpha=0.0)
+    compare_outputs(dn["out"], dn["lse"], orc.O, orc.LSE, O_TOL["fp8"])
+    wl = synth.make_workload("qwen4b_varlen_paged", lengths=[200, 640, 1000], Hq=4, Hkv=2, page_size=64,
+                             min_sparse_len=0)
+    dn = run_gpu(wl, dense=True)
+    orc = run_oracle(wl, alpha=0.0)
+    compare_outputs(dn["out"], dn["lse"], orc.O, orc.LSE, O_TOL["bf16"])
+
+
+def test_alpha_above_one_keeps_only_diagonal():
+    wl = synth.make_workload("llama_32k", L=1200, Hq=4, Hkv=1, n_planted=3)
+    gpu = _check_full(wl, alpha=1.5)
+    nb = -(-1200 // 128)
+    assert gpu["row_ptr"][-1] == nb
+    assert np.array_equal(gpu["col_idx"], np.arange(nb))
+
+
+def test_single_token_and_one_block_requests():
+    wl = synth.make_workload("qwen4b_varlen_paged", lengths=[1, 2, 127, 128, 129], Hq=4, Hkv=2, page_size=16,
+                             min_sparse_len=0, n_planted=0)
+    _check_full(wl)
+
+
+def test_runs_are_bitwise_deterministic():
+    wl = synth.make_workload("llama_32k", L=2600, Hq=8, Hkv=2, n_planted=6)
+    a = run_gpu(wl)
+    b = run_gpu(wl)
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key
