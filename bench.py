@@ -37,7 +37,23 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=6, help="attention rows the CPU baseline computes")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_probe():
+    """A plain device-to-device copy of exactly 1 GiB, three times: the reference
+    dispatch for scaling FETCH_SIZE / WRITE_SIZE counter readings."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "dispatches": 3}), flush=True)
 
 
 def csr_work(row_ptr, col_idx, wl, blk_off):
@@ -71,8 +87,7 @@ def csr_work(row_ptr, col_idx, wl, blk_off):
                 flops += 4 * d * G * float((pruned * nI).sum())
                 strict += 4 * d * G * float((pruned * nI).sum())
             pairs += nb * (nb + 1) // 2
-    kept = float(row_ptr[-1]) / float(pairs * 1.0 / 1.0) / 1.0
-    kept = float(row_ptr[-1]) / float(pairs * 1)
+    kept = float(row_ptr[-1]) / float(pairs)
     return flops, strict, kept
 
 
@@ -135,6 +150,9 @@ def cpu_baseline(wl, row_ptr, n_rows, seed=0):
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the kernels shard by KV head "
               f"with no exchange, so a multi-GPU figure would be N independent copies of this one.",

@@ -7,31 +7,41 @@
 //             path; both streams merge inside one online softmax.
 //   Figure 4  a pruned block J contributes |B_J| exp(s_J) (v_bar_J, 1): here
 //             the logit sm * q_i . k_bar_J + ln n_J on value v_bar_J.
-//   Fig. 1 / "What they did"  PackGQA: the G query heads of one KV head are
-//             packed into one tile so each K/V tile is fetched once for them.
+//   Figure 1 and "What they did"  PackGQA: the G query heads of one KV head
+//             are packed into one tile so each K/V tile is fetched once for
+//             them.
 //
 // gfx950 design (not a translation of the pages' Hopper kernel):
-//   * One workgroup = 8 waves = 256 packed query rows of one (KV head h, query
-//     block I): wave w owns 32 consecutive tokens of one query head. G*B rows
-//     per (h, I) are split over ceil(G*B/256) workgroups.
+//   * One workgroup = 8 waves (two per SIMD) = 256 packed query rows of one
+//     (KV head h, query block I): wave w owns 32 consecutive tokens of one
+//     query head. G*B rows per (h, I) are split over ceil(G*B/256) workgroups.
 //   * Transposed products keep every lane on one query: S^T = K Q^T and
 //     O^T = V^T P^T with v_mfma_f32_32x32x16_bf16. A lane (column c, half hf)
-//     then holds 64 scores and 64 output dims of query c, so the row max and
-//     row sum are in-lane plus one exchange with lane c+32, and the softmax
-//     probabilities feed the PV product straight from registers (the PV
-//     contraction index is relabelled to match the score accumulator layout,
-//     and V^T is read from LDS with the same relabelling).
-//   * K is staged in LDS row-major [key][d] (pitch 136 elements); V is staged
-//     transposed [d][key] (pitch B+4) so the PV operand is two 8-byte reads.
-//     The next selected block's K/V is loaded into registers while the
-//     current block computes.
-//   * Online softmax in base 2 with the scale folded into one multiply; the
-//     output rescale is skipped when no lane's running max moved.
-//   * The correction path stages B pooled keys/values at a time (fp32 ->
-//     bf16) and masks selected or non-causal columns through a per-column bias
-//     (log2 n_J or -inf) built from an LDS bitmap of the row's CSR entries.
+//     holds the scores and output dims of query c, so row max and row sum are
+//     in-lane plus one exchange with lane c+32, and the probabilities feed the
+//     PV product straight from registers (the PV contraction index is
+//     relabelled to match the score accumulator layout; V^T is read from LDS
+//     with the same relabelling).
+//   * Work items: the CSR row's key blocks (B keys), then correction chunks of
+//     64 pooled columns whose per-column bias log2(n_J) or -inf masks selected
+//     and non-causal blocks (from an LDS bitmap of the row). Every item
+//     reaches LDS as bf16 K rows and bf16 V^T columns, so the MFMA code has
+//     one path.
+//   * Staging: the next item's K and V pass through 32 registers per thread
+//     (loaded before the current item is computed, stored after it) into
+//     double-buffered LDS, with one workgroup barrier per item. K is
+//     row-major with a 272-byte pitch, V^T has a (B+4)-element pitch: MFMA
+//     operand reads of consecutive rows are bank-conflict free and use
+//     base + immediate addresses. Stores are mapped key-group-fastest so each
+//     32-lane pass writes one contiguous row segment (no conflicts).
+//   * Wave-uniform quantities live in scalar registers, so per-item and
+//     per-tile decisions are scalar branches.
+//   * Online softmax in base 2: max on raw scores, one fma + exp2 per score,
+//     fp32 row sums. The running max only moves when a block's max exceeds it
+//     by more than 8 (probabilities stay below 256, exact after the final
+//     division), which makes output rescales rare.
 //   * Workgroups run heaviest first (query block index descending over the
-//     ragged batch), and consecutive ids cycle over KV heads so that the
+//     ragged batch), and consecutive ids cycle over KV heads so the
 //     round-robin XCD dispatch keeps one KV head's blocks in one XCD's L2.
 #include "common.h"
 #include "launch.h"
@@ -43,18 +53,22 @@ namespace {
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kRowsPerWG = kWaves * 32;
-constexpr int kKPitch = kHeadDim + 8;  // bf16 elements per K row in LDS
+constexpr int kPC = 64;                 // pooled columns per correction item
+constexpr int kKPitch = kHeadDim + 8;   // bf16 elements per K row in LDS (272 B)
+constexpr int kColCache = 1024;         // CSR columns cached in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegBig = -1.0e30f;
+constexpr float kSlack = 8.0f;          // lazy-rescale threshold of the running max (log2)
 
 template <int BLK>
-struct Smem {
+struct Lds {
   static constexpr int kVPitch = BLK + 4;  // bf16 elements per V^T row
-  uint16_t k[BLK * kKPitch];
-  uint16_t vt[kHeadDim * kVPitch];
-  float bias[BLK];
+  uint16_t k[2][BLK * kKPitch];
+  uint16_t vt[2][kHeadDim * kVPitch];
+  float bias[2][kPC];
   uint32_t selbits[FP_MAX_BLOCKS_PER_SEQ / 32];
+  int32_t colcache[kColCache];
 };
 
 // Load 8 consecutive elements (bf16 or fp8) as 8 bf16 in a uint4.
@@ -73,181 +87,224 @@ __device__ __forceinline__ uint4 load8_as_bf16(const void* base, int64_t elem) {
   }
 }
 
-// Register-staged copy of one key block (K rows and V rows) on its way to LDS.
-template <int BLK>
-struct KVStage {
-  static constexpr int kKChunks = BLK * (kHeadDim / 8) / kThreads;  // 16-byte chunks of K per thread
-  static constexpr int kVTasks = (BLK / 4) * (kHeadDim / 8);        // 4 keys x 8 dims per task
-  uint4 k[kKChunks];
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Per-workgroup constants of the row being processed (all wave-uniform).
+struct RowCtx {
+  int r, I, h, L;
+  int n_exact;          // CSR entries (key blocks) of the row
+  int n_items;          // plus the correction chunks
+  const int32_t* cols;  // CSR row (nullptr in dense mode)
+  const int32_t* ccols; // first kColCache CSR columns, copied to LDS
+  int64_t pooled_base;  // element offset of the k_bar/v_bar row (h, blk_off[r])
+  int64_t tok_base;     // first token of the request
+  float kscale;         // pooled k_bar -> LDS scale (1/descale_k for FP8)
+  float vscale;         // pooled v_bar -> LDS scale (1/descale_v for FP8)
+};
+
+__device__ __forceinline__ int exact_block(const RowCtx& rc, int e) {
+  return !rc.cols ? e : uniform(e < kColCache ? rc.ccols[e] : rc.cols[e]);
+}
+
+// Element offset of key `row` of block J (request-local token J*B+row, clamped
+// to the request's last token) of the row's KV head.
+template <int BLK, bool PAGED>
+__device__ __forceinline__ int64_t kv_off(const AttnParams& p, const RowCtx& rc, int J, int row) {
+  const int rr = min(row, rc.L - 1 - J * BLK);
+  if constexpr (!PAGED) {
+    const int64_t base = ((rc.tok_base + (int64_t)J * BLK) * p.Hkv + rc.h) * kHeadDim;
+    return base + (int64_t)(rr * (p.Hkv * kHeadDim));
+  } else {
+    const int t = J * BLK + rr;
+    const int page = p.kv.page_table[(int64_t)rc.r * p.kv.max_pages + t / p.kv.page_size];
+    return (((int64_t)page * p.kv.page_size + (t % p.kv.page_size)) * p.Hkv + rc.h) * kHeadDim;
+  }
+}
+
+// Registers carrying one item from HBM to LDS (8 x 16 bytes per thread):
+//   exact K  (B=128): rows tid/16 + 32u, dims 8(tid%16).. (u < 4, bf16)
+//   exact V  (B=128): keys 4kg..4kg+3 (kg = tid%32), dims 8(tid/32).. (bf16)
+//   pooled K: rows tid/16 + 32u (u < 2), dims 8(tid%16).. (fp32, 2 words each)
+//   pooled V: columns 2kg, 2kg+1 (kg = tid%32), dims 8(tid/32).. (fp32)
+// (B=64 uses the first half of the exact entries: 2 K rows, 256 V tasks.)
+struct Stage {
+  uint4 k[4];
   uint4 v[4];
 };
 
-template <int BLK, bool FP8>
-__device__ __forceinline__ void kv_load(KVStage<BLK>& st, const AttnParams& p, int r, int J, int h, int L) {
-  const int tid = threadIdx.x;
+template <int BLK, bool FP8, bool PAGED>
+__device__ __forceinline__ void load_item(Stage& st, const AttnParams& p, const RowCtx& rc, int e, int tid) {
+  if (e < rc.n_exact) {
+    const int J = exact_block(rc, e);
+    constexpr int kKC = BLK * (kHeadDim / 8) / kThreads;  // 4 (B=128) or 2 (B=64)
 #pragma unroll
-  for (int u = 0; u < KVStage<BLK>::kKChunks; ++u) {
-    const int ci = tid + u * kThreads;
-    const int kk = ci >> 4, dc = ci & 15;
-    const int t = J * BLK + kk;
-    if ((unsigned)t < (unsigned)L) st.k[u] = load8_as_bf16<FP8>(p.k, kv_elem_offset(p.kv, p.rt, r, t, h, p.Hkv) + dc * 8);
-    else st.k[u] = make_uint4(0, 0, 0, 0);
-  }
-  if (tid < KVStage<BLK>::kVTasks) {
-    const int dc = tid & 15, kg = tid >> 4;
+    for (int u = 0; u < kKC; ++u)
+      st.k[u] = load8_as_bf16<FP8>(p.k, kv_off<BLK, PAGED>(p, rc, J, (tid >> 4) + 32 * u) + (tid & 15) * 8);
+    constexpr int KG = BLK / 4;
+    if (tid < KG * (kHeadDim / 8)) {
+      const int kg = tid % KG, dc = tid / KG;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = J * BLK + kg * 4 + i;
-      if ((unsigned)t < (unsigned)L) st.v[i] = load8_as_bf16<FP8>(p.v, kv_elem_offset(p.kv, p.rt, r, t, h, p.Hkv) + dc * 8);
-      else st.v[i] = make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < 4; ++i) st.v[i] = load8_as_bf16<FP8>(p.v, kv_off<BLK, PAGED>(p, rc, J, kg * 4 + i) + dc * 8);
+    }
+  } else {
+    const int c0 = (e - rc.n_exact) * kPC;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int Jp = min(c0 + (tid >> 4) + 32 * u, rc.I - 1);
+      const uint4* src = reinterpret_cast<const uint4*>(p.k_bar + rc.pooled_base + (int64_t)Jp * kHeadDim + (tid & 15) * 8);
+      st.k[2 * u] = src[0];
+      st.k[2 * u + 1] = src[1];
+    }
+    const int kg = tid & 31, dc = tid >> 5;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int Jp = min(c0 + kg * 2 + i, rc.I - 1);
+      const uint4* src = reinterpret_cast<const uint4*>(p.v_bar + rc.pooled_base + (int64_t)Jp * kHeadDim + dc * 8);
+      st.v[2 * i] = src[0];
+      st.v[2 * i + 1] = src[1];
     }
   }
 }
 
-// Write 4 keys x 8 dims (v[i] = 8 dims of key i) transposed into V^T.
-template <int BLK>
-__device__ __forceinline__ void vt_store4x8(Smem<BLK>& sm, int kg, int dc, const uint4 (&v)[4]) {
-  const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&v[0]);
-  const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&v[1]);
-  const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&v[2]);
-  const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&v[3]);
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    // dims 8dc+2m (low halves) and 8dc+2m+1 (high halves)
-    uint2 lo, hi;
-    lo.x = __builtin_amdgcn_perm(w1[m], w0[m], 0x05040100u);  // (k0.lo, k1.lo)
-    lo.y = __builtin_amdgcn_perm(w3[m], w2[m], 0x05040100u);  // (k2.lo, k3.lo)
-    hi.x = __builtin_amdgcn_perm(w1[m], w0[m], 0x07060302u);  // (k0.hi, k1.hi)
-    hi.y = __builtin_amdgcn_perm(w3[m], w2[m], 0x07060302u);
-    *reinterpret_cast<uint2*>(&sm.vt[(dc * 8 + 2 * m) * Smem<BLK>::kVPitch + kg * 4]) = lo;
-    *reinterpret_cast<uint2*>(&sm.vt[(dc * 8 + 2 * m + 1) * Smem<BLK>::kVPitch + kg * 4]) = hi;
-  }
+__device__ __forceinline__ uint4 cvt8(const uint4 a4, const uint4 b4, float s) {
+  const float4 a = __builtin_bit_cast(float4, a4), b = __builtin_bit_cast(float4, b4);
+  uint4 o;
+  o.x = pack_bf16x2(a.x * s, a.y * s);
+  o.y = pack_bf16x2(a.z * s, a.w * s);
+  o.z = pack_bf16x2(b.x * s, b.y * s);
+  o.w = pack_bf16x2(b.z * s, b.w * s);
+  return o;
 }
 
 template <int BLK>
-__device__ __forceinline__ void kv_store(const KVStage<BLK>& st, Smem<BLK>& sm) {
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void store_item(const Stage& st, Lds<BLK>& sm, int buf, const RowCtx& rc, int e, int tid) {
+  constexpr int VP = Lds<BLK>::kVPitch;
+  uint16_t* kb = sm.k[buf];
+  uint16_t* vt = sm.vt[buf];
+  if (e < rc.n_exact) {
+    constexpr int kKC = BLK * (kHeadDim / 8) / kThreads;
 #pragma unroll
-  for (int u = 0; u < KVStage<BLK>::kKChunks; ++u) {
-    const int ci = tid + u * kThreads;
-    const int kk = ci >> 4, dc = ci & 15;
-    *reinterpret_cast<uint4*>(&sm.k[kk * kKPitch + dc * 8]) = st.k[u];
-  }
-  if (tid < KVStage<BLK>::kVTasks) vt_store4x8<BLK>(sm, tid >> 4, tid & 15, st.v);
-}
-
-// Stage B pooled keys/values of correction chunk cb (fp32 -> bf16) plus the
-// per-column bias: log2(n_J) for a pruned causal block, -inf otherwise.
-// Returns (through LDS) nothing; the caller syncs.
-template <int BLK>
-__device__ __forceinline__ void stage_pooled(Smem<BLK>& sm, const AttnParams& p, int h, int r, int I, int L,
-                                             int cb, float kscale, float vscale) {
-  const int tid = threadIdx.x;
-  const int64_t base = ((int64_t)h * p.NB_tot + p.rt.blk_off[r]) * kHeadDim;
-  constexpr int kChunks = BLK * (kHeadDim / 8);
-  for (int ci = tid; ci < kChunks; ci += kThreads) {
-    const int kk = ci >> 4, dc = ci & 15;
-    const int J = cb * BLK + kk;
-    uint4 o = make_uint4(0, 0, 0, 0);
-    if (J < I) {
-      const float4* src = reinterpret_cast<const float4*>(p.k_bar + base + (int64_t)J * kHeadDim + dc * 8);
-      const float4 a = src[0], b = src[1];
-      o.x = pack_bf16x2(a.x * kscale, a.y * kscale);
-      o.y = pack_bf16x2(a.z * kscale, a.w * kscale);
-      o.z = pack_bf16x2(b.x * kscale, b.y * kscale);
-      o.w = pack_bf16x2(b.z * kscale, b.w * kscale);
-    }
-    *reinterpret_cast<uint4*>(&sm.k[kk * kKPitch + dc * 8]) = o;
-  }
-  constexpr int kVTasks = (BLK / 4) * (kHeadDim / 8);
-  for (int tk = tid; tk < kVTasks; tk += kThreads) {
-    const int dc = tk & 15, kg = tk >> 4;
-    uint4 v[4];
+    for (int u = 0; u < kKC; ++u)
+      *reinterpret_cast<uint4*>(&kb[((tid >> 4) + 32 * u) * kKPitch + (tid & 15) * 8]) = st.k[u];
+    constexpr int KG = BLK / 4;
+    if (tid < KG * (kHeadDim / 8)) {
+      const int kg = tid % KG, dc = tid / KG;
+      uint16_t* d = vt + (dc * 8) * VP + kg * 4;
+      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&st.v[0]);
+      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&st.v[1]);
+      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&st.v[2]);
+      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&st.v[3]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int J = cb * BLK + kg * 4 + i;
-      v[i] = make_uint4(0, 0, 0, 0);
-      if (J < I) {
-        const float4* src = reinterpret_cast<const float4*>(p.v_bar + base + (int64_t)J * kHeadDim + dc * 8);
-        const float4 a = src[0], b = src[1];
-        v[i].x = pack_bf16x2(a.x * vscale, a.y * vscale);
-        v[i].y = pack_bf16x2(a.z * vscale, a.w * vscale);
-        v[i].z = pack_bf16x2(b.x * vscale, b.y * vscale);
-        v[i].w = pack_bf16x2(b.z * vscale, b.w * vscale);
+      for (int m = 0; m < 4; ++m) {
+        uint2 lo, hi;
+        lo.x = __builtin_amdgcn_perm(w1[m], w0[m], 0x05040100u);  // keys 0,1 of dim 2m
+        lo.y = __builtin_amdgcn_perm(w3[m], w2[m], 0x05040100u);  // keys 2,3 of dim 2m
+        hi.x = __builtin_amdgcn_perm(w1[m], w0[m], 0x07060302u);  // dim 2m+1
+        hi.y = __builtin_amdgcn_perm(w3[m], w2[m], 0x07060302u);
+        *reinterpret_cast<uint2*>(d + (2 * m) * VP) = lo;
+        *reinterpret_cast<uint2*>(d + (2 * m + 1) * VP) = hi;
       }
     }
-    vt_store4x8<BLK>(sm, kg, dc, v);
-  }
-  for (int kk = tid; kk < BLK; kk += kThreads) {
-    const int J = cb * BLK + kk;
-    float bval = -INFINITY;
-    if (J < I && !((sm.selbits[J >> 5] >> (J & 31)) & 1u)) bval = __log2f((float)min(BLK, L - J * BLK));
-    sm.bias[kk] = bval;
+  } else {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      *reinterpret_cast<uint4*>(&kb[((tid >> 4) + 32 * u) * kKPitch + (tid & 15) * 8]) =
+          cvt8(st.k[2 * u], st.k[2 * u + 1], rc.kscale);
+    const int kg = tid & 31, dc = tid >> 5;
+    uint16_t* d = vt + (dc * 8) * VP + kg * 2;
+    const float4 a0 = __builtin_bit_cast(float4, st.v[0]), a1 = __builtin_bit_cast(float4, st.v[1]);
+    const float4 b0 = __builtin_bit_cast(float4, st.v[2]), b1 = __builtin_bit_cast(float4, st.v[3]);
+    const float x0[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    const float x1[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+    const float s = rc.vscale;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) *reinterpret_cast<uint32_t*>(d + q * VP) = pack_bf16x2(x0[q] * s, x1[q] * s);
+    if (tid < kPC) {
+      const int Jc = (e - rc.n_exact) * kPC + tid;
+      float bv = -INFINITY;
+      if (Jc < rc.I && !((sm.selbits[Jc >> 5] >> (Jc & 31)) & 1u)) bv = __log2f((float)min(BLK, rc.L - Jc * BLK));
+      sm.bias[buf][tid] = bv;
+    }
   }
 }
 
-// Per-wave state of the online softmax for 32 query rows.
+// Per-wave online-softmax state for 32 query rows.
 template <int BLK>
 struct WaveState {
+  static constexpr int NKT = BLK / 32;
   bf16x8 qf[kHeadDim / 16];  // B operand of S^T = K Q^T, one per 16-dim step
   f32x16 o[kHeadDim / 32];   // O^T accumulators, one per 32-dim tile
   float m;                   // running max (log2 units)
   float l;                   // this lane's partial row sum
 };
 
-// One key block (exact or pooled) for one wave. kt_lim: last 32-key tile that
-// is not fully masked; diag: causal mask inside tile kt_lim; use_bias: add
-// sm.bias per key column. tq: this lane's query offset inside the block.
+// One item for one wave. kt_lim: last 32-key tile that is not fully masked
+// (-1: none). diag: causal mask inside tile kt_lim (tq = query offset).
+// pooled: logit s*sl2 + bias[col].
 template <int BLK>
-__device__ __forceinline__ void attend_block(WaveState<BLK>& ws, const Smem<BLK>& sm, int kt_lim, bool diag,
-                                             bool use_bias, int tq, float sl2) {
+__device__ __forceinline__ void attend_item(WaveState<BLK>& ws, const uint16_t* kb, const uint16_t* vt,
+                                            const float* bias, int kt_lim, bool diag, bool pooled, int tq,
+                                            float sl2, int lk, int lv, int hf) {
   constexpr int NKT = BLK / 32;
-  const int lane = threadIdx.x & 63;
-  const int c = lane & 31, hf = lane >> 5;
+  constexpr int VP = Lds<BLK>::kVPitch;
   f32x16 s[NKT];
 #pragma unroll
   for (int kt = 0; kt < NKT; ++kt) {
-    if (kt > kt_lim) continue;
     f32x16 acc = {};
+    if (kt <= kt_lim) {
+      const uint16_t* base = kb + lk + kt * 32 * kKPitch;
 #pragma unroll
-    for (int ks = 0; ks < kHeadDim / 16; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[(kt * 32 + c) * kKPitch + ks * 16 + hf * 8]);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ws.qf[ks], acc, 0, 0, 0);
+      for (int ks = 0; ks < kHeadDim / 16; ++ks)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(base + ks * 16), ws.qf[ks],
+                                                      acc, 0, 0, 0);
     }
     s[kt] = acc;
   }
-  // scale, bias, mask; local max
-  float mloc = kNegBig;
+  // max
+  float mx = kNegBig;
+  if (pooled) {
 #pragma unroll
-  for (int kt = 0; kt < NKT; ++kt) {
-    if (kt > kt_lim) continue;
+    for (int kt = 0; kt < NKT; ++kt) {
+      if (kt > kt_lim) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float4 bb = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (use_bias) bb = *reinterpret_cast<const float4*>(&sm.bias[kt * 32 + i * 8 + hf * 4]);
+      for (int i = 0; i < 4; ++i) {
+        const float4 bb = *reinterpret_cast<const float4*>(&bias[kt * 32 + i * 8 + hf * 4]);
+        const float bv[4] = {bb.x, bb.y, bb.z, bb.w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float x = s[kt][4 * i + j] * sl2;
-        if (use_bias) x += (j == 0 ? bb.x : j == 1 ? bb.y : j == 2 ? bb.z : bb.w);
-        if (diag && kt == kt_lim) {
-          const int key = kt * 32 + i * 8 + hf * 4 + j;
-          if (key > tq) x = -INFINITY;
+        for (int jj = 0; jj < 4; ++jj) {
+          s[kt][4 * i + jj] = fmaf(s[kt][4 * i + jj], sl2, bv[jj]);
+          mx = fmaxf(mx, s[kt][4 * i + jj]);
         }
-        s[kt][4 * i + j] = x;
-        mloc = fmaxf(mloc, x);
       }
     }
+  } else {
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) {
+      if (kt > kt_lim) continue;
+      if (diag && kt == kt_lim) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            if (kt * 32 + i * 8 + hf * 4 + jj > tq) s[kt][4 * i + jj] = -INFINITY;
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kt][e]);
+    }
+    mx *= sl2;
   }
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-  const float m_new = fmaxf(ws.m, mloc);
-  const float corr = __builtin_amdgcn_exp2f(ws.m - m_new);
-  ws.m = m_new;
-  ws.l *= corr;
-  if (__ballot(corr != 1.0f) != 0) {
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  // Lazy running max (see the file header).
+  const float m_new = mx > ws.m + kSlack ? mx : ws.m;
+  if (__ballot(m_new != ws.m) != 0) {
+    const float corr = __builtin_amdgcn_exp2f(ws.m - m_new);
+    ws.l *= corr;
 #pragma unroll
     for (int dt = 0; dt < kHeadDim / 32; ++dt) ws.o[dt] *= corr;
   }
-  // probabilities -> bf16 B operands; PV
+  ws.m = m_new;
+  const float sc = pooled ? 1.0f : sl2;
+  const float neg_m = -m_new;
   float lsum = 0.f;
 #pragma unroll
   for (int kt = 0; kt < NKT; ++kt) {
@@ -255,30 +312,25 @@ __device__ __forceinline__ void attend_block(WaveState<BLK>& ws, const Smem<BLK>
     bf16x8 pf[2];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
-      f32x2 pr[4];
+      float pv[8];
 #pragma unroll
-      for (int t = 0; t < 8; t += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(s[kt][8 * s2 + t] - m_new);
-        const float p1 = __builtin_amdgcn_exp2f(s[kt][8 * s2 + t + 1] - m_new);
-        lsum += p0 + p1;
-        pr[t / 2] = f32x2{p0, p1};
+      for (int t = 0; t < 8; ++t) {
+        pv[t] = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * s2 + t], sc, neg_m));
+        lsum += pv[t];
       }
-      const bf16x2 b0 = __builtin_convertvector(pr[0], bf16x2);
-      const bf16x2 b1 = __builtin_convertvector(pr[1], bf16x2);
-      const bf16x2 b2 = __builtin_convertvector(pr[2], bf16x2);
-      const bf16x2 b3 = __builtin_convertvector(pr[3], bf16x2);
-      pf[s2] = bf16x8{b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
+      const bf16x4 lo = __builtin_convertvector(f32x4{pv[0], pv[1], pv[2], pv[3]}, bf16x4);
+      const bf16x4 hi = __builtin_convertvector(f32x4{pv[4], pv[5], pv[6], pv[7]}, bf16x4);
+      pf[s2] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
 #pragma unroll
     for (int dt = 0; dt < kHeadDim / 32; ++dt) {
-      const uint16_t* vrow = &sm.vt[(dt * 32 + c) * Smem<BLK>::kVPitch + kt * 32 + hf * 4];
+      const uint16_t* base = vt + lv + dt * 32 * VP + kt * 32;
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + s2 * 16);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + s2 * 16 + 8);
-        const u32x4 w = {lo.x, lo.y, hi.x, hi.y};
-        const bf16x8 a = __builtin_bit_cast(bf16x8, w);
-        ws.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[s2], ws.o[dt], 0, 0, 0);
+        const uint2 lo = *reinterpret_cast<const uint2*>(base + s2 * 16);
+        const uint2 hi = *reinterpret_cast<const uint2*>(base + s2 * 16 + 8);
+        const u32x4 wv = {lo.x, lo.y, hi.x, hi.y};
+        ws.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wv), pf[s2], ws.o[dt], 0, 0, 0);
       }
     }
   }
@@ -294,8 +346,7 @@ __device__ __forceinline__ void decode_work(const AttnParams& p, int& I, int& r,
   const int rem = blockIdx.x - pk * U;
   h = rem % p.Hkv;
   sub = rem / p.Hkv;
-  // C(I) = number of (r, I') with I' > I; non-increasing in I. Find the
-  // smallest I with C(I) <= pk.
+  // C(x) = number of (r, I') with I' > x; non-increasing. Smallest I with C(I) <= pk.
   auto C = [&](int x) {
     int s = 0;
     for (int q = 0; q < rt.R; ++q) s += max(0, rt.blk_off[q + 1] - rt.blk_off[q] - 1 - x);
@@ -318,35 +369,52 @@ __device__ __forceinline__ void decode_work(const AttnParams& p, int& I, int& r,
   }
 }
 
-template <int BLK, bool FP8>
+template <int BLK, bool FP8, bool PAGED>
 __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
-  __shared__ Smem<BLK> sm;
+  __shared__ Lds<BLK> sm;
   constexpr int NKT = BLK / 32;
-  int I, r, h, sub;
-  decode_work(p, I, r, h, sub);
+  RowCtx rc;
+  int sub;
+  decode_work(p, rc.I, rc.r, rc.h, sub);
   const ReqTable& rt = p.rt;
-  const int L = rt.tok_off[r + 1] - rt.tok_off[r];
-  const int nI = min(BLK, L - I * BLK);
-  const int64_t row = (int64_t)h * p.NB_tot + rt.blk_off[r] + I;
+  rc.tok_base = rt.tok_off[rc.r];
+  rc.L = rt.tok_off[rc.r + 1] - rt.tok_off[rc.r];
+  const int I = rc.I;
+  const int nI = min(BLK, rc.L - I * BLK);
+  const int64_t row = (int64_t)rc.h * p.NB_tot + rt.blk_off[rc.r] + I;
+  rc.n_exact = p.dense ? I + 1 : p.row_ptr[row + 1] - p.row_ptr[row];
+  rc.cols = p.dense ? nullptr : p.col_idx + p.row_ptr[row];
+  rc.ccols = sm.colcache;
+  const bool do_corr = p.mean_correction && !p.dense && I > 0;
+  rc.n_items = rc.n_exact + (do_corr ? (I + kPC - 1) / kPC : 0);
+  rc.pooled_base = ((int64_t)rc.h * p.NB_tot + rt.blk_off[rc.r]) * kHeadDim;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63;
+  const int lane = tid & 63;
+  const int w = uniform(tid >> 6);
   const int c = lane & 31, hf = lane >> 5;
-  const int prow0 = sub * kRowsPerWG + w * 32;   // first packed row of this wave
+  const int prow0 = sub * kRowsPerWG + w * 32;  // first packed row of this wave
   const bool wave_active = prow0 < p.G * BLK;
-  const int g = h * p.G + (wave_active ? prow0 / BLK : 0);
+  const int g = rc.h * p.G + (wave_active ? prow0 / BLK : 0);
   const int tq0 = prow0 % BLK;
   const int tq = tq0 + c;
   const bool q_valid = wave_active && tq < nI;
-  const int64_t tok = (int64_t)rt.tok_off[r] + (int64_t)I * BLK + tq;
+  const int64_t tok = rc.tok_base + (int64_t)I * BLK + tq;
+  const int lk = c * kKPitch + hf * 8;              // K operand base of this lane
+  const int lv = c * Lds<BLK>::kVPitch + hf * 4;    // V^T operand base of this lane
 
+  // Logit scale in log2 units; FP8 folds both descales into it and stages
+  // pooled k_bar / v_bar divided by the K / V descales (so both streams stay
+  // in code units), and multiplies the output by the V descale.
   float sl2 = p.sm_scale * kLog2e;
-  float kscale = 1.f, vscale = 1.f, oscale = 1.f;
+  rc.kscale = 1.f;
+  rc.vscale = 1.f;
+  float oscale = 1.f;
   if constexpr (FP8) {
     const float dq = *p.descale_q, dk = *p.descale_k, dv = *p.descale_v;
     sl2 *= dq * dk;
-    kscale = 1.f / dk;
-    vscale = 1.f / dv;
+    rc.kscale = 1.f / dk;
+    rc.vscale = 1.f / dv;
     oscale = dv;
   }
 
@@ -362,46 +430,38 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
     ws.qf[ks] = __builtin_bit_cast(bf16x8, qv);
   }
 
-  // exact blocks: the CSR row, or every causal block in dense mode
-  const int n_exact = p.dense ? I + 1 : p.row_ptr[row + 1] - p.row_ptr[row];
-  const int32_t* cols = p.dense ? nullptr : p.col_idx + p.row_ptr[row];
-  const bool do_corr = p.mean_correction && !p.dense && I > 0;
-
-  if (do_corr) {
-    for (int wd = tid; wd <= (I >> 5); wd += kThreads) sm.selbits[wd] = 0u;
+  if (!p.dense) {
+    if (do_corr)
+      for (int wd = tid; wd <= (I >> 5); wd += kThreads) sm.selbits[wd] = 0u;
+    for (int e = tid; e < min(rc.n_exact, kColCache); e += kThreads) sm.colcache[e] = rc.cols[e];
     __syncthreads();
-    for (int e = tid; e < n_exact; e += kThreads) {
-      const int J = cols[e];
-      atomicOr(&sm.selbits[J >> 5], 1u << (J & 31));
-    }
-  }
-
-  KVStage<BLK> st;
-  if (n_exact > 0) kv_load<BLK, FP8>(st, p, r, p.dense ? 0 : cols[0], h, L);
-  for (int e = 0; e < n_exact; ++e) {
-    const int J = p.dense ? e : cols[e];
-    __syncthreads();
-    kv_store<BLK>(st, sm);
-    __syncthreads();
-    if (e + 1 < n_exact) kv_load<BLK, FP8>(st, p, r, p.dense ? e + 1 : cols[e + 1], h, L);
-    if (wave_active) {
-      const bool diag = (J == I);
-      const int kt_lim = diag ? (tq0 >> 5) : NKT - 1;
-      attend_block<BLK>(ws, sm, kt_lim, diag, false, tq, sl2);
-    }
-  }
-
-  if (do_corr) {
-    const int nchunks = (I + BLK - 1) / BLK;
-    for (int cb = 0; cb < nchunks; ++cb) {
-      __syncthreads();
-      stage_pooled<BLK>(sm, p, h, r, I, L, cb, kscale, vscale);
-      __syncthreads();
-      if (wave_active) {
-        const int ncols = min(BLK, I - cb * BLK);
-        attend_block<BLK>(ws, sm, (ncols - 1) >> 5, false, true, tq, sl2);
+    if (do_corr) {
+      for (int e = tid; e < rc.n_exact; e += kThreads) {
+        const int J = e < kColCache ? sm.colcache[e] : rc.cols[e];
+        atomicOr(&sm.selbits[J >> 5], 1u << (J & 31));
       }
     }
+    __syncthreads();
+  }
+
+  const int N = rc.n_items;
+  Stage st;
+  load_item<BLK, FP8, PAGED>(st, p, rc, 0, tid);
+  store_item<BLK>(st, sm, 0, rc, 0, tid);
+  __syncthreads();
+  for (int e = 0; e < N; ++e) {
+    const int buf = e & 1;
+    if (e + 1 < N) load_item<BLK, FP8, PAGED>(st, p, rc, e + 1, tid);
+    if (wave_active) {
+      const bool pooled = e >= rc.n_exact;
+      const bool diag = e == rc.n_exact - 1;
+      int kt_lim = NKT - 1;
+      if (diag) kt_lim = tq0 >> 5;
+      if (pooled) kt_lim = (min(kPC, I - (e - rc.n_exact) * kPC) - 1) >> 5;
+      attend_item<BLK>(ws, sm.k[buf], sm.vt[buf], sm.bias[buf], kt_lim, diag, pooled, tq, sl2, lk, lv, hf);
+    }
+    if (e + 1 < N) store_item<BLK>(st, sm, buf ^ 1, rc, e + 1, tid);
+    __syncthreads();
   }
 
   if (!wave_active) return;
@@ -423,21 +483,27 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   }
 }
 
+template <int BLK, bool FP8>
+void launch_attn_t(const AttnParams& p, dim3 grid, hipStream_t stream) {
+  if (p.kv.paged) hipLaunchKernelGGL((attn_kernel<BLK, FP8, true>), grid, dim3(kThreads), 0, stream, p);
+  else hipLaunchKernelGGL((attn_kernel<BLK, FP8, false>), grid, dim3(kThreads), 0, stream, p);
+}
+
 }  // namespace
+
+int attn_rows_per_wg() { return kRowsPerWG; }
 
 hipError_t launch_attn(const AttnParams& p, hipStream_t stream) {
   const int64_t wgs = (int64_t)p.Hkv * p.NB_tot * p.subs;
   dim3 grid((unsigned)wgs);
   if (p.B == 128) {
-    if (p.fp8) hipLaunchKernelGGL((attn_kernel<128, true>), grid, dim3(kThreads), 0, stream, p);
-    else hipLaunchKernelGGL((attn_kernel<128, false>), grid, dim3(kThreads), 0, stream, p);
+    if (p.fp8) launch_attn_t<128, true>(p, grid, stream);
+    else launch_attn_t<128, false>(p, grid, stream);
   } else {
-    if (p.fp8) hipLaunchKernelGGL((attn_kernel<64, true>), grid, dim3(kThreads), 0, stream, p);
-    else hipLaunchKernelGGL((attn_kernel<64, false>), grid, dim3(kThreads), 0, stream, p);
+    if (p.fp8) launch_attn_t<64, true>(p, grid, stream);
+    else launch_attn_t<64, false>(p, grid, stream);
   }
   return hipGetLastError();
 }
-
-int attn_rows_per_wg() { return kRowsPerWG; }
 
 }  // namespace fpv2
