@@ -36,7 +36,7 @@ def parse():
     ap.add_argument("--alpha", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=6, help="attention rows the CPU baseline computes")
+    ap.add_argument("--cpu-rows", type=int, default=16, help="attention rows the CPU baseline computes")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
     return ap.parse_args()

@@ -11,6 +11,7 @@ from .oracle import (  # noqa: F401
     pool_queries,
     select_blocks,
     attend,
+    attend_row,
     attend_loop,
     prefill,
     gather_paged,

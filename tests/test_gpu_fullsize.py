@@ -1,0 +1,95 @@
+"""GPU parity at the full benchmark sizes, in the launch configuration the
+benchmark times.
+
+At these sizes the oracle computes pooling and selection for the whole layer
+(the CSR is compared bit-exactly outside the near-threshold band) and the
+attention outputs for sampled rows: the first, second, middle and last query
+block of the first and last KV head of every request (which covers ragged
+tails and the heaviest rows), plus random rows.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_common import (O_TOL, compare_csr, compare_outputs, compare_pooled, host_values, rows_for_sample, run_gpu,
+                        sets_from_csr)
+
+pytestmark = pytest.mark.gpu
+
+_CACHE = {}
+
+
+def _workload(name, **over):
+    key = (name, repr(sorted(over.items())))
+    if key not in _CACHE:
+        _CACHE.clear()  # keep one full-size workload in host memory at a time
+        wl = synth.make_workload(name, **over)
+        _CACHE[key] = (wl, host_values(wl))
+    return _CACHE[key]
+
+
+def _oracle_select(wl, Q, K, V, alpha):
+    kw = {}
+    if wl.paged:
+        kw = dict(K_pages=wl.k_pages.to(torch.float32).to(torch.float64).numpy(),
+                  V_pages=wl.v_pages.to(torch.float32).to(torch.float64).numpy(),
+                  page_table=wl.page_table.numpy(), page_size=wl.page_size)
+        K = V = None
+    return oracle.prefill(Q, K, V, wl.cu_seqlens, wl.num_kv_heads, wl.block_size, alpha, wl.sel_scale,
+                          wl.min_sparse_len, 1.0 / math.sqrt(wl.head_dim), True, do_attend=False, **kw)
+
+
+def _check(name, alpha=None, n_random=6, **over):
+    wl, (Q, K, V) = _workload(name, **over)
+    alpha = wl.alpha if alpha is None else alpha
+    print(f"[fullsize] {name} alpha={alpha} T={wl.total_tokens} dtype={wl.dtype} paged={wl.paged}", flush=True)
+    gpu = run_gpu(wl, alpha)
+    orc = _oracle_select(wl, Q, K, V, alpha)
+    compare_pooled(gpu, orc)
+    n_near = compare_csr(gpu, orc)
+    # attention on sampled rows, with the CSR the GPU chose
+    rows = rows_for_sample(wl, n_random=n_random)
+    sets = sets_from_csr(gpu["row_ptr"], gpu["col_idx"], orc.blk_off, wl.num_kv_heads)
+    NBt = orc.blk_off[-1]
+    G = wl.num_q_heads // wl.num_kv_heads
+    B = wl.block_size
+    o_ref = np.full((wl.total_tokens, wl.num_q_heads, wl.head_dim), np.nan)
+    lse_ref = np.full((wl.num_q_heads, wl.total_tokens), np.nan)
+    for gr in rows:
+        h, b = divmod(gr, NBt)
+        r = int(np.searchsorted(orc.blk_off, b, side="right") - 1)
+        I = b - orc.blk_off[r]
+        s, e = wl.cu_seqlens[r], wl.cu_seqlens[r + 1]
+        a0, a1 = orc.blk_off[r], orc.blk_off[r + 1]
+        o, l = oracle.attend_row(Q[s:e], K[s:e], V[s:e], orc.kbar[:, a0:a1], orc.vbar[:, a0:a1],
+                                 np.asarray(sets[r][h][I]), h, I, B, G, 1.0 / math.sqrt(wl.head_dim), True)
+        t0 = s + I * B
+        o_ref[t0:t0 + o.shape[0], h * G:(h + 1) * G] = o
+        lse_ref[h * G:(h + 1) * G, t0:t0 + o.shape[0]] = l.T
+    o_err, l_err = compare_outputs(gpu["out"], gpu["lse"], o_ref, lse_ref, O_TOL[wl.dtype])
+    nnz = int(gpu["row_ptr"][-1])
+    pairs = wl.num_kv_heads * sum(nb * (nb + 1) // 2 for nb in np.diff(orc.blk_off))
+    print(f"[fullsize] ok: nnz={nnz} kept={nnz / pairs:.4f} near_rows={n_near} rows_checked={len(rows)} "
+          f"O_err={o_err:.2e} LSE_err={l_err:.2e}", flush=True)
+    return gpu
+
+
+def test_llama_32k():
+    _check("llama_32k")
+
+
+@pytest.mark.parametrize("alpha", [0.3, 0.1, 0.5])
+def test_llama_128k_alpha_sweep(alpha):
+    _check("llama_128k", alpha=alpha, n_random=4)
+
+
+def test_qwen30b_128k_fp8():
+    _check("qwen30b_128k_fp8", n_random=4)
+
+
+def test_qwen4b_varlen_paged():
+    _check("qwen4b_varlen_paged", n_random=4)
