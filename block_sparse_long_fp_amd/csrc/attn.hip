@@ -238,103 +238,113 @@ struct WaveState {
   float l;                   // this lane's partial row sum
 };
 
-// One item for one wave. kt_lim: last 32-key tile that is not fully masked
-// (-1: none). diag: causal mask inside tile kt_lim (tq = query offset).
-// pooled: logit s*sl2 + bias[col].
+// One item for one wave, processed in 64-key halves (each: QK^T of two
+// 32-key tiles, online-softmax update, PV), which keeps 32 score registers
+// live instead of 64. kt_lim: last 32-key tile that is not fully masked (-1:
+// none). diag: causal mask inside tile kt_lim (tq = query offset). pooled:
+// logit s*sl2 + bias[col].
 template <int BLK>
 __device__ __forceinline__ void attend_item(WaveState<BLK>& ws, const uint16_t* kb, const uint16_t* vt,
                                             const float* bias, int kt_lim, bool diag, bool pooled, int tq,
                                             float sl2, int lk, int lv, int hf) {
   constexpr int NKT = BLK / 32;
   constexpr int VP = Lds<BLK>::kVPitch;
-  f32x16 s[NKT];
 #pragma unroll
-  for (int kt = 0; kt < NKT; ++kt) {
-    f32x16 acc = {};
-    if (kt <= kt_lim) {
-      const uint16_t* base = kb + lk + kt * 32 * kKPitch;
+  for (int hh = 0; hh < NKT / 2; ++hh) {
+    if (2 * hh > kt_lim) break;
+    f32x16 s[2];
 #pragma unroll
-      for (int ks = 0; ks < kHeadDim / 16; ++ks)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(base + ks * 16), ws.qf[ks],
-                                                      acc, 0, 0, 0);
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const int kt = 2 * hh + t2;
+      f32x16 acc = {};
+      if (kt <= kt_lim) {
+        const uint16_t* base = kb + lk + kt * 32 * kKPitch;
+#pragma unroll
+        for (int ks = 0; ks < kHeadDim / 16; ++ks)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(base + ks * 16),
+                                                        ws.qf[ks], acc, 0, 0, 0);
+      }
+      s[t2] = acc;
     }
-    s[kt] = acc;
-  }
-  // max
-  float mx = kNegBig;
-  if (pooled) {
+    float mx = kNegBig;
+    if (pooled) {
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) {
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const int kt = 2 * hh + t2;
+        if (kt > kt_lim) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float4 bb = *reinterpret_cast<const float4*>(&bias[kt * 32 + i * 8 + hf * 4]);
+          const float bv[4] = {bb.x, bb.y, bb.z, bb.w};
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            s[t2][4 * i + jj] = fmaf(s[t2][4 * i + jj], sl2, bv[jj]);
+            mx = fmaxf(mx, s[t2][4 * i + jj]);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const int kt = 2 * hh + t2;
+        if (kt > kt_lim) continue;
+        if (diag && kt == kt_lim) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+              if (kt * 32 + i * 8 + hf * 4 + jj > tq) s[t2][4 * i + jj] = -INFINITY;
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[t2][e]);
+      }
+      mx *= sl2;
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // Lazy running max (see the file header).
+    const float m_new = mx > ws.m + kSlack ? mx : ws.m;
+    if (__ballot(m_new != ws.m) != 0) {
+      const float corr = __builtin_amdgcn_exp2f(ws.m - m_new);
+      ws.l *= corr;
+#pragma unroll
+      for (int dt = 0; dt < kHeadDim / 32; ++dt) ws.o[dt] *= corr;
+    }
+    ws.m = m_new;
+    const float sc = pooled ? 1.0f : sl2;
+    const float neg_m = -m_new;
+    float lsum = 0.f;
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const int kt = 2 * hh + t2;
       if (kt > kt_lim) continue;
+      bf16x8 pf[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 bb = *reinterpret_cast<const float4*>(&bias[kt * 32 + i * 8 + hf * 4]);
-        const float bv[4] = {bb.x, bb.y, bb.z, bb.w};
+      for (int s2 = 0; s2 < 2; ++s2) {
+        float pv[8];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          s[kt][4 * i + jj] = fmaf(s[kt][4 * i + jj], sl2, bv[jj]);
-          mx = fmaxf(mx, s[kt][4 * i + jj]);
+        for (int t = 0; t < 8; ++t) {
+          pv[t] = __builtin_amdgcn_exp2f(fmaf(s[t2][8 * s2 + t], sc, neg_m));
+          lsum += pv[t];
+        }
+        const bf16x4 lo = __builtin_convertvector(f32x4{pv[0], pv[1], pv[2], pv[3]}, bf16x4);
+        const bf16x4 hi = __builtin_convertvector(f32x4{pv[4], pv[5], pv[6], pv[7]}, bf16x4);
+        pf[s2] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+#pragma unroll
+      for (int dt = 0; dt < kHeadDim / 32; ++dt) {
+        const uint16_t* base = vt + lv + dt * 32 * VP + kt * 32;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const uint2 lo = *reinterpret_cast<const uint2*>(base + s2 * 16);
+          const uint2 hi = *reinterpret_cast<const uint2*>(base + s2 * 16 + 8);
+          const u32x4 wv = {lo.x, lo.y, hi.x, hi.y};
+          ws.o[dt] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wv), pf[s2], ws.o[dt], 0, 0, 0);
         }
       }
     }
-  } else {
-#pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) {
-      if (kt > kt_lim) continue;
-      if (diag && kt == kt_lim) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj)
-            if (kt * 32 + i * 8 + hf * 4 + jj > tq) s[kt][4 * i + jj] = -INFINITY;
-      }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kt][e]);
-    }
-    mx *= sl2;
+    ws.l += lsum;
   }
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  // Lazy running max (see the file header).
-  const float m_new = mx > ws.m + kSlack ? mx : ws.m;
-  if (__ballot(m_new != ws.m) != 0) {
-    const float corr = __builtin_amdgcn_exp2f(ws.m - m_new);
-    ws.l *= corr;
-#pragma unroll
-    for (int dt = 0; dt < kHeadDim / 32; ++dt) ws.o[dt] *= corr;
-  }
-  ws.m = m_new;
-  const float sc = pooled ? 1.0f : sl2;
-  const float neg_m = -m_new;
-  float lsum = 0.f;
-#pragma unroll
-  for (int kt = 0; kt < NKT; ++kt) {
-    if (kt > kt_lim) continue;
-    bf16x8 pf[2];
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      float pv[8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        pv[t] = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * s2 + t], sc, neg_m));
-        lsum += pv[t];
-      }
-      const bf16x4 lo = __builtin_convertvector(f32x4{pv[0], pv[1], pv[2], pv[3]}, bf16x4);
-      const bf16x4 hi = __builtin_convertvector(f32x4{pv[4], pv[5], pv[6], pv[7]}, bf16x4);
-      pf[s2] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    }
-#pragma unroll
-    for (int dt = 0; dt < kHeadDim / 32; ++dt) {
-      const uint16_t* base = vt + lv + dt * 32 * VP + kt * 32;
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const uint2 lo = *reinterpret_cast<const uint2*>(base + s2 * 16);
-        const uint2 hi = *reinterpret_cast<const uint2*>(base + s2 * 16 + 8);
-        const u32x4 wv = {lo.x, lo.y, hi.x, hi.y};
-        ws.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wv), pf[s2], ws.o[dt], 0, 0, 0);
-      }
-    }
-  }
-  ws.l += lsum;
 }
 
 // blockIdx -> (query block I, request r) in descending-I order over the ragged
