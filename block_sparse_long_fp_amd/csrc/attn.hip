@@ -36,8 +36,9 @@
 //     32-lane pass writes one contiguous row segment (no conflicts).
 //   * Wave-uniform quantities live in scalar registers, so per-item and
 //     per-tile decisions are scalar branches.
-//   * Online softmax in base 2: max on raw scores, one fma + exp2 per score,
-//     fp32 row sums. The running max only moves when a block's max exceeds it
+//   * Online softmax in base 2, updated per 64-key half of an item (32 score
+//     registers live, which keeps the kernel within 256 VGPRs without
+//     spills): max on raw scores, one fma + exp2 per score, fp32 row sums. The running max only moves when a block's max exceeds it
 //     by more than 8 (probabilities stay below 256, exact after the final
 //     division), which makes output rescales rare.
 //   * Workgroups run heaviest first (query block index descending over the
@@ -95,16 +96,11 @@ struct RowCtx {
   int n_exact;          // CSR entries (key blocks) of the row
   int n_items;          // plus the correction chunks
   const int32_t* cols;  // CSR row (nullptr in dense mode)
-  const int32_t* ccols; // first kColCache CSR columns, copied to LDS
   int64_t pooled_base;  // element offset of the k_bar/v_bar row (h, blk_off[r])
   int64_t tok_base;     // first token of the request
   float kscale;         // pooled k_bar -> LDS scale (1/descale_k for FP8)
   float vscale;         // pooled v_bar -> LDS scale (1/descale_v for FP8)
 };
-
-__device__ __forceinline__ int exact_block(const RowCtx& rc, int e) {
-  return !rc.cols ? e : uniform(e < kColCache ? rc.ccols[e] : rc.cols[e]);
-}
 
 // Element offset of key `row` of block J (request-local token J*B+row, clamped
 // to the request's last token) of the row's KV head.
@@ -121,49 +117,76 @@ __device__ __forceinline__ int64_t kv_off(const AttnParams& p, const RowCtx& rc,
   }
 }
 
-// Registers carrying one item from HBM to LDS (8 x 16 bytes per thread):
-//   exact K  (B=128): rows tid/16 + 32u, dims 8(tid%16).. (u < 4, bf16)
-//   exact V  (B=128): keys 4kg..4kg+3 (kg = tid%32), dims 8(tid/32).. (bf16)
-//   pooled K: rows tid/16 + 32u (u < 2), dims 8(tid%16).. (fp32, 2 words each)
-//   pooled V: columns 2kg, 2kg+1 (kg = tid%32), dims 8(tid/32).. (fp32)
-// (B=64 uses the first half of the exact entries: 2 K rows, 256 V tasks.)
+// Staging of one item from HBM to LDS: every thread issues the same eight
+// 16-byte loads (stage slots) from one straight-line sequence whatever the
+// item kind (only the addresses are chosen per kind), so the loads stay in
+// flight while the current item is computed and no register copies merge
+// them afterwards. Slot plans, with E = elements per 16 bytes (8 bf16 or
+// 16 fp8) and C = d / E loads per key row:
+//   exact K: slot u < KL holds row tid/C + (512/C)u, elements E(tid%C)..;
+//            KL = B*C/512 (bf16: 4 at B=128, 2 at B=64; fp8: 2 or 1).
+//   exact V: slot 4+i (i < KL) holds key KL*kg + i (kg = tid % (B/KL)),
+//            elements E(tid / (B/KL)).., so each thread owns KL consecutive
+//            keys of E dims and writes V^T rows directly.
+//   Unused exact slots repeat a used address (the load hits the same line).
+//   pooled K: slots 2u, 2u+1 hold fp32 row tid/16 + 32u (u < 2), dims 8(tid%16)..
+//   pooled V: slots 4+2i, 5+2i hold fp32 column 2kg+i (kg = tid%32), dims 8(tid/32)..
 struct Stage {
-  uint4 k[4];
-  uint4 v[4];
+  uint4 x[8];
+};
+
+template <int BLK, bool FP8>
+struct ExactPlan {
+  static constexpr int E = FP8 ? 16 : 8;
+  static constexpr int C = kHeadDim / E;
+  static constexpr int KL = BLK * C / kThreads;
+  static constexpr int KG = BLK / KL;
+  static_assert(KL >= 1 && KL <= 4 && KG * C == kThreads, "exact staging plan");
 };
 
 template <int BLK, bool FP8, bool PAGED>
-__device__ __forceinline__ void load_item(Stage& st, const AttnParams& p, const RowCtx& rc, int e, int tid) {
+__device__ __forceinline__ void load_item(Stage& st, const AttnParams& p, const RowCtx& rc, const int32_t* colcache,
+                                          int e, int tid) {
+  using P = ExactPlan<BLK, FP8>;
+  g_u32x4* src[8];  // global address space, so the loads stay global (not flat)
   if (e < rc.n_exact) {
-    const int J = exact_block(rc, e);
-    constexpr int kKC = BLK * (kHeadDim / 8) / kThreads;  // 4 (B=128) or 2 (B=64)
+    const int J = !rc.cols ? e : uniform(e < kColCache ? lload_i32(colcache + e) : gload_i32(rc.cols + e));
+    g_uint8* kbase = (g_uint8*)p.k;
+    g_uint8* vbase = (g_uint8*)p.v;
+    constexpr int eb = FP8 ? 1 : 2;
 #pragma unroll
-    for (int u = 0; u < kKC; ++u)
-      st.k[u] = load8_as_bf16<FP8>(p.k, kv_off<BLK, PAGED>(p, rc, J, (tid >> 4) + 32 * u) + (tid & 15) * 8);
-    constexpr int KG = BLK / 4;
-    if (tid < KG * (kHeadDim / 8)) {
-      const int kg = tid % KG, dc = tid / KG;
+    for (int u = 0; u < 4; ++u) {
+      const int uu = u % P::KL;
+      const int64_t off = kv_off<BLK, PAGED>(p, rc, J, tid / P::C + (kThreads / P::C) * uu) + (tid % P::C) * P::E;
+      src[u] = (g_u32x4*)(kbase + off * eb);
+    }
+    const int kg = tid % P::KG, dc = tid / P::KG;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st.v[i] = load8_as_bf16<FP8>(p.v, kv_off<BLK, PAGED>(p, rc, J, kg * 4 + i) + dc * 8);
+    for (int i = 0; i < 4; ++i) {
+      const int ii = i % P::KL;
+      const int64_t off = kv_off<BLK, PAGED>(p, rc, J, kg * P::KL + ii) + dc * P::E;
+      src[4 + i] = (g_u32x4*)(vbase + off * eb);
     }
   } else {
     const int c0 = (e - rc.n_exact) * kPC;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int Jp = min(c0 + (tid >> 4) + 32 * u, rc.I - 1);
-      const uint4* src = reinterpret_cast<const uint4*>(p.k_bar + rc.pooled_base + (int64_t)Jp * kHeadDim + (tid & 15) * 8);
-      st.k[2 * u] = src[0];
-      st.k[2 * u + 1] = src[1];
+      g_u32x4* s = (g_u32x4*)((g_float*)p.k_bar + rc.pooled_base + (int64_t)Jp * kHeadDim + (tid & 15) * 8);
+      src[2 * u] = s;
+      src[2 * u + 1] = s + 1;
     }
     const int kg = tid & 31, dc = tid >> 5;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int Jp = min(c0 + kg * 2 + i, rc.I - 1);
-      const uint4* src = reinterpret_cast<const uint4*>(p.v_bar + rc.pooled_base + (int64_t)Jp * kHeadDim + dc * 8);
-      st.v[2 * i] = src[0];
-      st.v[2 * i + 1] = src[1];
+      g_u32x4* s = (g_u32x4*)((g_float*)p.v_bar + rc.pooled_base + (int64_t)Jp * kHeadDim + dc * 8);
+      src[4 + 2 * i] = s;
+      src[5 + 2 * i] = s + 1;
     }
   }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) st.x[i] = gload16(src[i]);
 }
 
 __device__ __forceinline__ uint4 cvt8(const uint4 a4, const uint4 b4, float s) {
@@ -176,24 +199,50 @@ __device__ __forceinline__ uint4 cvt8(const uint4 a4, const uint4 b4, float s) {
   return o;
 }
 
-template <int BLK>
+// The 16 e4m3 codes of a slot as 16 floats (exact).
+__device__ __forceinline__ void fp8x16_to_float(const uint4 w, float (&f)[16]) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) f[4 * q + b] = e4m3_to_float((ws[q] >> (8 * b)) & 0xFFu);
+}
+
+template <int BLK, bool FP8>
 __device__ __forceinline__ void store_item(const Stage& st, Lds<BLK>& sm, int buf, const RowCtx& rc, int e, int tid) {
+  using P = ExactPlan<BLK, FP8>;
   constexpr int VP = Lds<BLK>::kVPitch;
   uint16_t* kb = sm.k[buf];
   uint16_t* vt = sm.vt[buf];
   if (e < rc.n_exact) {
-    constexpr int kKC = BLK * (kHeadDim / 8) / kThreads;
 #pragma unroll
-    for (int u = 0; u < kKC; ++u)
-      *reinterpret_cast<uint4*>(&kb[((tid >> 4) + 32 * u) * kKPitch + (tid & 15) * 8]) = st.k[u];
-    constexpr int KG = BLK / 4;
-    if (tid < KG * (kHeadDim / 8)) {
-      const int kg = tid % KG, dc = tid / KG;
-      uint16_t* d = vt + (dc * 8) * VP + kg * 4;
-      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&st.v[0]);
-      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&st.v[1]);
-      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&st.v[2]);
-      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&st.v[3]);
+    for (int u = 0; u < P::KL; ++u) {
+      uint16_t* d = &kb[(tid / P::C + (kThreads / P::C) * u) * kKPitch + (tid % P::C) * P::E];
+      if constexpr (!FP8) {
+        *reinterpret_cast<uint4*>(d) = st.x[u];
+      } else {
+        float f[16];
+        fp8x16_to_float(st.x[u], f);
+        uint4 lo, hi;
+        lo.x = pack_bf16x2(f[0], f[1]);
+        lo.y = pack_bf16x2(f[2], f[3]);
+        lo.z = pack_bf16x2(f[4], f[5]);
+        lo.w = pack_bf16x2(f[6], f[7]);
+        hi.x = pack_bf16x2(f[8], f[9]);
+        hi.y = pack_bf16x2(f[10], f[11]);
+        hi.z = pack_bf16x2(f[12], f[13]);
+        hi.w = pack_bf16x2(f[14], f[15]);
+        reinterpret_cast<uint4*>(d)[0] = lo;
+        reinterpret_cast<uint4*>(d)[1] = hi;
+      }
+    }
+    const int kg = tid % P::KG, dc = tid / P::KG;
+    uint16_t* d = vt + (dc * P::E) * VP + kg * P::KL;
+    if constexpr (!FP8 && P::KL == 4) {
+      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&st.x[4]);
+      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&st.x[5]);
+      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&st.x[6]);
+      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&st.x[7]);
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         uint2 lo, hi;
@@ -204,16 +253,36 @@ __device__ __forceinline__ void store_item(const Stage& st, Lds<BLK>& sm, int bu
         *reinterpret_cast<uint2*>(d + (2 * m) * VP) = lo;
         *reinterpret_cast<uint2*>(d + (2 * m + 1) * VP) = hi;
       }
+    } else if constexpr (!FP8 && P::KL == 2) {
+      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&st.x[4]);
+      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&st.x[5]);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        *reinterpret_cast<uint32_t*>(d + (2 * m) * VP) = __builtin_amdgcn_perm(w1[m], w0[m], 0x05040100u);
+        *reinterpret_cast<uint32_t*>(d + (2 * m + 1) * VP) = __builtin_amdgcn_perm(w1[m], w0[m], 0x07060302u);
+      }
+    } else if constexpr (FP8 && P::KL == 2) {
+      float f0[16], f1[16];
+      fp8x16_to_float(st.x[4], f0);
+      fp8x16_to_float(st.x[5], f1);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) *reinterpret_cast<uint32_t*>(d + q * VP) = pack_bf16x2(f0[q], f1[q]);
+    } else {
+      static_assert(FP8 && P::KL == 1, "exact V staging plan");
+      float f0[16];
+      fp8x16_to_float(st.x[4], f0);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) d[q * VP] = static_cast<uint16_t>(pack_bf16x2(f0[q], 0.f));
     }
   } else {
 #pragma unroll
     for (int u = 0; u < 2; ++u)
       *reinterpret_cast<uint4*>(&kb[((tid >> 4) + 32 * u) * kKPitch + (tid & 15) * 8]) =
-          cvt8(st.k[2 * u], st.k[2 * u + 1], rc.kscale);
+          cvt8(st.x[2 * u], st.x[2 * u + 1], rc.kscale);
     const int kg = tid & 31, dc = tid >> 5;
     uint16_t* d = vt + (dc * 8) * VP + kg * 2;
-    const float4 a0 = __builtin_bit_cast(float4, st.v[0]), a1 = __builtin_bit_cast(float4, st.v[1]);
-    const float4 b0 = __builtin_bit_cast(float4, st.v[2]), b1 = __builtin_bit_cast(float4, st.v[3]);
+    const float4 a0 = __builtin_bit_cast(float4, st.x[4]), a1 = __builtin_bit_cast(float4, st.x[5]);
+    const float4 b0 = __builtin_bit_cast(float4, st.x[6]), b1 = __builtin_bit_cast(float4, st.x[7]);
     const float x0[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
     const float x1[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
     const float s = rc.vscale;
@@ -228,6 +297,18 @@ __device__ __forceinline__ void store_item(const Stage& st, Lds<BLK>& sm, int bu
   }
 }
 
+// Combine lane c with lane c+32 (the two key halves of one query) with the
+// gfx950 cross-half swap: with both operands x, the two results hold
+// x[0..31] and x[32..63] on every lane.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+}
+
 // Per-wave online-softmax state for 32 query rows.
 template <int BLK>
 struct WaveState {
@@ -238,40 +319,53 @@ struct WaveState {
   float l;                   // this lane's partial row sum
 };
 
+// Item kinds: a selected key block off the diagonal (all keys visible), the
+// diagonal block (causal mask inside tile kt_lim), or a chunk of pooled
+// columns (logit s*sl2 + bias[col]; columns past the chunk end have bias
+// -inf). Each kind is its own instantiation so the common case carries no
+// per-score masking or bias work.
+enum ItemKind { kExact = 0, kDiag = 1, kPooled = 2 };
+
 // One item for one wave, processed in 64-key halves (each: QK^T of two
 // 32-key tiles, online-softmax update, PV), which keeps 32 score registers
-// live instead of 64. kt_lim: last 32-key tile that is not fully masked (-1:
-// none). diag: causal mask inside tile kt_lim (tq = query offset). pooled:
-// logit s*sl2 + bias[col].
-template <int BLK>
+// live instead of 64. kt_lim: last 32-key tile that is not fully masked.
+template <int BLK, int KIND>
 __device__ __forceinline__ void attend_item(WaveState<BLK>& ws, const uint16_t* kb, const uint16_t* vt,
-                                            const float* bias, int kt_lim, bool diag, bool pooled, int tq,
-                                            float sl2, int lk, int lv, int hf) {
+                                            const float* bias, int kt_lim_rt, int tq, float sl2, int lk, int lv,
+                                            int hf) {
   constexpr int NKT = BLK / 32;
   constexpr int VP = Lds<BLK>::kVPitch;
+  const int kt_lim = KIND == kExact ? NKT - 1 : kt_lim_rt;
 #pragma unroll
   for (int hh = 0; hh < NKT / 2; ++hh) {
-    if (2 * hh > kt_lim) break;
+    if (KIND != kExact && 2 * hh > kt_lim) break;
+    // Tile 2hh+1 of a half is skipped when it lies past kt_lim (diagonal or
+    // short pooled chunk); its scores are then never read.
+    const bool two = KIND == kExact || 2 * hh + 1 <= kt_lim;
     f32x16 s[2];
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
       const int kt = 2 * hh + t2;
-      f32x16 acc = {};
-      if (kt <= kt_lim) {
-        const uint16_t* base = kb + lk + kt * 32 * kKPitch;
-#pragma unroll
-        for (int ks = 0; ks < kHeadDim / 16; ++ks)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(base + ks * 16),
-                                                        ws.qf[ks], acc, 0, 0, 0);
+      if (t2 == 1 && !two) {
+        s[1] = f32x16{};
+        continue;
       }
+      const uint16_t* base = kb + lk + kt * 32 * kKPitch;
+      f32x16 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(base), ws.qf[0],
+                                                           f32x16{}, 0, 0, 0);
+#pragma unroll
+      for (int ks = 1; ks < kHeadDim / 16; ++ks)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(base + ks * 16),
+                                                      ws.qf[ks], acc, 0, 0, 0);
       s[t2] = acc;
     }
-    float mx = kNegBig;
-    if (pooled) {
+    float mx;
+    if constexpr (KIND == kPooled) {
+      mx = kNegBig;
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
         const int kt = 2 * hh + t2;
-        if (kt > kt_lim) continue;
+        if (t2 == 1 && !two) break;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float4 bb = *reinterpret_cast<const float4*>(&bias[kt * 32 + i * 8 + hf * 4]);
@@ -284,23 +378,30 @@ __device__ __forceinline__ void attend_item(WaveState<BLK>& ws, const uint16_t* 
         }
       }
     } else {
+      if constexpr (KIND == kDiag) {
+        // Mask keys past the query in tile kt_lim (the only partial tile).
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          const int kt = 2 * hh + t2;
+          if (kt == kt_lim) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+              for (int jj = 0; jj < 4; ++jj)
+                if (kt * 32 + i * 8 + hf * 4 + jj > tq) s[t2][4 * i + jj] = -INFINITY;
+          }
+        }
+      }
+      mx = kNegBig;
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
-        const int kt = 2 * hh + t2;
-        if (kt > kt_lim) continue;
-        if (diag && kt == kt_lim) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-              if (kt * 32 + i * 8 + hf * 4 + jj > tq) s[t2][4 * i + jj] = -INFINITY;
-        }
+        if (t2 == 1 && !two) break;
 #pragma unroll
         for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[t2][e]);
       }
       mx *= sl2;
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_halves(mx);
     // Lazy running max (see the file header).
     const float m_new = mx > ws.m + kSlack ? mx : ws.m;
     if (__ballot(m_new != ws.m) != 0) {
@@ -310,22 +411,21 @@ __device__ __forceinline__ void attend_item(WaveState<BLK>& ws, const uint16_t* 
       for (int dt = 0; dt < kHeadDim / 32; ++dt) ws.o[dt] *= corr;
     }
     ws.m = m_new;
-    const float sc = pooled ? 1.0f : sl2;
+    const float sc = KIND == kPooled ? 1.0f : sl2;
     const float neg_m = -m_new;
-    float lsum = 0.f;
+    float lsum0 = 0.f;
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
       const int kt = 2 * hh + t2;
-      if (kt > kt_lim) continue;
+      if (t2 == 1 && !two) break;
       bf16x8 pf[2];
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         float pv[8];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          pv[t] = __builtin_amdgcn_exp2f(fmaf(s[t2][8 * s2 + t], sc, neg_m));
-          lsum += pv[t];
-        }
+        for (int t = 0; t < 8; ++t) pv[t] = __builtin_amdgcn_exp2f(fmaf(s[t2][8 * s2 + t], sc, neg_m));
+#pragma unroll
+        for (int t = 0; t < 8; ++t) lsum0 += pv[t];
         const bf16x4 lo = __builtin_convertvector(f32x4{pv[0], pv[1], pv[2], pv[3]}, bf16x4);
         const bf16x4 hi = __builtin_convertvector(f32x4{pv[4], pv[5], pv[6], pv[7]}, bf16x4);
         pf[s2] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -343,7 +443,7 @@ __device__ __forceinline__ void attend_item(WaveState<BLK>& ws, const uint16_t* 
         }
       }
     }
-    ws.l += lsum;
+    ws.l += lsum0;
   }
 }
 
@@ -394,7 +494,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   const int64_t row = (int64_t)rc.h * p.NB_tot + rt.blk_off[rc.r] + I;
   rc.n_exact = p.dense ? I + 1 : p.row_ptr[row + 1] - p.row_ptr[row];
   rc.cols = p.dense ? nullptr : p.col_idx + p.row_ptr[row];
-  rc.ccols = sm.colcache;
   const bool do_corr = p.mean_correction && !p.dense && I > 0;
   rc.n_items = rc.n_exact + (do_corr ? (I + kPC - 1) / kPC : 0);
   rc.pooled_base = ((int64_t)rc.h * p.NB_tot + rt.blk_off[rc.r]) * kHeadDim;
@@ -447,7 +546,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
     __syncthreads();
     if (do_corr) {
       for (int e = tid; e < rc.n_exact; e += kThreads) {
-        const int J = e < kColCache ? sm.colcache[e] : rc.cols[e];
+        const int J = e < kColCache ? lload_i32(sm.colcache + e) : gload_i32(rc.cols + e);
         atomicOr(&sm.selbits[J >> 5], 1u << (J & 31));
       }
     }
@@ -456,26 +555,34 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
 
   const int N = rc.n_items;
   Stage st;
-  load_item<BLK, FP8, PAGED>(st, p, rc, 0, tid);
-  store_item<BLK>(st, sm, 0, rc, 0, tid);
+  load_item<BLK, FP8, PAGED>(st, p, rc, sm.colcache, 0, tid);
+  store_item<BLK, FP8>(st, sm, 0, rc, 0, tid);
   __syncthreads();
   for (int e = 0; e < N; ++e) {
     const int buf = e & 1;
-    if (e + 1 < N) load_item<BLK, FP8, PAGED>(st, p, rc, e + 1, tid);
+    // The thread index is laundered per item so the per-slot address terms
+    // are recomputed (a few integer ops) instead of being held in registers
+    // across the whole loop.
+    int tid_l = tid;
+    asm volatile("" : "+v"(tid_l));
+    if (e + 1 < N) load_item<BLK, FP8, PAGED>(st, p, rc, sm.colcache, e + 1, tid_l);
     if (wave_active) {
-      const bool pooled = e >= rc.n_exact;
-      const bool diag = e == rc.n_exact - 1;
-      int kt_lim = NKT - 1;
-      if (diag) kt_lim = tq0 >> 5;
-      if (pooled) kt_lim = (min(kPC, I - (e - rc.n_exact) * kPC) - 1) >> 5;
-      attend_item<BLK>(ws, sm.k[buf], sm.vt[buf], sm.bias[buf], kt_lim, diag, pooled, tq, sl2, lk, lv, hf);
+      if (e < rc.n_exact - 1)
+        attend_item<BLK, kExact>(ws, sm.k[buf], sm.vt[buf], sm.bias[buf], NKT - 1, tq, sl2, lk, lv, hf);
+      else if (e == rc.n_exact - 1)
+        attend_item<BLK, kDiag>(ws, sm.k[buf], sm.vt[buf], sm.bias[buf], tq0 >> 5, tq, sl2, lk, lv, hf);
+      else
+        attend_item<BLK, kPooled>(ws, sm.k[buf], sm.vt[buf], sm.bias[buf],
+                                  (min(kPC, I - (e - rc.n_exact) * kPC) - 1) >> 5, tq, sl2, lk, lv, hf);
     }
-    if (e + 1 < N) store_item<BLK>(st, sm, buf ^ 1, rc, e + 1, tid);
+    int tid_s = tid;
+    asm volatile("" : "+v"(tid_s));
+    if (e + 1 < N) store_item<BLK, FP8>(st, sm, buf ^ 1, rc, e + 1, tid_s);
     __syncthreads();
   }
 
   if (!wave_active) return;
-  const float l_tot = ws.l + __shfl_xor(ws.l, 32);
+  const float l_tot = sum_halves(ws.l);
   if (q_valid) {
     const float inv = oscale / l_tot;
     uint16_t* orow = p.out + (tok * p.Hq + g) * kHeadDim;

@@ -75,4 +75,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// Loads through explicitly global / LDS pointers. Pointers merged from
+// several sources otherwise become generic (flat) accesses, which count
+// against both the vector-memory and the LDS wait counters and so force a
+// wait for outstanding global loads before every LDS read.
+typedef const __attribute__((address_space(1))) u32x4 g_u32x4;
+typedef const __attribute__((address_space(1))) int32_t g_int32;
+typedef const __attribute__((address_space(1))) uint8_t g_uint8;
+typedef const __attribute__((address_space(1))) float g_float;
+typedef const __attribute__((address_space(3))) int32_t l_int32;
+__device__ __forceinline__ uint4 gload16(g_u32x4* p) { return __builtin_bit_cast(uint4, *p); }
+__device__ __forceinline__ int32_t gload_i32(const int32_t* p) { return *(g_int32*)(p); }
+__device__ __forceinline__ int32_t lload_i32(const int32_t* p) { return *(l_int32*)(p); }
+
 }  // namespace fpv2
