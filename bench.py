@@ -27,6 +27,45 @@ PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # MI355X dense MFMA peaks
 HBM_PEAK_GBS = 8000.0
 
 
+# rocprofv3 HBM counters of the attention kernel are recorded in this file
+# together with a hash of the kernel's sources; the benchmark reports them as
+# roofline.traffic only while the sources still hash the same.
+TRAFFIC_RECORD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "attn_kernel_llama128k_bf16.md")
+ATTN_SOURCES = ["attn.hip", "common.h", "launch.h"]
+
+
+def attn_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(os.path.dirname(os.path.abspath(__file__)), "block_sparse_long_fp_amd", "csrc")
+    for name in ATTN_SOURCES:
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload, alpha):
+    """HBM bytes per attention launch from the recorded FETCH_SIZE / WRITE_SIZE
+    counters (KiB per dispatch, scaled by the copy-calibration factors), or None
+    when no record matches this workload and the current kernel sources."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            lines = [ln.strip() for ln in f if ln.strip().startswith("traffic-record:")]
+    except OSError:
+        return None
+    src = attn_source_hash()
+    for ln in lines:
+        kv = dict(tok.split("=", 1) for tok in ln.split()[1:] if "=" in tok)
+        try:
+            if (kv.get("source_sha256") == src and kv.get("workload") == workload
+                    and abs(float(kv.get("alpha", "nan")) - alpha) < 1e-9):
+                return (float(kv["fetch_kib"]) * float(kv["fetch_scale"])
+                        + float(kv["write_kib"]) * float(kv["write_scale"])) * 1024.0
+        except (KeyError, ValueError):
+            continue
+    return None
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -278,7 +317,7 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": achieved / peak,
-            "traffic": None,
+            "traffic": recorded_traffic(args.workload, wl.alpha),
             "kernel": "attn_kernel (fp_sparse_prefill)",
         },
         "wall_s_timed": wall,
