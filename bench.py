@@ -233,7 +233,7 @@ def main():
         if ev is not None:
             ev[2].record()
         fp.sparse_prefill(prob, att, q, k, v, bufs.k_bar, bufs.v_bar, bufs.row_ptr, bufs.col_idx, bufs.out,
-                          bufs.lse)
+                          bufs.lse, bufs.attn_workspace)
         if ev is not None:
             ev[3].record()
 
@@ -266,10 +266,12 @@ def main():
     dense_ms = None
     if not args.no_dense:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        fp.dense_prefill(prob, att, q, k, v, bufs.out, bufs.lse)
+        dws = fp.attn_workspace_bytes(prob, False)
+        dws = torch.empty(dws, dtype=torch.uint8, device="cuda:0") if dws else None
+        fp.dense_prefill(prob, att, q, k, v, bufs.out, bufs.lse, dws)
         torch.cuda.synchronize()
         e0.record()
-        fp.dense_prefill(prob, att, q, k, v, bufs.out, bufs.lse)
+        fp.dense_prefill(prob, att, q, k, v, bufs.out, bufs.lse, dws)
         e1.record()
         torch.cuda.synchronize()
         dense_ms = e0.elapsed_time(e1)

@@ -9,7 +9,7 @@ Entry points mirror the C ABI in include/fpv2.h:
   pool_blocks, select_blocks, sparse_prefill, dense_prefill
 plus the convenience ``prefill`` that allocates outputs and runs all three
 stages, and the host-only ``index_shape`` / ``select_workspace_bytes`` /
-``validate``.
+``attn_workspace_bytes`` / ``validate``.
 """
 from __future__ import annotations
 
@@ -87,10 +87,12 @@ def lib() -> ctypes.CDLL:
         L.fp_pool_blocks.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
         L.fp_select_blocks.argtypes = [P, ctypes.POINTER(_SelectArgs), vp, vp, vp, vp, ctypes.c_int64, vp,
                                        ctypes.c_size_t, vp]
-        L.fp_sparse_prefill.argtypes = [P, ctypes.POINTER(_AttnArgs), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
-        L.fp_dense_prefill.argtypes = [P, ctypes.POINTER(_AttnArgs), vp, vp, vp, vp, vp, vp]
-        for f in ("fp_index_shape", "fp_select_workspace_bytes", "fp_validate", "fp_pool_blocks", "fp_select_blocks",
-                  "fp_sparse_prefill", "fp_dense_prefill"):
+        L.fp_attn_workspace_bytes.argtypes = [P, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+        L.fp_sparse_prefill.argtypes = [P, ctypes.POINTER(_AttnArgs), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                        ctypes.c_size_t, vp]
+        L.fp_dense_prefill.argtypes = [P, ctypes.POINTER(_AttnArgs), vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        for f in ("fp_index_shape", "fp_select_workspace_bytes", "fp_attn_workspace_bytes", "fp_validate",
+                  "fp_pool_blocks", "fp_select_blocks", "fp_sparse_prefill", "fp_dense_prefill"):
             getattr(L, f).restype = ctypes.c_int32
         L.fp_status_string.argtypes = [ctypes.c_int32]
         L.fp_status_string.restype = ctypes.c_char_p
@@ -163,6 +165,21 @@ def select_workspace_bytes(prob: Problem) -> int:
     return n.value
 
 
+def attn_workspace_bytes(prob: Problem, sparse: bool = True) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().fp_attn_workspace_bytes(prob.ref, 1 if sparse else 0, ctypes.byref(n)))
+    return n.value
+
+
+def _attn_workspace(prob: Problem, sparse: bool, workspace, device):
+    """The caller's workspace, or a fresh torch allocation of the needed size."""
+    if workspace is None:
+        n = attn_workspace_bytes(prob, sparse)
+        if n > 0:
+            workspace = torch.empty(n, dtype=torch.uint8, device=device)
+    return workspace
+
+
 def select_args(alpha: float, sel_scale: float = 1.0, min_sparse_len: int = 0) -> _SelectArgs:
     return _SelectArgs(alpha, sel_scale, min_sparse_len)
 
@@ -188,15 +205,22 @@ def select_blocks(prob: Problem, sel: _SelectArgs, q_bar, k_bar, row_ptr, col_id
 
 
 def sparse_prefill(prob: Problem, attn: _AttnArgs, q, k, v, k_bar, v_bar, row_ptr, col_idx, out, lse=None,
-                   stream=None):
+                   workspace=None, stream=None):
+    """fp_sparse_prefill; ``workspace`` (uint8 device tensor of at least
+    attn_workspace_bytes(prob, True) bytes) is allocated here when None."""
+    workspace = _attn_workspace(prob, True, workspace, out.device)
+    nbytes = 0 if workspace is None else workspace.numel()
     _check(lib().fp_sparse_prefill(prob.ref, ctypes.byref(attn), _ptr(q), _ptr(k), _ptr(v), _ptr(k_bar),
                                    _ptr(v_bar), _ptr(row_ptr), _ptr(col_idx), _ptr(out), _ptr(lse),
-                                   _stream(stream)))
+                                   _ptr(workspace), nbytes, _stream(stream)))
 
 
-def dense_prefill(prob: Problem, attn: _AttnArgs, q, k, v, out, lse=None, stream=None):
+def dense_prefill(prob: Problem, attn: _AttnArgs, q, k, v, out, lse=None, workspace=None, stream=None):
+    """fp_dense_prefill; ``workspace`` as in sparse_prefill (only FP8 needs one)."""
+    workspace = _attn_workspace(prob, False, workspace, out.device)
+    nbytes = 0 if workspace is None else workspace.numel()
     _check(lib().fp_dense_prefill(prob.ref, ctypes.byref(attn), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
-                                  _stream(stream)))
+                                  _ptr(workspace), nbytes, _stream(stream)))
 
 
 class Buffers:
@@ -214,6 +238,8 @@ class Buffers:
         self.row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=device)
         self.col_idx = torch.empty(max(nnz, 1), dtype=torch.int32, device=device)
         self.workspace = torch.empty(select_workspace_bytes(prob), dtype=torch.uint8, device=device)
+        self.attn_workspace = torch.empty(max(attn_workspace_bytes(prob, True), 1), dtype=torch.uint8,
+                                          device=device)
         self.out = torch.empty((T, Hq, head_dim), dtype=torch.bfloat16, device=device)
         self.lse = torch.empty((Hq, T), **f32)
 
@@ -225,7 +251,7 @@ def run_prefill(prob: Problem, bufs: Buffers, q, k, v, alpha: float, sel_scale: 
     select_blocks(prob, select_args(alpha, sel_scale, min_sparse_len), bufs.q_bar, bufs.k_bar, bufs.row_ptr,
                   bufs.col_idx, bufs.workspace, stream)
     sparse_prefill(prob, attn_args(sm_scale, mean_correction), q, k, v, bufs.k_bar, bufs.v_bar, bufs.row_ptr,
-                   bufs.col_idx, bufs.out, bufs.lse, stream)
+                   bufs.col_idx, bufs.out, bufs.lse, bufs.attn_workspace, stream)
     return bufs
 
 

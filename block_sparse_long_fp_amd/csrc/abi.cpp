@@ -151,12 +151,32 @@ WsLayout ws_layout(const fp_problem* p, const Shape& s) {
   return w;
 }
 
+// Attention workspace: bf16 k_bar, v_bar (sparse calls) and, for FP8, bf16
+// copies of the K and V codes in the caller's layout.
+struct AttnWs {
+  size_t kbar16, vbar16, kk, vv, total;
+  int64_t kv_elems;
+};
+
+AttnWs attn_ws_layout(const fp_problem* p, const Shape& s, bool sparse) {
+  AttnWs w{};
+  const int64_t kv_rows = p->kv_layout == FP_KV_PAGED ? (int64_t)p->num_pages * p->page_size : s.T;
+  w.kv_elems = kv_rows * p->num_kv_heads * p->head_dim;
+  const size_t pool = sparse ? align256((size_t)p->num_kv_heads * s.NB_tot * p->head_dim * 2) : 0;
+  const size_t kv = p->dtype == FP_FP8_E4M3 ? align256((size_t)w.kv_elems * 2) : 0;
+  w.kbar16 = 0;
+  w.vbar16 = pool;
+  w.kk = 2 * pool;
+  w.vv = 2 * pool + kv;
+  w.total = 2 * pool + 2 * kv;
+  return w;
+}
+
 fp_status hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(FP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return ok();
 }
 
-int rows_per_wg() { return 256; }
 
 }  // namespace
 
@@ -178,6 +198,15 @@ fp_status fp_select_workspace_bytes(const fp_problem* p, size_t* bytes) {
   if (st) return st;
   if (!bytes) return fail(FP_ERR_NULL, "bytes is NULL");
   *bytes = ws_layout(p, s).total;
+  return ok();
+}
+
+fp_status fp_attn_workspace_bytes(const fp_problem* p, int32_t sparse, size_t* bytes) {
+  Shape s;
+  fp_status st = check_problem(p, &s);
+  if (st) return st;
+  if (!bytes) return fail(FP_ERR_NULL, "bytes is NULL");
+  *bytes = attn_ws_layout(p, s, sparse != 0).total;
   return ok();
 }
 
@@ -240,7 +269,8 @@ fp_status fp_select_blocks(const fp_problem* p, const fp_select_args* sel, const
 
 static fp_status run_attention(const fp_problem* p, const fp_attn_args* attn, const void* q, const void* k,
                                const void* v, const float* k_bar, const float* v_bar, const int32_t* row_ptr,
-                               const int32_t* col_idx, void* out, float* lse, void* stream, bool dense) {
+                               const int32_t* col_idx, void* out, float* lse, void* workspace,
+                               size_t workspace_bytes, void* stream, bool dense) {
   Shape s;
   fp_status st = check_problem(p, &s);
   if (st) return st;
@@ -251,8 +281,20 @@ static fp_status run_attention(const fp_problem* p, const fp_attn_args* attn, co
     if (attn->mean_correction && (!k_bar || !v_bar))
       return fail(FP_ERR_NULL, "fp_sparse_prefill: mean correction needs k_bar and v_bar");
   }
+  const AttnWs aw = attn_ws_layout(p, s, !dense);
+  if (aw.total > 0 && (!workspace || workspace_bytes < aw.total))
+    return fail(FP_ERR_WORKSPACE, "attention workspace %zu bytes < %zu needed", workspace ? workspace_bytes : (size_t)0,
+                aw.total);
+  char* ws = static_cast<char*>(workspace);
   AttnParams ap{};
   ap.q = q; ap.k = k; ap.v = v;
+  const bool fp8 = p->dtype == FP_FP8_E4M3;
+  ap.kk = fp8 ? static_cast<const void*>(ws + aw.kk) : k;
+  ap.vv = fp8 ? static_cast<const void*>(ws + aw.vv) : v;
+  ap.kv_elems = aw.kv_elems;
+  const bool pooled = !dense && attn->mean_correction;
+  ap.kbar16 = pooled ? reinterpret_cast<uint16_t*>(ws + aw.kbar16) : nullptr;
+  ap.vbar16 = pooled ? reinterpret_cast<uint16_t*>(ws + aw.vbar16) : nullptr;
   ap.k_bar = k_bar; ap.v_bar = v_bar; ap.row_ptr = row_ptr; ap.col_idx = col_idx;
   ap.out = static_cast<uint16_t*>(out);
   ap.lse = lse;
@@ -262,7 +304,7 @@ static fp_status run_attention(const fp_problem* p, const fp_attn_args* attn, co
   ap.B = p->block_size; ap.NB_tot = (int32_t)s.NB_tot; ap.T = (int32_t)s.T;
   ap.mean_correction = dense ? 0 : attn->mean_correction;
   ap.dense = dense ? 1 : 0;
-  ap.subs = (ap.G * ap.B + rows_per_wg() - 1) / rows_per_wg();
+  ap.subs = (ap.G * ap.B + attn_rows_per_wg() - 1) / attn_rows_per_wg();
   ap.fp8 = p->dtype == FP_FP8_E4M3;
   ap.kv = make_kv(p);
   ap.rt = make_table(p, s);
@@ -271,13 +313,17 @@ static fp_status run_attention(const fp_problem* p, const fp_attn_args* attn, co
 
 fp_status fp_sparse_prefill(const fp_problem* p, const fp_attn_args* attn, const void* q, const void* k,
                             const void* v, const float* k_bar, const float* v_bar, const int32_t* row_ptr,
-                            const int32_t* col_idx, void* out, float* lse, void* stream) {
-  return run_attention(p, attn, q, k, v, k_bar, v_bar, row_ptr, col_idx, out, lse, stream, false);
+                            const int32_t* col_idx, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  return run_attention(p, attn, q, k, v, k_bar, v_bar, row_ptr, col_idx, out, lse, workspace, workspace_bytes,
+                       stream, false);
 }
 
 fp_status fp_dense_prefill(const fp_problem* p, const fp_attn_args* attn, const void* q, const void* k,
-                           const void* v, void* out, float* lse, void* stream) {
-  return run_attention(p, attn, q, k, v, nullptr, nullptr, nullptr, nullptr, out, lse, stream, true);
+                           const void* v, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  return run_attention(p, attn, q, k, v, nullptr, nullptr, nullptr, nullptr, out, lse, workspace, workspace_bytes,
+                       stream, true);
 }
 
 const char* fp_status_string(fp_status s) {

@@ -18,32 +18,36 @@
 //   * Transposed products keep every lane on one query: S^T = K Q^T and
 //     O^T = V^T P^T with v_mfma_f32_32x32x16_bf16. A lane (column c, half hf)
 //     holds the scores and output dims of query c, so row max and row sum are
-//     in-lane plus one exchange with lane c+32, and the probabilities feed the
-//     PV product straight from registers (the PV contraction index is
-//     relabelled to match the score accumulator layout; V^T is read from LDS
-//     with the same relabelling).
-//   * Work items: the CSR row's key blocks (B keys), then correction chunks of
-//     64 pooled columns whose per-column bias log2(n_J) or -inf masks selected
-//     and non-causal blocks (from an LDS bitmap of the row). Every item
-//     reaches LDS as bf16 K rows and bf16 V^T columns, so the MFMA code has
-//     one path.
-//   * Staging: the next item's K and V pass through 32 registers per thread
-//     (loaded before the current item is computed, stored after it) into
-//     double-buffered LDS, with one workgroup barrier per item. K is
-//     row-major with a 272-byte pitch, V^T has a (B+4)-element pitch: MFMA
-//     operand reads of consecutive rows are bank-conflict free and use
-//     base + immediate addresses. Stores are mapped key-group-fastest so each
-//     32-lane pass writes one contiguous row segment (no conflicts).
-//   * Wave-uniform quantities live in scalar registers, so per-item and
-//     per-tile decisions are scalar branches.
-//   * Online softmax in base 2, updated per 64-key half of an item (32 score
-//     registers live, which keeps the kernel within 256 VGPRs without
-//     spills): max on raw scores, one fma + exp2 per score, fp32 row sums. The running max only moves when a block's max exceeds it
-//     by more than 8 (probabilities stay below 256, exact after the final
-//     division), which makes output rescales rare.
+//     in-lane plus one v_permlane32_swap, and the probabilities feed the PV
+//     product straight from registers (the PV contraction index is relabelled
+//     to match the score accumulator layout).
+//   * Work items: the CSR row's key blocks, then correction chunks of 64
+//     pooled columns whose per-column bias log2(n_J) or -inf masks selected
+//     and non-causal blocks (from an LDS bitmap of the row). Exact, diagonal
+//     and pooled items are separate instantiations of the item code.
+//   * Staging is direct HBM -> LDS (buffer_load ... lds / global_load_lds,
+//     16 bytes per lane) into double-buffered tiles, so no registers carry
+//     K or V. A tile stores rows in groups of four: group g (rows 4g..4g+3)
+//     occupies 1088 bytes, chunk-major (16-byte chunk c of row 4g+i at
+//     64c + 16i) with 64 bytes of padding, which is exactly the order one
+//     wave's 1 KiB DMA writes when lane l fetches chunk l/4 of row 4g + l%4.
+//     K operand reads (16 bytes: row, chunk 2ks+hf) are then base + 128 ks
+//     immediates, and V^T operands come from the gfx950 transposing read
+//     ds_read_b64_tr_b16 (lane j of a 16-lane group reads 4 dims of one key;
+//     the hardware hands lane i dim i of 4 consecutive keys), also at
+//     immediate offsets; both are bank-conflict free.
+//   * Pooled items read bf16 copies of k_bar, v_bar (scaled to code units for
+//     FP8) that a small conversion kernel writes into the workspace; FP8 K/V
+//     codes are converted the same way (exactly, code -> bf16), so the
+//     attention kernel itself runs one bf16 path.
+//   * Online softmax in base 2, updated per 64-key half of an item: max on
+//     raw scores, one fma + exp2 per score, fp32 row sums. The running max
+//     only moves when a half's max exceeds it by more than 8 (probabilities
+//     stay below 256, exact after the final division), so output rescales are
+//     rare.
 //   * Workgroups run heaviest first (query block index descending over the
 //     ragged batch), and consecutive ids cycle over KV heads so the
-//     round-robin XCD dispatch keeps one KV head's blocks in one XCD's L2.
+//     round-robin XCD dispatch spreads each head's K/V over the L2s.
 #include "common.h"
 #include "launch.h"
 
@@ -55,40 +59,32 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kRowsPerWG = kWaves * 32;
 constexpr int kPC = 64;                 // pooled columns per correction item
-constexpr int kKPitch = kHeadDim + 8;   // bf16 elements per K row in LDS (272 B)
+constexpr int kQuad = 4 * 256 + 64;     // LDS bytes of a group of four 256-byte rows
 constexpr int kColCache = 1024;         // CSR columns cached in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegBig = -1.0e30f;
 constexpr float kSlack = 8.0f;          // lazy-rescale threshold of the running max (log2)
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef __attribute__((address_space(1))) void* gbl_ptr;
+
 template <int BLK>
-struct Lds {
-  static constexpr int kVPitch = BLK + 4;  // bf16 elements per V^T row
-  uint16_t k[2][BLK * kKPitch];
-  uint16_t vt[2][kHeadDim * kVPitch];
-  float bias[2][kPC];
-  uint32_t selbits[FP_MAX_BLOCKS_PER_SEQ / 32];
-  int32_t colcache[kColCache];
+struct Tile {
+  static constexpr int kBytes = BLK / 4 * kQuad;
+  static constexpr int kWords = kBytes / 16;
 };
 
-// Load 8 consecutive elements (bf16 or fp8) as 8 bf16 in a uint4.
-template <bool FP8>
-__device__ __forceinline__ uint4 load8_as_bf16(const void* base, int64_t elem) {
-  if constexpr (FP8) {
-    const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(base) + elem);
-    uint4 o;
-    o.x = pack_bf16x2(e4m3_to_float(w.x & 0xFF), e4m3_to_float((w.x >> 8) & 0xFF));
-    o.y = pack_bf16x2(e4m3_to_float((w.x >> 16) & 0xFF), e4m3_to_float(w.x >> 24));
-    o.z = pack_bf16x2(e4m3_to_float(w.y & 0xFF), e4m3_to_float((w.y >> 8) & 0xFF));
-    o.w = pack_bf16x2(e4m3_to_float((w.y >> 16) & 0xFF), e4m3_to_float(w.y >> 24));
-    return o;
-  } else {
-    return *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + elem);
-  }
-}
-
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Buffer resource for raw 16-byte loads: base, byte range [0, num_records).
+// Lanes whose offset lies past the range read zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, int num_records) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, num_records, 0x00020000);
+}
 
 // Per-workgroup constants of the row being processed (all wave-uniform).
 struct RowCtx {
@@ -96,206 +92,9 @@ struct RowCtx {
   int n_exact;          // CSR entries (key blocks) of the row
   int n_items;          // plus the correction chunks
   const int32_t* cols;  // CSR row (nullptr in dense mode)
-  int64_t pooled_base;  // element offset of the k_bar/v_bar row (h, blk_off[r])
+  int64_t pooled_row0;  // row h * NB_tot + blk_off[r] of k_bar / v_bar
   int64_t tok_base;     // first token of the request
-  float kscale;         // pooled k_bar -> LDS scale (1/descale_k for FP8)
-  float vscale;         // pooled v_bar -> LDS scale (1/descale_v for FP8)
 };
-
-// Element offset of key `row` of block J (request-local token J*B+row, clamped
-// to the request's last token) of the row's KV head.
-template <int BLK, bool PAGED>
-__device__ __forceinline__ int64_t kv_off(const AttnParams& p, const RowCtx& rc, int J, int row) {
-  const int rr = min(row, rc.L - 1 - J * BLK);
-  if constexpr (!PAGED) {
-    const int64_t base = ((rc.tok_base + (int64_t)J * BLK) * p.Hkv + rc.h) * kHeadDim;
-    return base + (int64_t)(rr * (p.Hkv * kHeadDim));
-  } else {
-    const int t = J * BLK + rr;
-    const int page = p.kv.page_table[(int64_t)rc.r * p.kv.max_pages + t / p.kv.page_size];
-    return (((int64_t)page * p.kv.page_size + (t % p.kv.page_size)) * p.Hkv + rc.h) * kHeadDim;
-  }
-}
-
-// Staging of one item from HBM to LDS: every thread issues the same eight
-// 16-byte loads (stage slots) from one straight-line sequence whatever the
-// item kind (only the addresses are chosen per kind), so the loads stay in
-// flight while the current item is computed and no register copies merge
-// them afterwards. Slot plans, with E = elements per 16 bytes (8 bf16 or
-// 16 fp8) and C = d / E loads per key row:
-//   exact K: slot u < KL holds row tid/C + (512/C)u, elements E(tid%C)..;
-//            KL = B*C/512 (bf16: 4 at B=128, 2 at B=64; fp8: 2 or 1).
-//   exact V: slot 4+i (i < KL) holds key KL*kg + i (kg = tid % (B/KL)),
-//            elements E(tid / (B/KL)).., so each thread owns KL consecutive
-//            keys of E dims and writes V^T rows directly.
-//   Unused exact slots repeat a used address (the load hits the same line).
-//   pooled K: slots 2u, 2u+1 hold fp32 row tid/16 + 32u (u < 2), dims 8(tid%16)..
-//   pooled V: slots 4+2i, 5+2i hold fp32 column 2kg+i (kg = tid%32), dims 8(tid/32)..
-struct Stage {
-  uint4 x[8];
-};
-
-template <int BLK, bool FP8>
-struct ExactPlan {
-  static constexpr int E = FP8 ? 16 : 8;
-  static constexpr int C = kHeadDim / E;
-  static constexpr int KL = BLK * C / kThreads;
-  static constexpr int KG = BLK / KL;
-  static_assert(KL >= 1 && KL <= 4 && KG * C == kThreads, "exact staging plan");
-};
-
-template <int BLK, bool FP8, bool PAGED>
-__device__ __forceinline__ void load_item(Stage& st, const AttnParams& p, const RowCtx& rc, const int32_t* colcache,
-                                          int e, int tid) {
-  using P = ExactPlan<BLK, FP8>;
-  g_u32x4* src[8];  // global address space, so the loads stay global (not flat)
-  if (e < rc.n_exact) {
-    const int J = !rc.cols ? e : uniform(e < kColCache ? lload_i32(colcache + e) : gload_i32(rc.cols + e));
-    g_uint8* kbase = (g_uint8*)p.k;
-    g_uint8* vbase = (g_uint8*)p.v;
-    constexpr int eb = FP8 ? 1 : 2;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int uu = u % P::KL;
-      const int64_t off = kv_off<BLK, PAGED>(p, rc, J, tid / P::C + (kThreads / P::C) * uu) + (tid % P::C) * P::E;
-      src[u] = (g_u32x4*)(kbase + off * eb);
-    }
-    const int kg = tid % P::KG, dc = tid / P::KG;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ii = i % P::KL;
-      const int64_t off = kv_off<BLK, PAGED>(p, rc, J, kg * P::KL + ii) + dc * P::E;
-      src[4 + i] = (g_u32x4*)(vbase + off * eb);
-    }
-  } else {
-    const int c0 = (e - rc.n_exact) * kPC;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int Jp = min(c0 + (tid >> 4) + 32 * u, rc.I - 1);
-      g_u32x4* s = (g_u32x4*)((g_float*)p.k_bar + rc.pooled_base + (int64_t)Jp * kHeadDim + (tid & 15) * 8);
-      src[2 * u] = s;
-      src[2 * u + 1] = s + 1;
-    }
-    const int kg = tid & 31, dc = tid >> 5;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int Jp = min(c0 + kg * 2 + i, rc.I - 1);
-      g_u32x4* s = (g_u32x4*)((g_float*)p.v_bar + rc.pooled_base + (int64_t)Jp * kHeadDim + dc * 8);
-      src[4 + 2 * i] = s;
-      src[5 + 2 * i] = s + 1;
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) st.x[i] = gload16(src[i]);
-}
-
-__device__ __forceinline__ uint4 cvt8(const uint4 a4, const uint4 b4, float s) {
-  const float4 a = __builtin_bit_cast(float4, a4), b = __builtin_bit_cast(float4, b4);
-  uint4 o;
-  o.x = pack_bf16x2(a.x * s, a.y * s);
-  o.y = pack_bf16x2(a.z * s, a.w * s);
-  o.z = pack_bf16x2(b.x * s, b.y * s);
-  o.w = pack_bf16x2(b.z * s, b.w * s);
-  return o;
-}
-
-// The 16 e4m3 codes of a slot as 16 floats (exact).
-__device__ __forceinline__ void fp8x16_to_float(const uint4 w, float (&f)[16]) {
-  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) f[4 * q + b] = e4m3_to_float((ws[q] >> (8 * b)) & 0xFFu);
-}
-
-template <int BLK, bool FP8>
-__device__ __forceinline__ void store_item(const Stage& st, Lds<BLK>& sm, int buf, const RowCtx& rc, int e, int tid) {
-  using P = ExactPlan<BLK, FP8>;
-  constexpr int VP = Lds<BLK>::kVPitch;
-  uint16_t* kb = sm.k[buf];
-  uint16_t* vt = sm.vt[buf];
-  if (e < rc.n_exact) {
-#pragma unroll
-    for (int u = 0; u < P::KL; ++u) {
-      uint16_t* d = &kb[(tid / P::C + (kThreads / P::C) * u) * kKPitch + (tid % P::C) * P::E];
-      if constexpr (!FP8) {
-        *reinterpret_cast<uint4*>(d) = st.x[u];
-      } else {
-        float f[16];
-        fp8x16_to_float(st.x[u], f);
-        uint4 lo, hi;
-        lo.x = pack_bf16x2(f[0], f[1]);
-        lo.y = pack_bf16x2(f[2], f[3]);
-        lo.z = pack_bf16x2(f[4], f[5]);
-        lo.w = pack_bf16x2(f[6], f[7]);
-        hi.x = pack_bf16x2(f[8], f[9]);
-        hi.y = pack_bf16x2(f[10], f[11]);
-        hi.z = pack_bf16x2(f[12], f[13]);
-        hi.w = pack_bf16x2(f[14], f[15]);
-        reinterpret_cast<uint4*>(d)[0] = lo;
-        reinterpret_cast<uint4*>(d)[1] = hi;
-      }
-    }
-    const int kg = tid % P::KG, dc = tid / P::KG;
-    uint16_t* d = vt + (dc * P::E) * VP + kg * P::KL;
-    if constexpr (!FP8 && P::KL == 4) {
-      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&st.x[4]);
-      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&st.x[5]);
-      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&st.x[6]);
-      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&st.x[7]);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        uint2 lo, hi;
-        lo.x = __builtin_amdgcn_perm(w1[m], w0[m], 0x05040100u);  // keys 0,1 of dim 2m
-        lo.y = __builtin_amdgcn_perm(w3[m], w2[m], 0x05040100u);  // keys 2,3 of dim 2m
-        hi.x = __builtin_amdgcn_perm(w1[m], w0[m], 0x07060302u);  // dim 2m+1
-        hi.y = __builtin_amdgcn_perm(w3[m], w2[m], 0x07060302u);
-        *reinterpret_cast<uint2*>(d + (2 * m) * VP) = lo;
-        *reinterpret_cast<uint2*>(d + (2 * m + 1) * VP) = hi;
-      }
-    } else if constexpr (!FP8 && P::KL == 2) {
-      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&st.x[4]);
-      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&st.x[5]);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        *reinterpret_cast<uint32_t*>(d + (2 * m) * VP) = __builtin_amdgcn_perm(w1[m], w0[m], 0x05040100u);
-        *reinterpret_cast<uint32_t*>(d + (2 * m + 1) * VP) = __builtin_amdgcn_perm(w1[m], w0[m], 0x07060302u);
-      }
-    } else if constexpr (FP8 && P::KL == 2) {
-      float f0[16], f1[16];
-      fp8x16_to_float(st.x[4], f0);
-      fp8x16_to_float(st.x[5], f1);
-#pragma unroll
-      for (int q = 0; q < 16; ++q) *reinterpret_cast<uint32_t*>(d + q * VP) = pack_bf16x2(f0[q], f1[q]);
-    } else {
-      static_assert(FP8 && P::KL == 1, "exact V staging plan");
-      float f0[16];
-      fp8x16_to_float(st.x[4], f0);
-#pragma unroll
-      for (int q = 0; q < 16; ++q) d[q * VP] = static_cast<uint16_t>(pack_bf16x2(f0[q], 0.f));
-    }
-  } else {
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-      *reinterpret_cast<uint4*>(&kb[((tid >> 4) + 32 * u) * kKPitch + (tid & 15) * 8]) =
-          cvt8(st.x[2 * u], st.x[2 * u + 1], rc.kscale);
-    const int kg = tid & 31, dc = tid >> 5;
-    uint16_t* d = vt + (dc * 8) * VP + kg * 2;
-    const float4 a0 = __builtin_bit_cast(float4, st.x[4]), a1 = __builtin_bit_cast(float4, st.x[5]);
-    const float4 b0 = __builtin_bit_cast(float4, st.x[6]), b1 = __builtin_bit_cast(float4, st.x[7]);
-    const float x0[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-    const float x1[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-    const float s = rc.vscale;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) *reinterpret_cast<uint32_t*>(d + q * VP) = pack_bf16x2(x0[q] * s, x1[q] * s);
-    if (tid < kPC) {
-      const int Jc = (e - rc.n_exact) * kPC + tid;
-      float bv = -INFINITY;
-      if (Jc < rc.I && !((sm.selbits[Jc >> 5] >> (Jc & 31)) & 1u)) bv = __log2f((float)min(BLK, rc.L - Jc * BLK));
-      sm.bias[buf][tid] = bv;
-    }
-  }
-}
 
 // Combine lane c with lane c+32 (the two key halves of one query) with the
 // gfx950 cross-half swap: with both operands x, the two results hold
@@ -312,7 +111,6 @@ __device__ __forceinline__ float sum_halves(float x) {
 // Per-wave online-softmax state for 32 query rows.
 template <int BLK>
 struct WaveState {
-  static constexpr int NKT = BLK / 32;
   bf16x8 qf[kHeadDim / 16];  // B operand of S^T = K Q^T, one per 16-dim step
   f32x16 o[kHeadDim / 32];   // O^T accumulators, one per 32-dim tile
   float m;                   // running max (log2 units)
@@ -326,49 +124,81 @@ struct WaveState {
 // per-score masking or bias work.
 enum ItemKind { kExact = 0, kDiag = 1, kPooled = 2 };
 
+// V^T operand for PV job j of a half (tile 2hh + (j >> 3), MFMA s2 = (j >> 2) & 1,
+// dims 32 (j & 3) ..): keys 16 s2 + 4 hf + 0..3 and + 8..11 of the tile, each
+// four keys one transposing read.
+__device__ __forceinline__ bf16x8 v_operand(const uint8_t* vh, int j) {
+  const uint8_t* a = vh + (j >> 3) * 8 * kQuad + ((j >> 2) & 1) * 4 * kQuad + (j & 3) * 256;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)a);
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(a + 2 * kQuad));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// PV of a half: job j = (tile t2 = j >> 3, s2 = (j >> 2) & 1, dt = j & 3); the
+// four output accumulators rotate, so consecutive MFMAs are independent, and
+// V operands are read DEPTH jobs ahead (the first DEPTH are already in vf).
+template <int NJ, int DEPTH>
+__device__ __forceinline__ void pv_jobs(f32x16 (&o)[kHeadDim / 32], bf16x8 (&vf)[DEPTH], const bf16x8 (&pf)[2][2],
+                                        const uint8_t* vh) {
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    o[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j % DEPTH], pf[j >> 3][(j >> 2) & 1], o[j & 3], 0, 0, 0);
+    if (j + DEPTH < NJ) vf[j % DEPTH] = v_operand(vh, j + DEPTH);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // One item for one wave, processed in 64-key halves (each: QK^T of two
 // 32-key tiles, online-softmax update, PV), which keeps 32 score registers
-// live instead of 64. kt_lim: last 32-key tile that is not fully masked.
+// live instead of 64. Every half computes both of its tiles: on the diagonal
+// the causal mask also covers a tile past the query block's last visible key,
+// and a pooled chunk is one half whose unused columns have bias -inf (their
+// staged rows are zeros), so the code has no data-dependent tile skips.
+// kt_lim (diagonal only): the tile that holds the query's own position.
+// Operand reads run a few MFMAs ahead of their use; the schedule is pinned
+// with scheduling fences because the compiler otherwise places every LDS read
+// right before its MFMA and exposes the LDS latency each time.
 template <int BLK, int KIND>
-__device__ __forceinline__ void attend_item(WaveState<BLK>& ws, const uint16_t* kb, const uint16_t* vt,
-                                            const float* bias, int kt_lim_rt, int tq, float sl2, int lk, int lv,
+__device__ __forceinline__ void attend_item(WaveState<BLK>& ws, const uint8_t* kb, const uint8_t* vt,
+                                            const float* bias, int kt_lim, int tq, float sl2, int lk, int lv,
                                             int hf) {
-  constexpr int NKT = BLK / 32;
-  constexpr int VP = Lds<BLK>::kVPitch;
-  const int kt_lim = KIND == kExact ? NKT - 1 : kt_lim_rt;
+  constexpr int NH = KIND == kPooled ? 1 : BLK / 64;  // halves
+  constexpr int kDepth = 4;                            // operand reads in flight
 #pragma unroll
-  for (int hh = 0; hh < NKT / 2; ++hh) {
-    if (KIND != kExact && 2 * hh > kt_lim) break;
-    // Tile 2hh+1 of a half is skipped when it lies past kt_lim (diagonal or
-    // short pooled chunk); its scores are then never read.
-    const bool two = KIND == kExact || 2 * hh + 1 <= kt_lim;
-    f32x16 s[2];
+  for (int hh = 0; hh < NH; ++hh) {
+    if (KIND == kDiag && 2 * hh > kt_lim) break;
+    // QK^T of tiles 2hh, 2hh+1: jobs alternate between the two accumulation
+    // chains; rows 32kt + c of a tile, the 16 dims of step ks 128 ks bytes
+    // after the lane's first chunk (four-row groups, see the file header).
+    constexpr int NJ = 2 * (kHeadDim / 16);
+    const uint8_t* kh = kb + lk + (2 * hh) * 8 * kQuad;
+    bf16x8 kf[kDepth];
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-      const int kt = 2 * hh + t2;
-      if (t2 == 1 && !two) {
-        s[1] = f32x16{};
-        continue;
-      }
-      const uint16_t* base = kb + lk + kt * 32 * kKPitch;
-      f32x16 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(base), ws.qf[0],
-                                                           f32x16{}, 0, 0, 0);
+    for (int j = 0; j < kDepth; ++j)
+      kf[j] = *reinterpret_cast<const bf16x8*>(kh + (j & 1) * 8 * kQuad + (j >> 1) * 128);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-      for (int ks = 1; ks < kHeadDim / 16; ++ks)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(base + ks * 16),
-                                                      ws.qf[ks], acc, 0, 0, 0);
-      s[t2] = acc;
+    for (int j = 0; j < NJ; ++j) {
+      s[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j % kDepth], ws.qf[j >> 1], s[j & 1], 0, 0, 0);
+      if (j + kDepth < NJ)
+        kf[j % kDepth] =
+            *reinterpret_cast<const bf16x8*>(kh + ((j + kDepth) & 1) * 8 * kQuad + ((j + kDepth) >> 1) * 128);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    float mx;
+    // The first V operands load while the softmax runs.
+    const uint8_t* vh = vt + lv + (2 * hh) * 8 * kQuad;
+    bf16x8 vf[kDepth];
+#pragma unroll
+    for (int j = 0; j < kDepth; ++j) vf[j] = v_operand(vh, j);
+    __builtin_amdgcn_sched_barrier(0);
+    float mx = kNegBig;
     if constexpr (KIND == kPooled) {
-      mx = kNegBig;
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
-        const int kt = 2 * hh + t2;
-        if (t2 == 1 && !two) break;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float4 bb = *reinterpret_cast<const float4*>(&bias[kt * 32 + i * 8 + hf * 4]);
+          const float4 bb = *reinterpret_cast<const float4*>(&bias[t2 * 32 + i * 8 + hf * 4]);
           const float bv[4] = {bb.x, bb.y, bb.z, bb.w};
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
@@ -379,26 +209,21 @@ __device__ __forceinline__ void attend_item(WaveState<BLK>& ws, const uint16_t* 
       }
     } else {
       if constexpr (KIND == kDiag) {
-        // Mask keys past the query in tile kt_lim (the only partial tile).
+        // Keys past the query; only the half holding tile kt_lim has any.
+        if (2 * hh + 1 >= kt_lim) {
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          const int kt = 2 * hh + t2;
-          if (kt == kt_lim) {
+          for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
               for (int jj = 0; jj < 4; ++jj)
-                if (kt * 32 + i * 8 + hf * 4 + jj > tq) s[t2][4 * i + jj] = -INFINITY;
-          }
+                if ((2 * hh + t2) * 32 + i * 8 + hf * 4 + jj > tq) s[t2][4 * i + jj] = -INFINITY;
         }
       }
-      mx = kNegBig;
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        if (t2 == 1 && !two) break;
+      for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
         for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[t2][e]);
-      }
       mx *= sl2;
     }
     mx = max_halves(mx);
@@ -413,37 +238,25 @@ __device__ __forceinline__ void attend_item(WaveState<BLK>& ws, const uint16_t* 
     ws.m = m_new;
     const float sc = KIND == kPooled ? 1.0f : sl2;
     const float neg_m = -m_new;
-    float lsum0 = 0.f;
+    float lsum = 0.f;
+    bf16x8 pf[2][2];
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
-      const int kt = 2 * hh + t2;
-      if (t2 == 1 && !two) break;
-      bf16x8 pf[2];
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         float pv[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) pv[t] = __builtin_amdgcn_exp2f(fmaf(s[t2][8 * s2 + t], sc, neg_m));
 #pragma unroll
-        for (int t = 0; t < 8; ++t) lsum0 += pv[t];
+        for (int t = 0; t < 8; ++t) lsum += pv[t];
         const bf16x4 lo = __builtin_convertvector(f32x4{pv[0], pv[1], pv[2], pv[3]}, bf16x4);
         const bf16x4 hi = __builtin_convertvector(f32x4{pv[4], pv[5], pv[6], pv[7]}, bf16x4);
-        pf[s2] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
-#pragma unroll
-      for (int dt = 0; dt < kHeadDim / 32; ++dt) {
-        const uint16_t* base = vt + lv + dt * 32 * VP + kt * 32;
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const uint2 lo = *reinterpret_cast<const uint2*>(base + s2 * 16);
-          const uint2 hi = *reinterpret_cast<const uint2*>(base + s2 * 16 + 8);
-          const u32x4 wv = {lo.x, lo.y, hi.x, hi.y};
-          ws.o[dt] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wv), pf[s2], ws.o[dt], 0, 0, 0);
-        }
+        pf[t2][s2] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
     }
-    ws.l += lsum0;
+    ws.l += lsum;
+    __builtin_amdgcn_sched_barrier(0);
+    pv_jobs<16, kDepth>(ws.o, vf, pf, vh);
   }
 }
 
@@ -479,10 +292,104 @@ __device__ __forceinline__ void decode_work(const AttnParams& p, int& I, int& r,
   }
 }
 
-template <int BLK, bool FP8, bool PAGED>
+// Starts the DMA of item e into one K tile, one V tile and (pooled items) one
+// bias row. Wave w, instruction u writes the 1 KiB group 8u + w of the tile:
+// lane l fetches 16-byte chunk l/4 of tile row 32u + 4w + l%4.
+template <int BLK, bool PAGED>
+__device__ __forceinline__ void issue_item(const AttnParams& p, const RowCtx& rc, const int32_t* colcache,
+                                           const uint32_t* selbits, int e, uint8_t* kt, uint8_t* vt, float* bias,
+                                           int tid, int w, int lane, uint32_t voff_kv, uint32_t voff_pool) {
+  const int rstride = p.Hkv * kHeadDim * 2;  // bytes between consecutive tokens of K or V
+  if (e < rc.n_exact) {
+    const int J = !rc.cols ? e : uniform(e < kColCache ? lload_i32(colcache + e) : gload_i32(rc.cols + e));
+    const int lrem = rc.L - J * BLK;  // rows of block J inside the request (>= 1)
+    if constexpr (!PAGED) {
+      const int64_t row0 = ((rc.tok_base + (int64_t)J * BLK) * p.Hkv + rc.h) * (kHeadDim * 2);
+      const uint8_t* kb = static_cast<const uint8_t*>(p.kk) + row0;
+      const uint8_t* vb = static_cast<const uint8_t*>(p.vv) + row0;
+#pragma unroll
+      for (int u = 0; u < BLK / 32; ++u) {
+        const int nrec = uniform(min(max(lrem - 32 * u, 0), 32) * rstride);
+        const int64_t du = (int64_t)(32 * u) * rstride;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(kb + du, nrec), (lds_ptr)(kt + (8 * u + w) * kQuad), 16,
+                                                 voff_kv, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(vb + du, nrec), (lds_ptr)(vt + (8 * u + w) * kQuad), 16,
+                                                 voff_kv, 0, 0, 0);
+      }
+    } else {
+      // Rows past the request repeat its last token (masked by the causal
+      // mask of the diagonal item); each lane looks up its row's page.
+#pragma unroll
+      for (int u = 0; u < BLK / 32; ++u) {
+        const int rr = min(32 * u + 4 * w + (lane & 3), lrem - 1);
+        const int t = J * BLK + rr;
+        const int page = p.kv.page_table[(int64_t)rc.r * p.kv.max_pages + t / p.kv.page_size];
+        const int64_t off = (((int64_t)page * p.kv.page_size + t % p.kv.page_size) * p.Hkv + rc.h) * (kHeadDim * 2) +
+                            (lane >> 2) * 16;
+        __builtin_amdgcn_global_load_lds((gbl_ptr)(static_cast<const uint8_t*>(p.kk) + off),
+                                         (lds_ptr)(kt + (8 * u + w) * kQuad), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gbl_ptr)(static_cast<const uint8_t*>(p.vv) + off),
+                                         (lds_ptr)(vt + (8 * u + w) * kQuad), 16, 0, 0);
+      }
+    }
+  } else {
+    // Correction chunk: pooled columns c0 .. c0+63 (bf16 rows of 256 bytes);
+    // columns at or past I read zeros and get bias -inf.
+    const int c0 = (e - rc.n_exact) * kPC;
+    const int64_t row0 = (rc.pooled_row0 + c0) * (kHeadDim * 2);
+    const uint8_t* kb = reinterpret_cast<const uint8_t*>(p.kbar16) + row0;
+    const uint8_t* vb = reinterpret_cast<const uint8_t*>(p.vbar16) + row0;
+#pragma unroll
+    for (int u = 0; u < kPC / 32; ++u) {
+      const int nrec = uniform(min(max(rc.I - c0 - 32 * u, 0), 32) * (kHeadDim * 2));
+      const int du = 32 * u * (kHeadDim * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(kb + du, nrec), (lds_ptr)(kt + (8 * u + w) * kQuad), 16,
+                                               voff_pool, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(vb + du, nrec), (lds_ptr)(vt + (8 * u + w) * kQuad), 16,
+                                               voff_pool, 0, 0, 0);
+    }
+    if (tid < kPC) {
+      const int Jc = c0 + tid;
+      float bv = -INFINITY;
+      if (Jc < rc.I && !((selbits[Jc >> 5] >> (Jc & 31)) & 1u)) bv = __log2f((float)min(BLK, rc.L - Jc * BLK));
+      bias[tid] = bv;
+    }
+  }
+}
+
+// Waits for this wave's tile DMA, then for every wave of the workgroup.
+__device__ __forceinline__ void tiles_ready() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt unconstrained
+  __syncthreads();
+}
+
+// One item of the row from tile set (kt, vt, bias).
+template <int BLK>
+__device__ __forceinline__ void compute_item(WaveState<BLK>& ws, const RowCtx& rc, int e, const uint8_t* kt,
+                                             const uint8_t* vt, const float* bias, int tq0, int tq, float sl2,
+                                             int lk, int lv, int hf) {
+  if (e < rc.n_exact - 1)
+    attend_item<BLK, kExact>(ws, kt, vt, bias, 0, tq, sl2, lk, lv, hf);
+  else if (e == rc.n_exact - 1)
+    attend_item<BLK, kDiag>(ws, kt, vt, bias, tq0 >> 5, tq, sl2, lk, lv, hf);
+  else
+    attend_item<BLK, kPooled>(ws, kt, vt, bias, 0, tq, sl2, lk, lv, hf);
+}
+
+template <int BLK, bool PAGED>
 __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
-  __shared__ Lds<BLK> sm;
-  constexpr int NKT = BLK / 32;
+  // Two tile sets, each its own LDS object, so the compiler can tell the
+  // in-flight DMA into one set from the operand reads of the other.
+  __shared__ uint4 k_lds0[Tile<BLK>::kWords], k_lds1[Tile<BLK>::kWords];
+  __shared__ uint4 v_lds0[Tile<BLK>::kWords], v_lds1[Tile<BLK>::kWords];
+  __shared__ float bias0[kPC], bias1[kPC];
+  __shared__ uint32_t selbits[FP_MAX_BLOCKS_PER_SEQ / 32];
+  __shared__ int32_t colcache[kColCache];
+  uint8_t* const kt0 = reinterpret_cast<uint8_t*>(k_lds0);
+  uint8_t* const kt1 = reinterpret_cast<uint8_t*>(k_lds1);
+  uint8_t* const vt0 = reinterpret_cast<uint8_t*>(v_lds0);
+  uint8_t* const vt1 = reinterpret_cast<uint8_t*>(v_lds1);
+
   RowCtx rc;
   int sub;
   decode_work(p, rc.I, rc.r, rc.h, sub);
@@ -496,7 +403,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   rc.cols = p.dense ? nullptr : p.col_idx + p.row_ptr[row];
   const bool do_corr = p.mean_correction && !p.dense && I > 0;
   rc.n_items = rc.n_exact + (do_corr ? (I + kPC - 1) / kPC : 0);
-  rc.pooled_base = ((int64_t)rc.h * p.NB_tot + rt.blk_off[rc.r]) * kHeadDim;
+  rc.pooled_row0 = (int64_t)rc.h * p.NB_tot + rt.blk_off[rc.r];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -509,22 +416,24 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   const int tq = tq0 + c;
   const bool q_valid = wave_active && tq < nI;
   const int64_t tok = rc.tok_base + (int64_t)I * BLK + tq;
-  const int lk = c * kKPitch + hf * 8;              // K operand base of this lane
-  const int lv = c * Lds<BLK>::kVPitch + hf * 4;    // V^T operand base of this lane
+  // K operand: row c of a 32-row tile, chunk hf (then + 128 bytes per 16 dims).
+  const int lk = (c >> 2) * kQuad + (c & 3) * 16 + hf * 64;
+  // V^T operand: lane j of 16-lane group gq reads dims 16(gq&1) + 4(j&3)..+3 of
+  // key 4(gq>>1) + j/4 (tile_off layout).
+  const int j16 = lane & 15, gq = lane >> 4;
+  const int lv = (gq >> 1) * kQuad + (gq & 1) * 128 + ((j16 & 3) >> 1) * 64 + (j16 >> 2) * 16 + (j16 & 1) * 8;
+  // DMA offsets: chunk lane/4 of row 4w + lane%4 of a 32-row slab.
+  const uint32_t voff_kv = (uint32_t)((4 * w + (lane & 3)) * p.Hkv * kHeadDim * 2 + (lane >> 2) * 16);
+  const uint32_t voff_pool = (uint32_t)((4 * w + (lane & 3)) * kHeadDim * 2 + (lane >> 2) * 16);
 
-  // Logit scale in log2 units; FP8 folds both descales into it and stages
-  // pooled k_bar / v_bar divided by the K / V descales (so both streams stay
-  // in code units), and multiplies the output by the V descale.
+  // Logit scale in log2 units. FP8 folds the Q and K descales into it (K, V
+  // and the pooled rows are staged in code units) and multiplies the output
+  // by the V descale.
   float sl2 = p.sm_scale * kLog2e;
-  rc.kscale = 1.f;
-  rc.vscale = 1.f;
   float oscale = 1.f;
-  if constexpr (FP8) {
-    const float dq = *p.descale_q, dk = *p.descale_k, dv = *p.descale_v;
-    sl2 *= dq * dk;
-    rc.kscale = 1.f / dk;
-    rc.vscale = 1.f / dv;
-    oscale = dv;
+  if (p.fp8) {
+    sl2 *= *p.descale_q * *p.descale_k;
+    oscale = *p.descale_v;
   }
 
   WaveState<BLK> ws;
@@ -535,50 +444,49 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
 #pragma unroll
   for (int ks = 0; ks < kHeadDim / 16; ++ks) {
     uint4 qv = make_uint4(0, 0, 0, 0);
-    if (q_valid) qv = load8_as_bf16<FP8>(p.q, (tok * p.Hq + g) * kHeadDim + ks * 16 + hf * 8);
+    if (q_valid) {
+      const int64_t el = (tok * p.Hq + g) * kHeadDim + ks * 16 + hf * 8;
+      if (p.fp8) {
+        const uint2 w8 = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(p.q) + el);
+        qv.x = pack_bf16x2(e4m3_to_float(w8.x & 0xFF), e4m3_to_float((w8.x >> 8) & 0xFF));
+        qv.y = pack_bf16x2(e4m3_to_float((w8.x >> 16) & 0xFF), e4m3_to_float(w8.x >> 24));
+        qv.z = pack_bf16x2(e4m3_to_float(w8.y & 0xFF), e4m3_to_float((w8.y >> 8) & 0xFF));
+        qv.w = pack_bf16x2(e4m3_to_float((w8.y >> 16) & 0xFF), e4m3_to_float(w8.y >> 24));
+      } else {
+        qv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + el);
+      }
+    }
     ws.qf[ks] = __builtin_bit_cast(bf16x8, qv);
   }
 
   if (!p.dense) {
     if (do_corr)
-      for (int wd = tid; wd <= (I >> 5); wd += kThreads) sm.selbits[wd] = 0u;
-    for (int e = tid; e < min(rc.n_exact, kColCache); e += kThreads) sm.colcache[e] = rc.cols[e];
+      for (int wd = tid; wd <= (I >> 5); wd += kThreads) selbits[wd] = 0u;
+    for (int e = tid; e < min(rc.n_exact, kColCache); e += kThreads) colcache[e] = rc.cols[e];
     __syncthreads();
     if (do_corr) {
       for (int e = tid; e < rc.n_exact; e += kThreads) {
-        const int J = e < kColCache ? lload_i32(sm.colcache + e) : gload_i32(rc.cols + e);
-        atomicOr(&sm.selbits[J >> 5], 1u << (J & 31));
+        const int J = e < kColCache ? lload_i32(colcache + e) : gload_i32(rc.cols + e);
+        atomicOr(&selbits[J >> 5], 1u << (J & 31));
       }
     }
     __syncthreads();
   }
 
   const int N = rc.n_items;
-  Stage st;
-  load_item<BLK, FP8, PAGED>(st, p, rc, sm.colcache, 0, tid);
-  store_item<BLK, FP8>(st, sm, 0, rc, 0, tid);
-  __syncthreads();
-  for (int e = 0; e < N; ++e) {
-    const int buf = e & 1;
-    // The thread index is laundered per item so the per-slot address terms
-    // are recomputed (a few integer ops) instead of being held in registers
-    // across the whole loop.
-    int tid_l = tid;
-    asm volatile("" : "+v"(tid_l));
-    if (e + 1 < N) load_item<BLK, FP8, PAGED>(st, p, rc, sm.colcache, e + 1, tid_l);
-    if (wave_active) {
-      if (e < rc.n_exact - 1)
-        attend_item<BLK, kExact>(ws, sm.k[buf], sm.vt[buf], sm.bias[buf], NKT - 1, tq, sl2, lk, lv, hf);
-      else if (e == rc.n_exact - 1)
-        attend_item<BLK, kDiag>(ws, sm.k[buf], sm.vt[buf], sm.bias[buf], tq0 >> 5, tq, sl2, lk, lv, hf);
-      else
-        attend_item<BLK, kPooled>(ws, sm.k[buf], sm.vt[buf], sm.bias[buf],
-                                  (min(kPC, I - (e - rc.n_exact) * kPC) - 1) >> 5, tq, sl2, lk, lv, hf);
-    }
-    int tid_s = tid;
-    asm volatile("" : "+v"(tid_s));
-    if (e + 1 < N) store_item<BLK, FP8>(st, sm, buf ^ 1, rc, e + 1, tid_s);
-    __syncthreads();
+  issue_item<BLK, PAGED>(p, rc, colcache, selbits, 0, kt0, vt0, bias0, tid, w, lane, voff_kv, voff_pool);
+  tiles_ready();
+  for (int e = 0; e < N; e += 2) {
+    // Item e from set 0 while item e+1 streams into set 1, then the reverse.
+    if (e + 1 < N)
+      issue_item<BLK, PAGED>(p, rc, colcache, selbits, e + 1, kt1, vt1, bias1, tid, w, lane, voff_kv, voff_pool);
+    if (wave_active) compute_item<BLK>(ws, rc, e, kt0, vt0, bias0, tq0, tq, sl2, lk, lv, hf);
+    tiles_ready();
+    if (e + 1 >= N) break;
+    if (e + 2 < N)
+      issue_item<BLK, PAGED>(p, rc, colcache, selbits, e + 2, kt0, vt0, bias0, tid, w, lane, voff_kv, voff_pool);
+    if (wave_active) compute_item<BLK>(ws, rc, e + 1, kt1, vt1, bias1, tq0, tq, sl2, lk, lv, hf);
+    tiles_ready();
   }
 
   if (!wave_active) return;
@@ -600,10 +508,46 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   }
 }
 
-template <int BLK, bool FP8>
+// Conversion pass before the attention kernel (one launch, grid-stride):
+// bf16 copies of k_bar, v_bar in code units (divided by the K / V descales
+// for FP8), and for FP8 the K and V codes as bf16 (exact).
+__global__ __launch_bounds__(256) void prep_kernel(AttnParams p, int64_t n_pool8, int64_t n_kv8) {
+  const float ks = p.fp8 ? 1.f / *p.descale_k : 1.f;
+  const float vs = p.fp8 ? 1.f / *p.descale_v : 1.f;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < 2 * n_pool8 + 2 * n_kv8; i += stride) {
+    if (i < 2 * n_pool8) {
+      const bool isv = i >= n_pool8;
+      const int64_t k8 = isv ? i - n_pool8 : i;
+      const float* src = (isv ? p.v_bar : p.k_bar) + k8 * 8;
+      const float s = isv ? vs : ks;
+      const float4 a = *reinterpret_cast<const float4*>(src);
+      const float4 b = *reinterpret_cast<const float4*>(src + 4);
+      uint4 o;
+      o.x = pack_bf16x2(a.x * s, a.y * s);
+      o.y = pack_bf16x2(a.z * s, a.w * s);
+      o.z = pack_bf16x2(b.x * s, b.y * s);
+      o.w = pack_bf16x2(b.z * s, b.w * s);
+      reinterpret_cast<uint4*>(isv ? p.vbar16 : p.kbar16)[k8] = o;
+    } else {
+      const int64_t j = i - 2 * n_pool8;
+      const bool isv = j >= n_kv8;
+      const int64_t k8 = isv ? j - n_kv8 : j;
+      const uint2 c = reinterpret_cast<const uint2*>(isv ? p.v : p.k)[k8];
+      uint4 o;
+      o.x = pack_bf16x2(e4m3_to_float(c.x & 0xFF), e4m3_to_float((c.x >> 8) & 0xFF));
+      o.y = pack_bf16x2(e4m3_to_float((c.x >> 16) & 0xFF), e4m3_to_float(c.x >> 24));
+      o.z = pack_bf16x2(e4m3_to_float(c.y & 0xFF), e4m3_to_float((c.y >> 8) & 0xFF));
+      o.w = pack_bf16x2(e4m3_to_float((c.y >> 16) & 0xFF), e4m3_to_float(c.y >> 24));
+      reinterpret_cast<uint4*>(const_cast<void*>(isv ? p.vv : p.kk))[k8] = o;
+    }
+  }
+}
+
+template <int BLK>
 void launch_attn_t(const AttnParams& p, dim3 grid, hipStream_t stream) {
-  if (p.kv.paged) hipLaunchKernelGGL((attn_kernel<BLK, FP8, true>), grid, dim3(kThreads), 0, stream, p);
-  else hipLaunchKernelGGL((attn_kernel<BLK, FP8, false>), grid, dim3(kThreads), 0, stream, p);
+  if (p.kv.paged) hipLaunchKernelGGL((attn_kernel<BLK, true>), grid, dim3(kThreads), 0, stream, p);
+  else hipLaunchKernelGGL((attn_kernel<BLK, false>), grid, dim3(kThreads), 0, stream, p);
 }
 
 }  // namespace
@@ -611,15 +555,17 @@ void launch_attn_t(const AttnParams& p, dim3 grid, hipStream_t stream) {
 int attn_rows_per_wg() { return kRowsPerWG; }
 
 hipError_t launch_attn(const AttnParams& p, hipStream_t stream) {
+  const int64_t n_pool8 = p.kbar16 ? (int64_t)p.Hkv * p.NB_tot * kHeadDim / 8 : 0;
+  const int64_t n_kv8 = p.fp8 ? p.kv_elems / 8 : 0;
+  if (n_pool8 + n_kv8 > 0) {
+    const int64_t work = 2 * n_pool8 + 2 * n_kv8;
+    const int blocks = (int)(work < 8192 * 256 ? (work + 255) / 256 : 8192);
+    hipLaunchKernelGGL(prep_kernel, dim3(blocks), dim3(256), 0, stream, p, n_pool8, n_kv8);
+  }
   const int64_t wgs = (int64_t)p.Hkv * p.NB_tot * p.subs;
   dim3 grid((unsigned)wgs);
-  if (p.B == 128) {
-    if (p.fp8) launch_attn_t<128, true>(p, grid, stream);
-    else launch_attn_t<128, false>(p, grid, stream);
-  } else {
-    if (p.fp8) launch_attn_t<64, true>(p, grid, stream);
-    else launch_attn_t<64, false>(p, grid, stream);
-  }
+  if (p.B == 128) launch_attn_t<128>(p, grid, stream);
+  else launch_attn_t<64>(p, grid, stream);
   return hipGetLastError();
 }
 

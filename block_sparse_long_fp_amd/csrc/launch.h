@@ -43,10 +43,15 @@ struct SelectParams {
 
 struct AttnParams {
   const void* q;
-  const void* k;
+  const void* k;        // caller's K / V (bf16 or FP8 codes)
   const void* v;
+  const void* kk;       // K / V as bf16 the attention kernel reads: k / v for
+  const void* vv;       // bf16 inputs, the workspace copies for FP8
   const float* k_bar;
   const float* v_bar;
+  uint16_t* kbar16;     // workspace: bf16 k_bar / v_bar in code units (or NULL)
+  uint16_t* vbar16;
+  int64_t kv_elems;     // elements of each of K and V (tokens or page slots x Hkv x d)
   const int32_t* row_ptr;
   const int32_t* col_idx;
   uint16_t* out;        // bf16 bits
@@ -68,5 +73,6 @@ size_t pool_lds_bytes(int G);
 hipError_t launch_pool(const PoolParams& p, hipStream_t stream);
 hipError_t launch_select(const SelectParams& p, hipStream_t stream);
 hipError_t launch_attn(const AttnParams& p, hipStream_t stream);
+int attn_rows_per_wg();
 
 }  // namespace fpv2

@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define FPV2_ABI_VERSION 1
+#define FPV2_ABI_VERSION 2
 
 /* Status codes. */
 typedef int32_t fp_status;
@@ -78,7 +78,7 @@ enum {
   FP_ERR_DTYPE = 5,       /* unknown dtype, or FP8 without its three descales    */
   FP_ERR_LAYOUT = 6,      /* unknown kv_layout or inconsistent page arguments    */
   FP_ERR_CAPACITY = 7,    /* col_idx capacity below the worst-case nnz           */
-  FP_ERR_WORKSPACE = 8,   /* workspace NULL or smaller than fp_select_workspace_bytes */
+  FP_ERR_WORKSPACE = 8,   /* workspace NULL or below fp_*_workspace_bytes      */
   FP_ERR_ARG = 9,         /* bad scalar argument (NaN alpha, sel_scale, sm_scale) */
   FP_ERR_UNSUPPORTED = 10,/* valid request outside this build (head_dim != 128,  */
                           /* more than FP_MAX_SEQS requests, too many blocks)    */
@@ -144,6 +144,12 @@ fp_status fp_index_shape(const fp_problem* p, int64_t* num_rows, int64_t* max_nn
 /* Bytes of DEVICE workspace fp_select_blocks needs for this problem. */
 fp_status fp_select_workspace_bytes(const fp_problem* p, size_t* bytes);
 
+/* Bytes of DEVICE workspace fp_sparse_prefill (sparse = 1) or fp_dense_prefill
+ * (sparse = 0) needs: bf16 copies of k_bar and v_bar for the correction
+ * (sparse only), and for FP8 bf16 copies of the K and V codes (exact). 0 for
+ * a dense bf16 problem. */
+fp_status fp_attn_workspace_bytes(const fp_problem* p, int32_t sparse, size_t* bytes);
+
 /* Validate a problem and (optionally, may be NULL) selection/attention args
  * exactly as the compute calls do, without touching any device pointer. */
 fp_status fp_validate(const fp_problem* p, const fp_select_args* sel, const fp_attn_args* attn);
@@ -177,16 +183,21 @@ fp_status fp_select_blocks(const fp_problem* p, const fp_select_args* sel, const
  * k_bar, v_bar: DEVICE fp32 from fp_pool_blocks (read only when
  * mean_correction = 1). row_ptr, col_idx: DEVICE CSR from fp_select_blocks
  * (or any CSR of the same shape with the diagonal in every row).
- * out: DEVICE bf16 [T, Hq, d]. lse: DEVICE fp32 [Hq, T], or NULL to skip. */
+ * out: DEVICE bf16 [T, Hq, d]. lse: DEVICE fp32 [Hq, T], or NULL to skip.
+ * workspace: DEVICE scratch of at least fp_attn_workspace_bytes(p, 1) bytes
+ * (may be NULL when that is 0); contents on entry do not matter, garbage on
+ * exit; the call must not overlap another call using the same workspace. */
 fp_status fp_sparse_prefill(const fp_problem* p, const fp_attn_args* attn, const void* q,
                             const void* k, const void* v, const float* k_bar, const float* v_bar,
                             const int32_t* row_ptr, const int32_t* col_idx, void* out, float* lse,
-                            void* stream);
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Dense causal attention over every key j <= i of the request (the comparator
- * for the sparse path; mean_correction is ignored). Same layouts as above. */
+ * for the sparse path; mean_correction is ignored). Same layouts as above;
+ * workspace as above with fp_attn_workspace_bytes(p, 0). */
 fp_status fp_dense_prefill(const fp_problem* p, const fp_attn_args* attn, const void* q,
-                           const void* k, const void* v, void* out, float* lse, void* stream);
+                           const void* k, const void* v, void* out, float* lse, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /* Static text for a status code; never NULL. */
 const char* fp_status_string(fp_status s);

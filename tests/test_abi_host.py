@@ -8,6 +8,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import block_sparse_long_fp_amd as fp
 
@@ -29,13 +30,27 @@ def test_exports_every_declared_symbol():
     L = ctypes.CDLL(fp.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
-    assert fp.lib().fp_abi_version() == 1
+    ver = int(re.search(r"#define FPV2_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert fp.lib().fp_abi_version() == ver
 
 
 def _prob(**kw):
     base = dict(cu_seqlens=[0, 1000, 3000], num_q_heads=32, num_kv_heads=8, block_size=128)
     base.update(kw)
     return fp.Problem(**base)
+
+
+def test_attention_workspace_sizes():
+    def a256(x):
+        return (x + 255) // 256 * 256
+    p = _prob()
+    nb, T, Hkv, d = 24, 3000, 8, 128
+    assert fp.attn_workspace_bytes(p, True) == 2 * a256(Hkv * nb * d * 2)
+    assert fp.attn_workspace_bytes(p, False) == 0
+    ds = [torch.ones(1) for _ in range(3)]
+    p8 = _prob(dtype=fp.FP_FP8_E4M3, descales=ds)
+    assert fp.attn_workspace_bytes(p8, True) == 2 * a256(Hkv * nb * d * 2) + 2 * a256(T * Hkv * d * 2)
+    assert fp.attn_workspace_bytes(p8, False) == 2 * a256(T * Hkv * d * 2)
 
 
 def test_index_shape_and_workspace():
@@ -130,10 +145,16 @@ def test_compute_calls_reject_before_launch():
     assert L.fp_select_blocks(p.ref, ctypes.byref(sel), fake, fake, fake, fake, nnz - 1, fake, ws, None) == 7
     assert L.fp_select_blocks(p.ref, ctypes.byref(sel), fake, fake, fake, fake, nnz, fake, ws - 1, None) == 8
     assert L.fp_select_blocks(p.ref, ctypes.byref(sel), fake, fake, fake, fake, nnz, None, ws, None) == 8
+    aws = fp.attn_workspace_bytes(p, True)
+    assert aws > 0 and fp.attn_workspace_bytes(p, False) == 0  # bf16: only the pooled copies
     assert L.fp_sparse_prefill(p.ref, ctypes.byref(attn), fake, fake, fake, None, fake, fake, fake, fake, None,
-                               None) == 1
+                               fake, aws, None) == 1
     assert L.fp_sparse_prefill(p.ref, ctypes.byref(attn), fake, fake, fake, fake, fake, None, fake, fake, None,
-                               None) == 1
-    assert L.fp_dense_prefill(p.ref, ctypes.byref(attn), fake, fake, fake, None, None, None) == 1
+                               fake, aws, None) == 1
+    assert L.fp_sparse_prefill(p.ref, ctypes.byref(attn), fake, fake, fake, fake, fake, fake, fake, fake, None,
+                               fake, aws - 1, None) == 8
+    assert L.fp_sparse_prefill(p.ref, ctypes.byref(attn), fake, fake, fake, fake, fake, fake, fake, fake, None,
+                               None, aws, None) == 8
+    assert L.fp_dense_prefill(p.ref, ctypes.byref(attn), fake, fake, fake, None, None, None, 0, None) == 1
     for code in range(12):
         assert L.fp_status_string(code)
