@@ -118,10 +118,9 @@ struct WaveState {
 };
 
 // Item kinds: a selected key block off the diagonal (all keys visible), the
-// diagonal block (causal mask inside tile kt_lim), or a chunk of pooled
+// diagonal block (causal mask from tile kt_lim on), or a chunk of pooled
 // columns (logit s*sl2 + bias[col]; columns past the chunk end have bias
-// -inf). Each kind is its own instantiation so the common case carries no
-// per-score masking or bias work.
+// -inf).
 enum ItemKind { kExact = 0, kDiag = 1, kPooled = 2 };
 
 // V^T operand for PV job j of a half (tile 2hh + (j >> 3), MFMA s2 = (j >> 2) & 1,
@@ -153,20 +152,25 @@ __device__ __forceinline__ void pv_jobs(f32x16 (&o)[kHeadDim / 32], bf16x8 (&vf)
 // live instead of 64. Every half computes both of its tiles: on the diagonal
 // the causal mask also covers a tile past the query block's last visible key,
 // and a pooled chunk is one half whose unused columns have bias -inf (their
-// staged rows are zeros), so the code has no data-dependent tile skips.
+// staged rows are zeros), so the code has no data-dependent tile skips, and
+// the three item kinds share one copy of the MFMA code (their differences are
+// short wave-uniform branches on the scores).
 // kt_lim (diagonal only): the tile that holds the query's own position.
 // Operand reads run a few MFMAs ahead of their use; the schedule is pinned
 // with scheduling fences because the compiler otherwise places every LDS read
 // right before its MFMA and exposes the LDS latency each time.
-template <int BLK, int KIND>
+template <int BLK>
 __device__ __forceinline__ void attend_item(WaveState<BLK>& ws, const uint8_t* kb, const uint8_t* vt,
-                                            const float* bias, int kt_lim, int tq, float sl2, int lk, int lv,
-                                            int hf) {
-  constexpr int NH = KIND == kPooled ? 1 : BLK / 64;  // halves
-  constexpr int kDepth = 4;                            // operand reads in flight
+                                            const float* bias, int kind, int kt_lim, int tq, float sl2, int lk,
+                                            int lv, int hf) {
+  constexpr int kDepth = 4;  // operand reads in flight
+  const int nh = kind == kPooled ? 1 : BLK / 64;
+  // Pooled scores are turned into log2-unit logits with their bias before
+  // the max; exact scores are scaled after it.
+  const float sc = kind == kPooled ? 1.0f : sl2;
 #pragma unroll
-  for (int hh = 0; hh < NH; ++hh) {
-    if (KIND == kDiag && 2 * hh > kt_lim) break;
+  for (int hh = 0; hh < BLK / 64; ++hh) {
+    if (hh >= nh || (kind == kDiag && 2 * hh > kt_lim)) break;
     // QK^T of tiles 2hh, 2hh+1: jobs alternate between the two accumulation
     // chains; rows 32kt + c of a tile, the 16 dims of step ks 128 ks bytes
     // after the lane's first chunk (four-row groups, see the file header).
@@ -192,41 +196,34 @@ __device__ __forceinline__ void attend_item(WaveState<BLK>& ws, const uint8_t* k
 #pragma unroll
     for (int j = 0; j < kDepth; ++j) vf[j] = v_operand(vh, j);
     __builtin_amdgcn_sched_barrier(0);
-    float mx = kNegBig;
-    if constexpr (KIND == kPooled) {
+    if (kind == kPooled) {
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float4 bb = *reinterpret_cast<const float4*>(&bias[t2 * 32 + i * 8 + hf * 4]);
-          const float bv[4] = {bb.x, bb.y, bb.z, bb.w};
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            s[t2][4 * i + jj] = fmaf(s[t2][4 * i + jj], sl2, bv[jj]);
-            mx = fmaxf(mx, s[t2][4 * i + jj]);
-          }
+          s[t2][4 * i + 0] = fmaf(s[t2][4 * i + 0], sl2, bb.x);
+          s[t2][4 * i + 1] = fmaf(s[t2][4 * i + 1], sl2, bb.y);
+          s[t2][4 * i + 2] = fmaf(s[t2][4 * i + 2], sl2, bb.z);
+          s[t2][4 * i + 3] = fmaf(s[t2][4 * i + 3], sl2, bb.w);
         }
       }
-    } else {
-      if constexpr (KIND == kDiag) {
-        // Keys past the query; only the half holding tile kt_lim has any.
-        if (2 * hh + 1 >= kt_lim) {
-#pragma unroll
-          for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-              for (int jj = 0; jj < 4; ++jj)
-                if ((2 * hh + t2) * 32 + i * 8 + hf * 4 + jj > tq) s[t2][4 * i + jj] = -INFINITY;
-        }
-      }
+    } else if (kind == kDiag && 2 * hh + 1 >= kt_lim) {
+      // Keys past the query; only the half holding tile kt_lim has any.
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[t2][e]);
-      mx *= sl2;
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            if ((2 * hh + t2) * 32 + i * 8 + hf * 4 + jj > tq) s[t2][4 * i + jj] = -INFINITY;
     }
-    mx = max_halves(mx);
+    float mx = kNegBig;
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[t2][e]);
+    mx = max_halves(mx * sc);
     // Lazy running max (see the file header).
     const float m_new = mx > ws.m + kSlack ? mx : ws.m;
     if (__ballot(m_new != ws.m) != 0) {
@@ -236,7 +233,6 @@ __device__ __forceinline__ void attend_item(WaveState<BLK>& ws, const uint8_t* k
       for (int dt = 0; dt < kHeadDim / 32; ++dt) ws.o[dt] *= corr;
     }
     ws.m = m_new;
-    const float sc = KIND == kPooled ? 1.0f : sl2;
     const float neg_m = -m_new;
     float lsum = 0.f;
     bf16x8 pf[2][2];
@@ -368,12 +364,8 @@ template <int BLK>
 __device__ __forceinline__ void compute_item(WaveState<BLK>& ws, const RowCtx& rc, int e, const uint8_t* kt,
                                              const uint8_t* vt, const float* bias, int tq0, int tq, float sl2,
                                              int lk, int lv, int hf) {
-  if (e < rc.n_exact - 1)
-    attend_item<BLK, kExact>(ws, kt, vt, bias, 0, tq, sl2, lk, lv, hf);
-  else if (e == rc.n_exact - 1)
-    attend_item<BLK, kDiag>(ws, kt, vt, bias, tq0 >> 5, tq, sl2, lk, lv, hf);
-  else
-    attend_item<BLK, kPooled>(ws, kt, vt, bias, 0, tq, sl2, lk, lv, hf);
+  const int kind = e < rc.n_exact - 1 ? kExact : (e == rc.n_exact - 1 ? kDiag : kPooled);
+  attend_item<BLK>(ws, kt, vt, bias, kind, tq0 >> 5, tq, sl2, lk, lv, hf);
 }
 
 template <int BLK, bool PAGED>
