@@ -181,6 +181,7 @@ __device__ __forceinline__ void attend_item(WaveState<BLK>& ws, const uint8_t* k
     for (int j = 0; j < kDepth; ++j)
       kf[j] = *reinterpret_cast<const bf16x8*>(kh + (j & 1) * 8 * kQuad + (j >> 1) * 128);
     __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
     f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
@@ -190,6 +191,7 @@ __device__ __forceinline__ void attend_item(WaveState<BLK>& ws, const uint8_t* k
             *reinterpret_cast<const bf16x8*>(kh + ((j + kDepth) & 1) * 8 * kQuad + ((j + kDepth) >> 1) * 128);
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
     // The first V operands load while the softmax runs.
     const uint8_t* vh = vt + lv + (2 * hh) * 8 * kQuad;
     bf16x8 vf[kDepth];
@@ -252,7 +254,9 @@ __device__ __forceinline__ void attend_item(WaveState<BLK>& ws, const uint8_t* k
     }
     ws.l += lsum;
     __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
     pv_jobs<16, kDepth>(ws.o, vf, pf, vh);
+    __builtin_amdgcn_s_setprio(0);
   }
 }
 
