@@ -159,11 +159,12 @@ __device__ __forceinline__ void pv_jobs(f32x16 (&o)[kHeadDim / 32], bf16x8 (&vf)
 // Operand reads run a few MFMAs ahead of their use; the schedule is pinned
 // with scheduling fences because the compiler otherwise places every LDS read
 // right before its MFMA and exposes the LDS latency each time.
-template <int BLK>
+template <int BLK, bool EXACT>
 __device__ __forceinline__ void attend_item(WaveState<BLK>& ws, const uint8_t* kb, const uint8_t* vt,
                                             const float* bias, int kind, int kt_lim, int tq, float sl2, int lk,
                                             int lv, int hf) {
   constexpr int kDepth = 4;  // operand reads in flight
+  if (EXACT) kind = kExact;
   const int nh = kind == kPooled ? 1 : BLK / 64;
   // Pooled scores are turned into log2-unit logits with their bias before
   // the max; exact scores are scaled after it.
@@ -364,13 +365,54 @@ __device__ __forceinline__ void tiles_ready() {
 }
 
 // One item of the row from tile set (kt, vt, bias).
-template <int BLK>
+template <int BLK, bool EXACT>
 __device__ __forceinline__ void compute_item(WaveState<BLK>& ws, const RowCtx& rc, int e, const uint8_t* kt,
                                              const uint8_t* vt, const float* bias, int tq0, int tq, float sl2,
                                              int lk, int lv, int hf) {
-  const int kind = e < rc.n_exact - 1 ? kExact : (e == rc.n_exact - 1 ? kDiag : kPooled);
-  attend_item<BLK>(ws, kt, vt, bias, kind, tq0 >> 5, tq, sl2, lk, lv, hf);
+  const int kind = EXACT ? kExact : (e == rc.n_exact - 1 ? kDiag : kPooled);
+  attend_item<BLK, EXACT>(ws, kt, vt, bias, kind, tq0 >> 5, tq, sl2, lk, lv, hf);
 }
+
+// The item loop of one workgroup. step<EXACT, SET>: stream item e+1 into the
+// other tile set while item e is computed from set SET, then wait for the
+// stream and for every wave.
+template <int BLK, bool PAGED>
+struct ItemLoop {
+  const AttnParams& p;
+  const RowCtx& rc;
+  const int32_t* colcache;
+  const uint32_t* selbits;
+  uint8_t *kt0, *kt1, *vt0, *vt1;
+  float *bias0, *bias1;
+  int N, tid, w, lane;
+  uint32_t voff_kv, voff_pool;
+  bool wave_active;
+  int tq0, tq;
+  float sl2;
+  int lk, lv, hf;
+
+  template <bool EXACT, int SET>
+  __device__ __forceinline__ void step(WaveState<BLK>& ws, int e) {
+    if (e + 1 < N)
+      issue_item<BLK, PAGED>(p, rc, colcache, selbits, e + 1, SET ? kt0 : kt1, SET ? vt0 : vt1, SET ? bias0 : bias1,
+                             tid, w, lane, voff_kv, voff_pool);
+    if (wave_active)
+      compute_item<BLK, EXACT>(ws, rc, e, SET ? kt1 : kt0, SET ? vt1 : vt0, SET ? bias1 : bias0, tq0, tq, sl2, lk,
+                               lv, hf);
+    tiles_ready();
+  }
+
+  template <bool EXACT>
+  __device__ __forceinline__ void run(WaveState<BLK>& ws, int e0, int e1) {
+    int e = e0;
+    if (e < e1 && (e & 1)) step<EXACT, 1>(ws, e++);
+    for (; e + 1 < e1; e += 2) {
+      step<EXACT, 0>(ws, e);
+      step<EXACT, 1>(ws, e + 1);
+    }
+    if (e < e1) step<EXACT, 0>(ws, e);
+  }
+};
 
 template <int BLK, bool PAGED>
 __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
@@ -470,20 +512,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   }
 
   const int N = rc.n_items;
+  // The row's off-diagonal kept blocks run first through an instantiation of
+  // the item code without any score adjustment; the diagonal block and the
+  // correction chunks follow through the general one. Item e always lives in
+  // tile set e & 1.
   issue_item<BLK, PAGED>(p, rc, colcache, selbits, 0, kt0, vt0, bias0, tid, w, lane, voff_kv, voff_pool);
   tiles_ready();
-  for (int e = 0; e < N; e += 2) {
-    // Item e from set 0 while item e+1 streams into set 1, then the reverse.
-    if (e + 1 < N)
-      issue_item<BLK, PAGED>(p, rc, colcache, selbits, e + 1, kt1, vt1, bias1, tid, w, lane, voff_kv, voff_pool);
-    if (wave_active) compute_item<BLK>(ws, rc, e, kt0, vt0, bias0, tq0, tq, sl2, lk, lv, hf);
-    tiles_ready();
-    if (e + 1 >= N) break;
-    if (e + 2 < N)
-      issue_item<BLK, PAGED>(p, rc, colcache, selbits, e + 2, kt0, vt0, bias0, tid, w, lane, voff_kv, voff_pool);
-    if (wave_active) compute_item<BLK>(ws, rc, e + 1, kt1, vt1, bias1, tq0, tq, sl2, lk, lv, hf);
-    tiles_ready();
-  }
+  ItemLoop<BLK, PAGED> L{p, rc, colcache, selbits, kt0, kt1, vt0, vt1, bias0, bias1, N, tid, w, lane,
+                         voff_kv, voff_pool, wave_active, tq0, tq, sl2, lk, lv, hf};
+  L.template run<true>(ws, 0, rc.n_exact - 1);
+  L.template run<false>(ws, rc.n_exact - 1, N);
 
   if (!wave_active) return;
   const float l_tot = sum_halves(ws.l);
