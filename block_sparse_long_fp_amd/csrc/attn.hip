@@ -373,6 +373,122 @@ __device__ __forceinline__ void compute_item(WaveState<BLK>& ws, const RowCtx& r
   attend_item<BLK, EXACT>(ws, kt, vt, bias, kind, tq0 >> 5, tq, sl2, lk, lv, hf);
 }
 
+// K operand of QK job j of a half (tile 2hh + (j & 1), dims 16 (j >> 1) ..).
+__device__ __forceinline__ bf16x8 k_operand(const uint8_t* kh, int j) {
+  return *reinterpret_cast<const bf16x8*>(kh + (j & 1) * 8 * kQuad + (j >> 1) * 128);
+}
+
+// QK^T of one half: two accumulation chains, K operands read kDepth ahead.
+template <int DEPTH>
+__device__ __forceinline__ void qk_half(const bf16x8 (&qf)[kHeadDim / 16], const uint8_t* kh, f32x16 (&s)[2]) {
+  constexpr int NJ = 2 * (kHeadDim / 16);
+  bf16x8 kf[DEPTH];
+#pragma unroll
+  for (int j = 0; j < DEPTH; ++j) kf[j] = k_operand(kh, j);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(1);
+  s[0] = f32x16{};
+  s[1] = f32x16{};
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    s[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j % DEPTH], qf[j >> 1], s[j & 1], 0, 0, 0);
+    if (j + DEPTH < NJ) kf[j % DEPTH] = k_operand(kh, j + DEPTH);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __builtin_amdgcn_s_setprio(0);
+}
+
+// PV of one half interleaved with QK^T of the next: the two MFMA streams
+// alternate, so every accumulation chain sees at least three independent
+// MFMAs between its own steps.
+template <int DEPTH>
+__device__ __forceinline__ void pv_qk_half(f32x16 (&o)[kHeadDim / 32], bf16x8 (&vf)[DEPTH], const bf16x8 (&pf)[2][2],
+                                           const uint8_t* vh, const bf16x8 (&qf)[kHeadDim / 16], const uint8_t* kn,
+                                           f32x16 (&sn)[2]) {
+  constexpr int NJ = 16;
+  bf16x8 kf[DEPTH];
+#pragma unroll
+  for (int j = 0; j < DEPTH; ++j) kf[j] = k_operand(kn, j);
+  sn[0] = f32x16{};
+  sn[1] = f32x16{};
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    o[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j % DEPTH], pf[j >> 3][(j >> 2) & 1], o[j & 3], 0, 0, 0);
+    if (j + DEPTH < NJ) vf[j % DEPTH] = v_operand(vh, j + DEPTH);
+    sn[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j % DEPTH], qf[j >> 1], sn[j & 1], 0, 0, 0);
+    if (j + DEPTH < NJ) kf[j % DEPTH] = k_operand(kn, j + DEPTH);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __builtin_amdgcn_s_setprio(0);
+}
+
+// Online-softmax update of one half of exact scores (in score units): new
+// running max (lazy), output rescale if it moved, probabilities as bf16 P
+// operands and their fp32 sum.
+template <int BLK>
+__device__ __forceinline__ void softmax_exact(WaveState<BLK>& ws, const f32x16 (&s)[2], float sl2, bf16x8 (&pf)[2][2]) {
+  float mx = kNegBig;
+#pragma unroll
+  for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[t2][e]);
+  mx = max_halves(mx * sl2);
+  const float m_new = mx > ws.m + kSlack ? mx : ws.m;
+  if (__ballot(m_new != ws.m) != 0) {
+    const float corr = __builtin_amdgcn_exp2f(ws.m - m_new);
+    ws.l *= corr;
+#pragma unroll
+    for (int dt = 0; dt < kHeadDim / 32; ++dt) ws.o[dt] *= corr;
+  }
+  ws.m = m_new;
+  const float neg_m = -m_new;
+  float lsum = 0.f;
+#pragma unroll
+  for (int t2 = 0; t2 < 2; ++t2) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      float pv[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) pv[t] = __builtin_amdgcn_exp2f(fmaf(s[t2][8 * s2 + t], sl2, neg_m));
+#pragma unroll
+      for (int t = 0; t < 8; ++t) lsum += pv[t];
+      const bf16x4 lo = __builtin_convertvector(f32x4{pv[0], pv[1], pv[2], pv[3]}, bf16x4);
+      const bf16x4 hi = __builtin_convertvector(f32x4{pv[4], pv[5], pv[6], pv[7]}, bf16x4);
+      pf[t2][s2] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  }
+  ws.l += lsum;
+}
+
+// An off-diagonal kept block: all keys visible, no score adjustment. Its
+// halves are software-pipelined: QK^T(0); softmax(0); PV(0) with QK^T(1);
+// softmax(1); PV(1).
+template <int BLK>
+__device__ __forceinline__ void attend_exact(WaveState<BLK>& ws, const uint8_t* kb, const uint8_t* vt, float sl2,
+                                             int lk, int lv) {
+  constexpr int NH = BLK / 64;
+  constexpr int kDepth = 4;
+  f32x16 sb[2][2];
+  qk_half<kDepth>(ws.qf, kb + lk, sb[0]);
+#pragma unroll
+  for (int hh = 0; hh < NH; ++hh) {
+    const uint8_t* vh = vt + lv + (2 * hh) * 8 * kQuad;
+    bf16x8 vf[kDepth];
+#pragma unroll
+    for (int j = 0; j < kDepth; ++j) vf[j] = v_operand(vh, j);
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 pf[2][2];
+    softmax_exact(ws, sb[hh & 1], sl2, pf);
+    __builtin_amdgcn_sched_barrier(0);
+    if (hh + 1 < NH)
+      pv_qk_half<kDepth>(ws.o, vf, pf, vh, ws.qf, kb + lk + (2 * hh + 2) * 8 * kQuad, sb[(hh + 1) & 1]);
+    else
+      pv_jobs<16, kDepth>(ws.o, vf, pf, vh);
+  }
+}
+
 // The item loop of one workgroup. step<EXACT, SET>: stream item e+1 into the
 // other tile set while item e is computed from set SET, then wait for the
 // stream and for every wave.
@@ -396,9 +512,13 @@ struct ItemLoop {
     if (e + 1 < N)
       issue_item<BLK, PAGED>(p, rc, colcache, selbits, e + 1, SET ? kt0 : kt1, SET ? vt0 : vt1, SET ? bias0 : bias1,
                              tid, w, lane, voff_kv, voff_pool);
-    if (wave_active)
-      compute_item<BLK, EXACT>(ws, rc, e, SET ? kt1 : kt0, SET ? vt1 : vt0, SET ? bias1 : bias0, tq0, tq, sl2, lk,
-                               lv, hf);
+    if (wave_active) {
+      if (EXACT)
+        attend_exact<BLK>(ws, SET ? kt1 : kt0, SET ? vt1 : vt0, sl2, lk, lv);
+      else
+        compute_item<BLK, false>(ws, rc, e, SET ? kt1 : kt0, SET ? vt1 : vt0, SET ? bias1 : bias0, tq0, tq, sl2,
+                                 lk, lv, hf);
+    }
     tiles_ready();
   }
 
