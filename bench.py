@@ -31,7 +31,7 @@ HBM_PEAK_GBS = 8000.0
 # together with a hash of the kernel's sources; the benchmark reports them as
 # roofline.traffic only while the sources still hash the same.
 TRAFFIC_RECORD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "attn_kernel_llama128k_bf16.md")
-ATTN_SOURCES = ["attn.hip", "common.h", "launch.h"]
+ATTN_SOURCES = ["attn.hip", "common.h"]
 
 
 def attn_source_hash():
@@ -72,7 +72,13 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama_128k")
+    ap.add_argument("--seq-len", type=int, default=None,
+                    help="override the sequence length of a single-request workload (same recipe and seed)")
     ap.add_argument("--alpha", type=float, default=None)
+    ap.add_argument("--sink", type=int, default=0, help="forced keep: first key blocks of each request")
+    ap.add_argument("--window", type=int, default=0, help="forced keep: key blocks left of the diagonal")
+    ap.add_argument("--last-n", type=int, default=0, help="forced keep: dense last query blocks")
+    ap.add_argument("--no-mean-correction", action="store_true", help="drop pruned blocks (the ablation)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=16, help="attention rows the CPU baseline computes")
@@ -95,7 +101,7 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes": n, "dispatches": 3}), flush=True)
 
 
-def csr_work(row_ptr, col_idx, wl, blk_off):
+def csr_work(row_ptr, col_idx, wl, blk_off, mean_correction=True):
     """Algorithmic work of one attention launch from the CSR.
 
     Per selected (h, I, J): 4 * d * (G * n_I) * n_J FLOPs (QK^T and PV over the
@@ -121,7 +127,7 @@ def csr_work(row_ptr, col_idx, wl, blk_off):
             exact = (c - 1) * nI * B + nI * nI
             flops += 4 * d * G * float(exact.sum())
             strict += 4 * d * G * float(((c - 1) * nI * B + nI * (nI + 1) / 2).sum())
-            if not dense_req:
+            if mean_correction and not dense_req:
                 pruned = np.arange(nb) - (c - 1)
                 flops += 4 * d * G * float((pruned * nI).sum())
                 strict += 4 * d * G * float((pruned * nI).sum())
@@ -138,7 +144,7 @@ def stage1_bytes(wl):
     return T * (wl.num_q_heads + 2 * wl.num_kv_heads) * d * e + 3 * wl.num_kv_heads * nbt * d * 4
 
 
-def cpu_baseline(wl, row_ptr, n_rows, seed=0):
+def cpu_baseline(wl, row_ptr, n_rows, seed=0, mean_correction=True, forced=None):
     """Time the fp64 oracle on the host (pool + select for the whole layer,
     attention for a few sampled rows, extrapolated by computed key count)."""
     import torch
@@ -156,8 +162,9 @@ def cpu_baseline(wl, row_ptr, n_rows, seed=0):
     Q, K, V = deq(wl.q, wl.descale_q), deq(wl.k, wl.descale_k), deq(wl.v, wl.descale_v)
     t_conv = time.perf_counter() - t0
     t0 = time.perf_counter()
+    forced = forced or {}
     res = oracle.prefill(Q, K, V, wl.cu_seqlens, wl.num_kv_heads, wl.block_size, wl.alpha, wl.sel_scale,
-                         wl.min_sparse_len, 1.0 / math.sqrt(wl.head_dim), True, do_attend=False)
+                         wl.min_sparse_len, 1.0 / math.sqrt(wl.head_dim), mean_correction, do_attend=False, **forced)
     t_sel = time.perf_counter() - t0
     rng = np.random.default_rng(seed)
     nrows = len(res.row_ptr) - 1
@@ -171,12 +178,13 @@ def cpu_baseline(wl, row_ptr, n_rows, seed=0):
         I = b - blk_off[r]
         c = res.row_ptr[gr + 1] - res.row_ptr[gr]
         dense_req = wl.seqlens[r] < wl.min_sparse_len
-        return c * wl.block_size + (0 if dense_req else I - (c - 1))
+        return c * wl.block_size + (0 if dense_req or not mean_correction else I - (c - 1))
     total_cost = float(sum(row_cost(g) for g in range(nrows)))
     sample_cost = float(sum(row_cost(g) for g in sample))
     t0 = time.perf_counter()
     oracle.prefill(Q, K, V, wl.cu_seqlens, wl.num_kv_heads, wl.block_size, wl.alpha, wl.sel_scale,
-                   wl.min_sparse_len, 1.0 / math.sqrt(wl.head_dim), True, do_attend=True, rows=sample)
+                   wl.min_sparse_len, 1.0 / math.sqrt(wl.head_dim), mean_correction, do_attend=True, rows=sample,
+                   **forced)
     t_att_sample = time.perf_counter() - t0 - t_sel   # prefill re-runs pool+select first
     t_att = max(t_att_sample, 0.0) * total_cost / max(sample_cost, 1.0)
     sec = t_sel + t_att
@@ -203,6 +211,9 @@ def main():
 
     t0 = time.perf_counter()
     over = {} if args.alpha is None else {"alpha": args.alpha}
+    if args.seq_len is not None:
+        over["L"] = args.seq_len
+        over["n_planted"] = max(1, args.seq_len // 2048)  # the recipe's one planted block per 2048 tokens
     wl = synth.make_workload(args.workload, **over)
     t_gen = time.perf_counter() - t0
     dev = torch.device("cuda:0")
@@ -219,8 +230,8 @@ def main():
                       fp.FP_FP8_E4M3 if wl.dtype == "fp8" else fp.FP_BF16, descales, table,
                       wl.page_size, k.shape[0] if wl.paged else 0)
     bufs = fp.Buffers(prob, dev)
-    sel = fp.select_args(wl.alpha, wl.sel_scale, wl.min_sparse_len)
-    att = fp.attn_args(0.0, True)
+    sel = fp.select_args(wl.alpha, wl.sel_scale, wl.min_sparse_len, args.sink, args.window, args.last_n)
+    att = fp.attn_args(0.0, not args.no_mean_correction)
     torch.cuda.synchronize()
 
     def step(ev=None):
@@ -257,7 +268,7 @@ def main():
     col_idx = bufs.col_idx[: int(row_ptr[-1])].cpu().numpy()
     nbs = [-(-L // wl.block_size) for L in wl.seqlens]
     blk_off = np.concatenate([[0], np.cumsum(nbs)]).astype(np.int64)
-    flops, strict, kept = csr_work(row_ptr, col_idx, wl, blk_off)
+    flops, strict, kept = csr_work(row_ptr, col_idx, wl, blk_off, not args.no_mean_correction)
     att_avg = float(np.mean(att_ms))
     dense_eq = wl.dense_equiv_flops()
     peak = PEAK_TFLOPS[wl.dtype]
@@ -297,6 +308,8 @@ def main():
             "head_dim": wl.head_dim,
             "block_size": wl.block_size,
             "alpha": wl.alpha,
+            "forced_keep_blocks": {"sink": args.sink, "window": args.window, "last_n": args.last_n},
+            "mean_correction": not args.no_mean_correction,
             "sel_scale": wl.sel_scale,
             "min_sparse_len": wl.min_sparse_len,
             "paged": wl.paged,
@@ -328,7 +341,8 @@ def main():
     if not args.no_cpu_baseline:
         print(f"[bench] GPU timing done ({ms:.2f} ms/layer); timing the CPU oracle baseline", file=sys.stderr,
               flush=True)
-        rec["cpu_baseline"] = cpu_baseline(wl, row_ptr, args.cpu_rows)
+        rec["cpu_baseline"] = cpu_baseline(wl, row_ptr, args.cpu_rows, mean_correction=not args.no_mean_correction,
+                                           forced=dict(sink=args.sink, window=args.window, last_n=args.last_n))
     print(json.dumps(rec), flush=True)
 
 

@@ -62,7 +62,9 @@ class _Problem(ctypes.Structure):
 
 
 class _SelectArgs(ctypes.Structure):
-    _fields_ = [("alpha", ctypes.c_float), ("sel_scale", ctypes.c_float), ("min_sparse_len", ctypes.c_int32)]
+    _fields_ = [("alpha", ctypes.c_float), ("sel_scale", ctypes.c_float), ("min_sparse_len", ctypes.c_int32),
+                ("sink_blocks", ctypes.c_int32), ("window_blocks", ctypes.c_int32),
+                ("last_n_blocks", ctypes.c_int32)]
 
 
 class _AttnArgs(ctypes.Structure):
@@ -180,8 +182,10 @@ def _attn_workspace(prob: Problem, sparse: bool, workspace, device):
     return workspace
 
 
-def select_args(alpha: float, sel_scale: float = 1.0, min_sparse_len: int = 0) -> _SelectArgs:
-    return _SelectArgs(alpha, sel_scale, min_sparse_len)
+def select_args(alpha: float, sel_scale: float = 1.0, min_sparse_len: int = 0, sink: int = 0, window: int = 0,
+                last_n: int = 0) -> _SelectArgs:
+    """fp_select_args; sink / window / last_n are the forced keeps, in blocks."""
+    return _SelectArgs(alpha, sel_scale, min_sparse_len, sink, window, last_n)
 
 
 def attn_args(sm_scale: float = 0.0, mean_correction: bool = True) -> _AttnArgs:
@@ -245,11 +249,12 @@ class Buffers:
 
 
 def run_prefill(prob: Problem, bufs: Buffers, q, k, v, alpha: float, sel_scale: float = 1.0,
-                min_sparse_len: int = 0, sm_scale: float = 0.0, mean_correction: bool = True, stream=None):
+                min_sparse_len: int = 0, sm_scale: float = 0.0, mean_correction: bool = True, stream=None,
+                sink: int = 0, window: int = 0, last_n: int = 0):
     """All three stages on preallocated buffers (nothing allocated here)."""
     pool_blocks(prob, q, k, v, bufs.q_bar, bufs.k_bar, bufs.v_bar, stream)
-    select_blocks(prob, select_args(alpha, sel_scale, min_sparse_len), bufs.q_bar, bufs.k_bar, bufs.row_ptr,
-                  bufs.col_idx, bufs.workspace, stream)
+    select_blocks(prob, select_args(alpha, sel_scale, min_sparse_len, sink, window, last_n), bufs.q_bar, bufs.k_bar,
+                  bufs.row_ptr, bufs.col_idx, bufs.workspace, stream)
     sparse_prefill(prob, attn_args(sm_scale, mean_correction), q, k, v, bufs.k_bar, bufs.v_bar, bufs.row_ptr,
                    bufs.col_idx, bufs.out, bufs.lse, bufs.attn_workspace, stream)
     return bufs
@@ -258,13 +263,15 @@ def run_prefill(prob: Problem, bufs: Buffers, q, k, v, alpha: float, sel_scale: 
 def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: Sequence[int], block_size: int,
             alpha: float, sel_scale: float = 1.0, min_sparse_len: int = 0, sm_scale: float = 0.0,
             mean_correction: bool = True, descales: Optional[Sequence[torch.Tensor]] = None,
-            page_table: Optional[torch.Tensor] = None, page_size: int = 0):
+            page_table: Optional[torch.Tensor] = None, page_size: int = 0, sink: int = 0, window: int = 0,
+            last_n: int = 0):
     """Mean-corrected block-sparse causal prefill of a ragged batch.
 
     q [T, Hq, 128]; k, v [T, Hkv, 128] (contiguous) or page pools
     [num_pages, page_size, Hkv, 128] with ``page_table`` [R, max_pages]
     (int32, device). bf16, or float8_e4m3fn with ``descales`` = three
-    one-element fp32 device tensors. Returns a ``Buffers`` with out, lse,
+    one-element fp32 device tensors. ``sink`` / ``window`` / ``last_n`` are
+    the forced keeps, in blocks. Returns a ``Buffers`` with out, lse,
     row_ptr, col_idx and the pooled statistics.
     """
     Hq = q.shape[1]
@@ -273,4 +280,5 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: Seque
     prob = Problem(cu_seqlens, Hq, Hkv, block_size, q.shape[-1], dtype, descales, page_table, page_size,
                    k.shape[0] if page_table is not None else 0)
     bufs = Buffers(prob, q.device, q.shape[-1])
-    return run_prefill(prob, bufs, q, k, v, alpha, sel_scale, min_sparse_len, sm_scale, mean_correction)
+    return run_prefill(prob, bufs, q, k, v, alpha, sel_scale, min_sparse_len, sm_scale, mean_correction,
+                       sink=sink, window=window, last_n=last_n)

@@ -102,6 +102,9 @@ fp_status check_select(const fp_select_args* a) {
   if (std::isnan(a->alpha)) return fail(FP_ERR_ARG, "alpha is NaN");
   if (!std::isfinite(a->sel_scale)) return fail(FP_ERR_ARG, "sel_scale must be finite");
   if (a->min_sparse_len < 0) return fail(FP_ERR_ARG, "min_sparse_len=%d must be >= 0", a->min_sparse_len);
+  if (a->sink_blocks < 0 || a->window_blocks < 0 || a->last_n_blocks < 0)
+    return fail(FP_ERR_ARG, "sink_blocks=%d window_blocks=%d last_n_blocks=%d must be >= 0", a->sink_blocks,
+                a->window_blocks, a->last_n_blocks);
   return FP_OK;
 }
 
@@ -262,6 +265,9 @@ fp_status fp_select_blocks(const fp_problem* p, const fp_select_args* sel, const
   sp.all_keep = sel->alpha <= 0.f;
   sp.log_alpha = sel->alpha > 0.f ? (float)std::log((double)sel->alpha) : 0.f;
   sp.min_sparse_len = sel->min_sparse_len;
+  sp.sink = sel->sink_blocks;
+  sp.window = sel->window_blocks;
+  sp.last_n = sel->last_n_blocks;
   sp.Hkv = p->num_kv_heads; sp.NB_tot = (int32_t)s.NB_tot; sp.B = p->block_size;
   sp.rt = make_table(p, s);
   return hip_status(launch_select(sp, (hipStream_t)stream), "select launch");

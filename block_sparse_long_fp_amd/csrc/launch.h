@@ -37,6 +37,7 @@ struct SelectParams {
   float log_alpha;    // ln(alpha), fp32
   int32_t all_keep;   // alpha <= 0
   int32_t min_sparse_len;
+  int32_t sink, window, last_n;  // forced keeps, in blocks
   int32_t Hkv, NB_tot, B;
   ReqTable rt;
 };

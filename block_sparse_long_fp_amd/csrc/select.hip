@@ -10,7 +10,8 @@
 //
 // Row (h, I) of request r scores every causal key block J <= I with
 // z_J = tau * q_bar[h,I] . k_bar[h,J] (fp32), takes the row max m, and keeps J
-// iff z_J - m >= ln(alpha) (the same as exp(z_J - m) >= alpha), plus J = I.
+// iff z_J - m >= ln(alpha) (the same as exp(z_J - m) >= alpha), plus the
+// forced blocks (the diagonal, and optionally sink / window / last-n rows).
 //
 // Three kernels, no host round trip:
 //   score_kernel    one workgroup per (KV head, tile of 32 query blocks of one
@@ -42,6 +43,15 @@ __device__ __forceinline__ int64_t pair_offset(const ReqTable& rt, int r) {
     s += nb * (nb + 1) / 2;
   }
   return s;
+}
+
+// Blocks kept whatever their score: the diagonal, the attention sink (the
+// first p.sink blocks), the local window (p.window blocks left of the
+// diagonal) and every causal block of the request's last p.last_n query
+// blocks ([article] --flashprefill-attention-sink, --flashprefill-window,
+// --flashprefill-last-n-blocks; counts in blocks).
+__device__ __forceinline__ bool forced_keep(const SelectParams& p, int I, int J, int NB) {
+  return J == I || J < p.sink || J >= I - p.window || I >= NB - p.last_n;
 }
 
 __device__ __forceinline__ bool request_dense(const SelectParams& p, int r) {
@@ -127,7 +137,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(SelectParams p) {
   // Count: each thread re-reads the z values it wrote itself.
   int cnt = 0;
   if (row_ok) {
-    for (int J = jq; J <= I; J += 8) cnt += ((zrow[J] - m) >= p.log_alpha) || (J == I);
+    for (int J = jq; J <= I; J += 8) cnt += ((zrow[J] - m) >= p.log_alpha) || forced_keep(p, I, J, NB);
   }
   cnt += __shfl_xor(cnt, 1);
   cnt += __shfl_xor(cnt, 2);
@@ -184,6 +194,7 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(SelectParams p
   int r = 0;
   while (r + 1 < rt.R && rt.blk_off[r + 1] <= b) ++r;
   const int I = b - rt.blk_off[r];
+  const int NB = rt.blk_off[r + 1] - rt.blk_off[r];
   int32_t* out = p.col_idx + p.row_ptr[row];
   if (request_dense(p, r)) {
     for (int J = lane; J <= I; J += 64) out[J] = J;
@@ -194,7 +205,7 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(SelectParams p
   int base = 0;
   for (int J0 = 0; J0 <= I; J0 += 64) {
     const int J = J0 + lane;
-    const bool keep = (J <= I) && (((zrow[J] - m) >= p.log_alpha) || (J == I));
+    const bool keep = (J <= I) && (((zrow[J] - m) >= p.log_alpha) || forced_keep(p, I, J, NB));
     const uint64_t mask = __ballot(keep);
     const int pre = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
     if (keep) out[base + pre] = J;

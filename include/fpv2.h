@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define FPV2_ABI_VERSION 2
+#define FPV2_ABI_VERSION 3
 
 /* Status codes. */
 typedef int32_t fp_status;
@@ -119,11 +119,18 @@ typedef struct fp_problem {
 /* Block selection ([digest] abstract: max-based dynamic thresholding;
  * [article] flags --flashprefill-abs-threshold and -min-sparse-q-len).
  * Row (h, I) scores z_J = sel_scale * q_bar[h,I] . k_bar[h,J] for J <= I and
- * keeps J iff exp(z_J - max_J z_J) >= alpha, plus the diagonal J = I. */
+ * keeps J iff exp(z_J - max_J z_J) >= alpha, plus the forced blocks: the
+ * diagonal J = I always, and ([article] flags --flashprefill-attention-sink,
+ * --flashprefill-window, --flashprefill-last-n-blocks; all counted in blocks,
+ * 0 = off) J < sink_blocks, J >= I - window_blocks, and every J <= I when I is
+ * one of the request's last last_n_blocks query blocks. */
 typedef struct fp_select_args {
   float alpha;                   /* threshold; alpha <= 0 keeps every causal block */
   float sel_scale;               /* score temperature tau, finite                  */
   int32_t min_sparse_len;        /* requests with L_r < this keep every causal block */
+  int32_t sink_blocks;           /* >= 0 */
+  int32_t window_blocks;         /* >= 0 */
+  int32_t last_n_blocks;         /* >= 0 */
 } fp_select_args;
 
 /* Attention ([digest] Figures 3-4). */

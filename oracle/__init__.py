@@ -10,6 +10,7 @@ from .oracle import (  # noqa: F401
     pool_keys,
     pool_queries,
     select_blocks,
+    forced_keep,
     attend,
     attend_row,
     attend_loop,

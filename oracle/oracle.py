@@ -83,15 +83,31 @@ def pool_queries(Q: np.ndarray, B: int, G: int) -> np.ndarray:
     return out
 
 
+def forced_keep(I: int, NB: int, sink: int = 0, window: int = 0, last_n: int = 0) -> np.ndarray:
+    """Blocks J <= I a row keeps whatever their score: the diagonal, the first
+    ``sink`` blocks (attention sink), the ``window`` blocks left of the
+    diagonal (local window), and every causal block when I is one of the
+    request's last ``last_n`` query blocks ([article] SGLang flags
+    --flashprefill-attention-sink, --flashprefill-window and
+    --flashprefill-last-n-blocks; counts are in blocks)."""
+    J = np.arange(I + 1)
+    keep = (J == I) | (J < sink) | (J >= I - window)
+    if I >= NB - last_n:
+        keep[:] = True
+    return keep
+
+
 def select_blocks(qbar: np.ndarray, kbar: np.ndarray, alpha: float, sel_scale: float = 1.0,
-                  dense: bool = False, band_rel: float = 1e-4):
+                  dense: bool = False, band_rel: float = 1e-4, sink: int = 0, window: int = 0,
+                  last_n: int = 0):
     """Step 3: per (h, I) the ascending list of kept key blocks.
 
     [digest] abstract and Table 9 (alpha, "max-based dynamic thresholding");
-    the diagonal is always kept. Returns (sets, near): sets[h][I] is an int64
-    array; ``near`` lists (h, I, J) whose exp(z - m) lies within
-    band_rel * alpha of alpha, the pairs a float32 implementation may decide
-    either way.
+    the diagonal is always kept, and so are the forced blocks of
+    ``forced_keep`` (all off by default). Returns (sets, near): sets[h][I] is
+    an int64 array; ``near`` lists (h, I, J) whose exp(z - m) lies within
+    band_rel * alpha of alpha and that no rule forces, the pairs a float32
+    implementation may decide either way.
     """
     Hkv, NB, d = qbar.shape
     sets: List[List[np.ndarray]] = []
@@ -105,11 +121,10 @@ def select_blocks(qbar: np.ndarray, kbar: np.ndarray, alpha: float, sel_scale: f
             z = sel_scale * (kbar[h, :I + 1, :] @ qbar[h, I, :])   # [I+1]
             m = z.max()
             ratio = np.exp(z - m)
-            keep = ratio >= alpha
-            keep[I] = True
+            forced = forced_keep(I, NB, sink, window, last_n)
+            keep = (ratio >= alpha) | forced
             rows.append(np.nonzero(keep)[0].astype(np.int64))
-            close = np.abs(ratio - alpha) <= band_rel * alpha
-            close[I] = False
+            close = (np.abs(ratio - alpha) <= band_rel * alpha) & ~forced
             near.extend((h, I, int(J)) for J in np.nonzero(close)[0])
         sets.append(rows)
     return sets, near
@@ -257,7 +272,7 @@ def prefill(Q: np.ndarray, K: np.ndarray, V: np.ndarray, cu_seqlens: Sequence[in
             B: int, alpha: float, sel_scale: float = 1.0, min_sparse_len: int = 0,
             sm_scale: Optional[float] = None, mean_correction: bool = True, do_attend: bool = True,
             rows: Optional[Sequence[int]] = None, K_pages=None, V_pages=None, page_table=None,
-            page_size: int = 0) -> OracleResult:
+            page_size: int = 0, sink: int = 0, window: int = 0, last_n: int = 0) -> OracleResult:
     """The whole path over a ragged batch ([digest] Fix 3: continuous batching).
 
     Q [T, Hq, d] and (contiguous) K, V [T, Hkv, d] hold the dequantised fp64
@@ -265,6 +280,7 @@ def prefill(Q: np.ndarray, K: np.ndarray, V: np.ndarray, cu_seqlens: Sequence[in
     through the page table from ``K_pages``/``V_pages``. Requests shorter than
     ``min_sparse_len`` run dense ([article] minimum sparse query length flag).
     ``rows`` limits attention to some global CSR rows (h*NB_tot + blk_off[r] + I).
+    ``sink``, ``window``, ``last_n``: forced keeps per request (``forced_keep``).
     """
     T, Hq, d = Q.shape
     Hkv = num_kv_heads
@@ -301,7 +317,7 @@ def prefill(Q: np.ndarray, K: np.ndarray, V: np.ndarray, cu_seqlens: Sequence[in
         a, b = blk_off[r], blk_off[r + 1]
         qbar[:, a:b], kbar[:, a:b], vbar[:, a:b] = qb, kb, vb
         dense = L < min_sparse_len
-        sets, nr = select_blocks(qb, kb, alpha, sel_scale, dense=dense)
+        sets, nr = select_blocks(qb, kb, alpha, sel_scale, dense=dense, sink=sink, window=window, last_n=last_n)
         all_sets.append(sets)
         near.extend((h * NBt + a + I, J) for (h, I, J) in nr)
         if do_attend:

@@ -36,8 +36,9 @@ def upload(wl, device="cuda:0", paged: Optional[bool] = None):
 
 
 def run_gpu(wl, alpha=None, mean_correction=True, paged=None, dense=False, min_sparse_len=None,
-            device="cuda:0"):
-    """Run pool -> select -> attention (or the dense kernel); return CPU results."""
+            device="cuda:0", forced=None):
+    """Run pool -> select -> attention (or the dense kernel); return CPU results.
+    ``forced``: dict(sink=, window=, last_n=) forced keeps, in blocks."""
     alpha = wl.alpha if alpha is None else alpha
     msl = wl.min_sparse_len if min_sparse_len is None else min_sparse_len
     prob, q, k, v = upload(wl, device, paged)
@@ -45,7 +46,7 @@ def run_gpu(wl, alpha=None, mean_correction=True, paged=None, dense=False, min_s
     if dense:
         fp.dense_prefill(prob, fp.attn_args(), q, k, v, bufs.out, bufs.lse)
     else:
-        fp.run_prefill(prob, bufs, q, k, v, alpha, wl.sel_scale, msl, 0.0, mean_correction)
+        fp.run_prefill(prob, bufs, q, k, v, alpha, wl.sel_scale, msl, 0.0, mean_correction, **(forced or {}))
     torch.cuda.synchronize()
     res = dict(out=bufs.out.float().cpu().numpy(), lse=bufs.lse.cpu().numpy())
     if not dense:
@@ -68,7 +69,7 @@ def host_values(wl):
 
 
 def run_oracle(wl, alpha=None, mean_correction=True, do_attend=True, rows=None, paged=None,
-               min_sparse_len=None, Qkv=None):
+               min_sparse_len=None, Qkv=None, forced=None):
     alpha = wl.alpha if alpha is None else alpha
     msl = wl.min_sparse_len if min_sparse_len is None else min_sparse_len
     Q, K, V = host_values(wl) if Qkv is None else Qkv
@@ -80,7 +81,7 @@ def run_oracle(wl, alpha=None, mean_correction=True, do_attend=True, rows=None, 
         kw = dict(K_pages=kp, V_pages=vp, page_table=wl.page_table.numpy(), page_size=wl.page_size)
         K = V = None
     return oracle.prefill(Q, K, V, wl.cu_seqlens, wl.num_kv_heads, wl.block_size, alpha, wl.sel_scale, msl,
-                          1.0 / math.sqrt(wl.head_dim), mean_correction, do_attend, rows, **kw)
+                          1.0 / math.sqrt(wl.head_dim), mean_correction, do_attend, rows, **kw, **(forced or {}))
 
 
 def csr_rows(row_ptr, col_idx):

@@ -17,12 +17,13 @@ import oracle
 pytestmark = pytest.mark.gpu
 
 
-def _check_full(wl, alpha=None, mean_correction=True, paged=None, min_sparse_len=None):
+def _check_full(wl, alpha=None, mean_correction=True, paged=None, min_sparse_len=None, forced=None):
     print(f"[parity] {wl.name} L={wl.seqlens} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} B={wl.block_size} "
           f"dtype={wl.dtype} alpha={alpha if alpha is not None else wl.alpha} mc={mean_correction} "
-          f"paged={paged if paged is not None else wl.paged}", flush=True)
-    gpu = run_gpu(wl, alpha, mean_correction, paged, min_sparse_len=min_sparse_len)
-    orc = run_oracle(wl, alpha, mean_correction, do_attend=False, paged=paged, min_sparse_len=min_sparse_len)
+          f"paged={paged if paged is not None else wl.paged} forced={forced}", flush=True)
+    gpu = run_gpu(wl, alpha, mean_correction, paged, min_sparse_len=min_sparse_len, forced=forced)
+    orc = run_oracle(wl, alpha, mean_correction, do_attend=False, paged=paged, min_sparse_len=min_sparse_len,
+                     forced=forced)
     compare_pooled(gpu, orc)
     n_near = compare_csr(gpu, orc)
     # Attention on the CSR the GPU chose (identical to the oracle's outside the band).
@@ -129,6 +130,26 @@ def test_single_token_and_one_block_requests():
     wl = synth.make_workload("qwen4b_varlen_paged", lengths=[1, 2, 127, 128, 129], Hq=4, Hkv=2, page_size=16,
                              min_sparse_len=0, n_planted=0)
     _check_full(wl)
+
+
+@pytest.mark.parametrize("forced", [dict(sink=2, window=4, last_n=8), dict(sink=1, window=0, last_n=0),
+                                    dict(sink=0, window=2, last_n=3)])
+def test_forced_keeps_sink_window_last_n(forced):
+    """The article's serving flags (attention sink 2, window 4, last-n 8
+    blocks) and single rules, on a ragged GQA-4 batch."""
+    wl = synth.make_workload("llama_32k", lengths=[3000, 5000], Hq=8, Hkv=2, n_planted=4, kind="varlen",
+                             seeds_base=7, page_size=0, min_sparse_len=0)
+    gpu = _check_full(wl, forced=forced)
+    # every forced block is in the GPU's CSR
+    nb = [-(-L // wl.block_size) for L in wl.seqlens]
+    off = np.concatenate([[0], np.cumsum(nb)])
+    for h in range(wl.num_kv_heads):
+        for r, NB in enumerate(nb):
+            for I in range(NB):
+                row = h * off[-1] + off[r] + I
+                cols = set(gpu["col_idx"][gpu["row_ptr"][row]:gpu["row_ptr"][row + 1]].tolist())
+                want = set(np.nonzero(oracle.forced_keep(I, NB, **forced))[0].tolist())
+                assert want <= cols, (h, r, I)
 
 
 def test_runs_are_bitwise_deterministic():

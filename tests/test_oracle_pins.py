@@ -363,3 +363,30 @@ def test_sampled_rows_match_full_run():
         hs = slice(h * 2, h * 2 + 2)
         assert np.array_equal(part.O[s:e, hs], full.O[s:e, hs])
         assert np.array_equal(part.LSE[hs, s:e], full.LSE[hs, s:e])
+
+
+@pytest.mark.parametrize("sink,window,last_n", [(2, 4, 8), (1, 0, 0), (0, 3, 0), (0, 0, 2), (40, 40, 40)])
+def test_forced_keeps_rules(sink, window, last_n):
+    """[article] serving flags: attention sink, local window and dense last-n
+    query blocks, all counted in blocks. With alpha > 1 only forced blocks
+    survive, so each row must be exactly the rule's set (built here from
+    Python sets); with a real alpha the row is the unforced selection united
+    with the forced set, and no forced pair is listed as near-threshold."""
+    rng = np.random.default_rng(11)
+    Hkv, NB, d = 2, 13, 16
+    qbar = rng.standard_normal((Hkv, NB, d))
+    kbar = rng.standard_normal((Hkv, NB, d))
+    only, _ = oracle.select_blocks(qbar, kbar, 2.0, sink=sink, window=window, last_n=last_n)
+    for h in range(Hkv):
+        for I in range(NB):
+            want = {I} | {J for J in range(min(sink, I + 1))} | {J for J in range(max(0, I - window), I + 1)}
+            if I >= NB - last_n:
+                want = set(range(I + 1))
+            assert set(only[h][I].tolist()) == want, (h, I)
+    plain, _ = oracle.select_blocks(qbar, kbar, 0.3)
+    forced, near = oracle.select_blocks(qbar, kbar, 0.3, sink=sink, window=window, last_n=last_n)
+    for h in range(Hkv):
+        for I in range(NB):
+            assert set(forced[h][I].tolist()) == set(plain[h][I].tolist()) | set(only[h][I].tolist())
+    for h, I, J in near:
+        assert J not in set(only[h][I].tolist())
