@@ -58,6 +58,7 @@ class _Problem(ctypes.Structure):
         ("page_size", ctypes.c_int32),
         ("max_pages_per_seq", ctypes.c_int32),
         ("num_pages", ctypes.c_int32),
+        ("cu_seqlens_k", ctypes.POINTER(ctypes.c_int32)),
     ]
 
 
@@ -83,7 +84,7 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         P = ctypes.POINTER(_Problem)
         vp, i64p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64)
-        L.fp_index_shape.argtypes = [P, i64p, i64p, i64p]
+        L.fp_index_shape.argtypes = [P, i64p, i64p, i64p, i64p]
         L.fp_select_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
         L.fp_validate.argtypes = [P, ctypes.POINTER(_SelectArgs), ctypes.POINTER(_AttnArgs)]
         L.fp_pool_blocks.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
@@ -122,18 +123,27 @@ def _stream(stream=None):
 
 
 class Problem:
-    """Holds an fp_problem and keeps its host arrays alive."""
+    """Holds an fp_problem and keeps its host arrays alive.
+
+    ``cu_seqlens`` are the query offsets; ``cu_seqlens_k`` (None: the same) the
+    key offsets. In chunked prefill request r's queries are the last
+    Lq_r = cu_seqlens[r+1] - cu_seqlens[r] of its Lk_r keys."""
 
     def __init__(self, cu_seqlens: Sequence[int], num_q_heads: int, num_kv_heads: int, block_size: int,
                  head_dim: int = 128, dtype: int = FP_BF16, descales: Optional[Sequence[torch.Tensor]] = None,
-                 page_table: Optional[torch.Tensor] = None, page_size: int = 0, num_pages: int = 0):
+                 page_table: Optional[torch.Tensor] = None, page_size: int = 0, num_pages: int = 0,
+                 cu_seqlens_k: Optional[Sequence[int]] = None):
         cu = [int(x) for x in cu_seqlens]
         self.cu_seqlens = cu
+        self.cu_seqlens_k = cu if cu_seqlens_k is None else [int(x) for x in cu_seqlens_k]
         self._cu = (ctypes.c_int32 * len(cu))(*cu)
         self._keep = []
         s = _Problem()
         s.num_seqs = len(cu) - 1
         s.cu_seqlens = ctypes.cast(self._cu, ctypes.POINTER(ctypes.c_int32))
+        if cu_seqlens_k is not None:
+            self._cuk = (ctypes.c_int32 * len(self.cu_seqlens_k))(*self.cu_seqlens_k)
+            s.cu_seqlens_k = ctypes.cast(self._cuk, ctypes.POINTER(ctypes.c_int32))
         s.num_q_heads, s.num_kv_heads, s.head_dim, s.block_size = num_q_heads, num_kv_heads, head_dim, block_size
         s.dtype = dtype
         if descales is not None:
@@ -156,9 +166,11 @@ class Problem:
 
 
 def index_shape(prob: Problem):
-    rows, nnz, nb = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
-    _check(lib().fp_index_shape(prob.ref, ctypes.byref(rows), ctypes.byref(nnz), ctypes.byref(nb)))
-    return rows.value, nnz.value, nb.value
+    """(CSR rows, worst-case nnz, query blocks NBq_tot, key blocks NBk_tot)."""
+    rows, nnz, nbq, nbk = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().fp_index_shape(prob.ref, ctypes.byref(rows), ctypes.byref(nnz), ctypes.byref(nbq),
+                                ctypes.byref(nbk)))
+    return rows.value, nnz.value, nbq.value, nbk.value
 
 
 def select_workspace_bytes(prob: Problem) -> int:
@@ -231,14 +243,14 @@ class Buffers:
     """Device buffers of one prefill problem (allocated with torch)."""
 
     def __init__(self, prob: Problem, device, head_dim: int = 128):
-        rows, nnz, nb = index_shape(prob)
+        rows, nnz, nbq, nbk = index_shape(prob)
         Hkv = prob.s.num_kv_heads
         T = prob.cu_seqlens[-1]
         Hq = prob.s.num_q_heads
         f32 = dict(dtype=torch.float32, device=device)
-        self.q_bar = torch.empty((Hkv, nb, head_dim), **f32)
-        self.k_bar = torch.empty((Hkv, nb, head_dim), **f32)
-        self.v_bar = torch.empty((Hkv, nb, head_dim), **f32)
+        self.q_bar = torch.empty((Hkv, nbq, head_dim), **f32)
+        self.k_bar = torch.empty((Hkv, nbk, head_dim), **f32)
+        self.v_bar = torch.empty((Hkv, nbk, head_dim), **f32)
         self.row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=device)
         self.col_idx = torch.empty(max(nnz, 1), dtype=torch.int32, device=device)
         self.workspace = torch.empty(select_workspace_bytes(prob), dtype=torch.uint8, device=device)
@@ -264,21 +276,22 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: Seque
             alpha: float, sel_scale: float = 1.0, min_sparse_len: int = 0, sm_scale: float = 0.0,
             mean_correction: bool = True, descales: Optional[Sequence[torch.Tensor]] = None,
             page_table: Optional[torch.Tensor] = None, page_size: int = 0, sink: int = 0, window: int = 0,
-            last_n: int = 0):
+            last_n: int = 0, cu_seqlens_k: Optional[Sequence[int]] = None):
     """Mean-corrected block-sparse causal prefill of a ragged batch.
 
-    q [T, Hq, 128]; k, v [T, Hkv, 128] (contiguous) or page pools
+    q [Tq, Hq, 128]; k, v [Tk, Hkv, 128] (contiguous) or page pools
     [num_pages, page_size, Hkv, 128] with ``page_table`` [R, max_pages]
     (int32, device). bf16, or float8_e4m3fn with ``descales`` = three
     one-element fp32 device tensors. ``sink`` / ``window`` / ``last_n`` are
-    the forced keeps, in blocks. Returns a ``Buffers`` with out, lse,
-    row_ptr, col_idx and the pooled statistics.
+    the forced keeps, in blocks. ``cu_seqlens_k`` (chunked prefill): key
+    offsets; each request's queries are its last positions. Returns a
+    ``Buffers`` with out, lse, row_ptr, col_idx and the pooled statistics.
     """
     Hq = q.shape[1]
     Hkv = k.shape[-2]
     dtype = FP_FP8_E4M3 if q.dtype == torch.float8_e4m3fn else FP_BF16
     prob = Problem(cu_seqlens, Hq, Hkv, block_size, q.shape[-1], dtype, descales, page_table, page_size,
-                   k.shape[0] if page_table is not None else 0)
+                   k.shape[0] if page_table is not None else 0, cu_seqlens_k)
     bufs = Buffers(prob, q.device, q.shape[-1])
     return run_prefill(prob, bufs, q, k, v, alpha, sel_scale, min_sparse_len, sm_scale, mean_correction,
                        sink=sink, window=window, last_n=last_n)

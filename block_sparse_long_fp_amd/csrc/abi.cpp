@@ -34,11 +34,14 @@ fp_status ok() {
 // Host-side shape facts derived from a validated problem.
 struct Shape {
   int R;
-  int64_t T;
-  int64_t NB_tot;
-  int64_t pairs;  // sum_r NB_r (NB_r + 1) / 2
-  int nb_max;
+  int64_t Tq, Tk;
+  int64_t NBq_tot, NBk_tot;
+  int64_t pairs;  // causal (query block, key block) pairs per KV head
+  int nb_max;     // max_r NBk_r
 };
+
+// Key offsets of the problem: cu_seqlens_k, or cu_seqlens for a whole prefill.
+const int32_t* key_offsets(const fp_problem* p) { return p->cu_seqlens_k ? p->cu_seqlens_k : p->cu_seqlens; }
 
 fp_status check_problem(const fp_problem* p, Shape* sh) {
   if (!p) return fail(FP_ERR_NULL, "problem is NULL");
@@ -56,41 +59,58 @@ fp_status check_problem(const fp_problem* p, Shape* sh) {
   if (p->dtype != FP_BF16 && p->dtype != FP_FP8_E4M3) return fail(FP_ERR_DTYPE, "dtype=%d unknown", p->dtype);
   if (p->dtype == FP_FP8_E4M3 && (!p->descale_q || !p->descale_k || !p->descale_v))
     return fail(FP_ERR_DTYPE, "FP8 needs descale_q, descale_k and descale_v");
+  const int32_t* cuk = key_offsets(p);
   if (p->cu_seqlens[0] != 0) return fail(FP_ERR_SHAPE, "cu_seqlens[0]=%d must be 0", p->cu_seqlens[0]);
+  if (cuk[0] != 0) return fail(FP_ERR_SHAPE, "cu_seqlens_k[0]=%d must be 0", cuk[0]);
+  const int B = p->block_size;
   Shape s{};
   s.R = p->num_seqs;
-  int64_t nb_tot = 0, pairs = 0;
-  int nb_max = 0, len_max = 0;
+  int64_t nbq_tot = 0, nbk_tot = 0, pairs = 0, tq = 0, tk = 0;
+  int nb_max = 0, lk_max = 0;
   for (int r = 0; r < p->num_seqs; ++r) {
-    const int64_t L = (int64_t)p->cu_seqlens[r + 1] - p->cu_seqlens[r];
-    if (L < 1) return fail(FP_ERR_SHAPE, "request %d has length %lld (cu_seqlens must increase)", r, (long long)L);
-    const int64_t nb = (L + p->block_size - 1) / p->block_size;
-    if (nb > FP_MAX_BLOCKS_PER_SEQ)
-      return fail(FP_ERR_UNSUPPORTED, "request %d has %lld blocks (max %d)", r, (long long)nb, FP_MAX_BLOCKS_PER_SEQ);
-    nb_tot += nb;
-    pairs += nb * (nb + 1) / 2;
-    if (nb > nb_max) nb_max = (int)nb;
-    if (L > len_max) len_max = (int)L;
+    const int64_t Lq = (int64_t)p->cu_seqlens[r + 1] - p->cu_seqlens[r];
+    const int64_t Lk = (int64_t)cuk[r + 1] - cuk[r];
+    if (Lq < 1) return fail(FP_ERR_SHAPE, "request %d has %lld queries (cu_seqlens must increase)", r, (long long)Lq);
+    if (Lk < Lq)
+      return fail(FP_ERR_SHAPE, "request %d has %lld keys < %lld queries", r, (long long)Lk, (long long)Lq);
+    if ((Lk - Lq) % B != 0)
+      return fail(FP_ERR_SHAPE, "request %d: chunk offset %lld is not a multiple of block_size %d", r,
+                  (long long)(Lk - Lq), B);
+    const int64_t nbk = (Lk + B - 1) / B;
+    const int64_t nbq = (Lq + B - 1) / B;
+    const int64_t qb0 = (Lk - Lq) / B;
+    if (nbk > FP_MAX_BLOCKS_PER_SEQ)
+      return fail(FP_ERR_UNSUPPORTED, "request %d has %lld blocks (max %d)", r, (long long)nbk, FP_MAX_BLOCKS_PER_SEQ);
+    nbq_tot += nbq;
+    nbk_tot += nbk;
+    pairs += nbq * qb0 + nbq * (nbq + 1) / 2;
+    tq += Lq;
+    tk += Lk;
+    if (nbk > nb_max) nb_max = (int)nbk;
+    if (Lk > lk_max) lk_max = (int)Lk;
   }
-  s.T = p->cu_seqlens[p->num_seqs];
+  if (tq > INT32_MAX || tk > INT32_MAX) return fail(FP_ERR_UNSUPPORTED, "more than 2^31 tokens");
+  s.Tq = tq;
+  s.Tk = tk;
   if ((int64_t)p->num_kv_heads * pairs > INT32_MAX)
     return fail(FP_ERR_UNSUPPORTED, "worst-case nnz %lld exceeds int32 CSR offsets",
                 (long long)((int64_t)p->num_kv_heads * pairs));
-  if (s.T * p->num_q_heads > INT32_MAX)
-    return fail(FP_ERR_UNSUPPORTED, "T * num_q_heads = %lld exceeds int32 LSE indexing",
-                (long long)(s.T * p->num_q_heads));
+  if (s.Tq * p->num_q_heads > INT32_MAX)
+    return fail(FP_ERR_UNSUPPORTED, "Tq * num_q_heads = %lld exceeds int32 LSE indexing",
+                (long long)(s.Tq * p->num_q_heads));
   if (p->kv_layout == FP_KV_PAGED) {
     if (!p->page_table) return fail(FP_ERR_NULL, "paged layout needs page_table");
     if (p->page_size < 1) return fail(FP_ERR_LAYOUT, "page_size=%d must be >= 1", p->page_size);
     if (p->num_pages < 1) return fail(FP_ERR_LAYOUT, "num_pages=%d must be >= 1", p->num_pages);
-    const int64_t need = ((int64_t)len_max + p->page_size - 1) / p->page_size;
+    const int64_t need = ((int64_t)lk_max + p->page_size - 1) / p->page_size;
     if (p->max_pages_per_seq < need)
       return fail(FP_ERR_LAYOUT, "max_pages_per_seq=%d < %lld pages of the longest request", p->max_pages_per_seq,
                   (long long)need);
   } else if (p->kv_layout != FP_KV_CONTIGUOUS) {
     return fail(FP_ERR_LAYOUT, "kv_layout=%d unknown", p->kv_layout);
   }
-  s.NB_tot = nb_tot;
+  s.NBq_tot = nbq_tot;
+  s.NBk_tot = nbk_tot;
   s.pairs = pairs;
   s.nb_max = nb_max;
   if (sh) *sh = s;
@@ -118,13 +138,22 @@ fp_status check_attn(const fp_attn_args* a) {
 
 ReqTable make_table(const fp_problem* p, const Shape& s) {
   ReqTable t{};
+  const int32_t* cuk = key_offsets(p);
+  const int B = p->block_size;
   t.R = s.R;
   t.nb_max = s.nb_max;
   t.blk_off[0] = 0;
-  for (int r = 0; r <= s.R; ++r) t.tok_off[r] = p->cu_seqlens[r];
+  t.kblk_off[0] = 0;
+  for (int r = 0; r <= s.R; ++r) {
+    t.tok_off[r] = p->cu_seqlens[r];
+    t.ktok_off[r] = cuk[r];
+  }
   for (int r = 0; r < s.R; ++r) {
-    const int L = p->cu_seqlens[r + 1] - p->cu_seqlens[r];
-    t.blk_off[r + 1] = t.blk_off[r] + (L + p->block_size - 1) / p->block_size;
+    const int Lq = p->cu_seqlens[r + 1] - p->cu_seqlens[r];
+    const int Lk = cuk[r + 1] - cuk[r];
+    t.blk_off[r + 1] = t.blk_off[r] + (Lq + B - 1) / B;
+    t.kblk_off[r + 1] = t.kblk_off[r] + (Lk + B - 1) / B;
+    t.qb0[r] = (Lk - Lq) / B;
   }
   return t;
 }
@@ -146,7 +175,7 @@ struct WsLayout {
 
 WsLayout ws_layout(const fp_problem* p, const Shape& s) {
   WsLayout w{};
-  const int64_t rows = (int64_t)p->num_kv_heads * s.NB_tot;
+  const int64_t rows = (int64_t)p->num_kv_heads * s.NBq_tot;
   w.z = 0;
   w.rowmax = align256((size_t)p->num_kv_heads * s.pairs * sizeof(float));
   w.counts = w.rowmax + align256((size_t)rows * sizeof(float));
@@ -163,9 +192,9 @@ struct AttnWs {
 
 AttnWs attn_ws_layout(const fp_problem* p, const Shape& s, bool sparse) {
   AttnWs w{};
-  const int64_t kv_rows = p->kv_layout == FP_KV_PAGED ? (int64_t)p->num_pages * p->page_size : s.T;
+  const int64_t kv_rows = p->kv_layout == FP_KV_PAGED ? (int64_t)p->num_pages * p->page_size : s.Tk;
   w.kv_elems = kv_rows * p->num_kv_heads * p->head_dim;
-  const size_t pool = sparse ? align256((size_t)p->num_kv_heads * s.NB_tot * p->head_dim * 2) : 0;
+  const size_t pool = sparse ? align256((size_t)p->num_kv_heads * s.NBk_tot * p->head_dim * 2) : 0;
   const size_t kv = p->dtype == FP_FP8_E4M3 ? align256((size_t)w.kv_elems * 2) : 0;
   w.kbar16 = 0;
   w.vbar16 = pool;
@@ -185,13 +214,15 @@ fp_status hip_status(hipError_t e, const char* what) {
 
 extern "C" {
 
-fp_status fp_index_shape(const fp_problem* p, int64_t* num_rows, int64_t* max_nnz, int64_t* num_blocks) {
+fp_status fp_index_shape(const fp_problem* p, int64_t* num_rows, int64_t* max_nnz, int64_t* num_q_blocks,
+                         int64_t* num_k_blocks) {
   Shape s;
   fp_status st = check_problem(p, &s);
   if (st) return st;
-  if (num_rows) *num_rows = (int64_t)p->num_kv_heads * s.NB_tot;
+  if (num_rows) *num_rows = (int64_t)p->num_kv_heads * s.NBq_tot;
   if (max_nnz) *max_nnz = (int64_t)p->num_kv_heads * s.pairs;
-  if (num_blocks) *num_blocks = s.NB_tot;
+  if (num_q_blocks) *num_q_blocks = s.NBq_tot;
+  if (num_k_blocks) *num_k_blocks = s.NBk_tot;
   return ok();
 }
 
@@ -232,7 +263,8 @@ fp_status fp_pool_blocks(const fp_problem* p, const void* q, const void* k, cons
   pp.q_bar = q_bar; pp.k_bar = k_bar; pp.v_bar = v_bar;
   pp.descale_q = p->descale_q; pp.descale_k = p->descale_k; pp.descale_v = p->descale_v;
   pp.Hq = p->num_q_heads; pp.Hkv = p->num_kv_heads; pp.G = p->num_q_heads / p->num_kv_heads;
-  pp.B = p->block_size; pp.NB_tot = (int32_t)s.NB_tot; pp.fp8 = p->dtype == FP_FP8_E4M3;
+  pp.B = p->block_size; pp.NBq_tot = (int32_t)s.NBq_tot; pp.NBk_tot = (int32_t)s.NBk_tot;
+  pp.fp8 = p->dtype == FP_FP8_E4M3;
   pp.kv = make_kv(p);
   pp.rt = make_table(p, s);
   if (pool_lds_bytes(pp.G) > 64 * 1024) return fail(FP_ERR_UNSUPPORTED, "GQA ratio %d too large for pooling", pp.G);
@@ -268,7 +300,8 @@ fp_status fp_select_blocks(const fp_problem* p, const fp_select_args* sel, const
   sp.sink = sel->sink_blocks;
   sp.window = sel->window_blocks;
   sp.last_n = sel->last_n_blocks;
-  sp.Hkv = p->num_kv_heads; sp.NB_tot = (int32_t)s.NB_tot; sp.B = p->block_size;
+  sp.Hkv = p->num_kv_heads; sp.NBq_tot = (int32_t)s.NBq_tot; sp.NBk_tot = (int32_t)s.NBk_tot;
+  sp.B = p->block_size;
   sp.rt = make_table(p, s);
   return hip_status(launch_select(sp, (hipStream_t)stream), "select launch");
 }
@@ -307,7 +340,8 @@ static fp_status run_attention(const fp_problem* p, const fp_attn_args* attn, co
   ap.descale_q = p->descale_q; ap.descale_k = p->descale_k; ap.descale_v = p->descale_v;
   ap.sm_scale = attn->sm_scale > 0.f ? attn->sm_scale : 1.0f / std::sqrt((float)p->head_dim);
   ap.Hq = p->num_q_heads; ap.Hkv = p->num_kv_heads; ap.G = p->num_q_heads / p->num_kv_heads;
-  ap.B = p->block_size; ap.NB_tot = (int32_t)s.NB_tot; ap.T = (int32_t)s.T;
+  ap.B = p->block_size; ap.NBq_tot = (int32_t)s.NBq_tot; ap.NBk_tot = (int32_t)s.NBk_tot;
+  ap.T = (int32_t)s.Tq;
   ap.mean_correction = dense ? 0 : attn->mean_correction;
   ap.dense = dense ? 1 : 0;
   ap.subs = (ap.G * ap.B + attn_rows_per_wg() - 1) / attn_rows_per_wg();

@@ -92,8 +92,8 @@ struct RowCtx {
   int n_exact;          // CSR entries (key blocks) of the row
   int n_items;          // plus the correction chunks
   const int32_t* cols;  // CSR row (nullptr in dense mode)
-  int64_t pooled_row0;  // row h * NB_tot + blk_off[r] of k_bar / v_bar
-  int64_t tok_base;     // first token of the request
+  int64_t pooled_row0;  // row h * NBk_tot + kblk_off[r] of k_bar / v_bar
+  int64_t tok_base;     // first key token of the request (contiguous K / V)
 };
 
 // Combine lane c with lane c+32 (the two key halves of one query) with the
@@ -261,8 +261,9 @@ __device__ __forceinline__ void attend_item(WaveState<BLK>& ws, const uint8_t* k
   }
 }
 
-// blockIdx -> (query block I, request r) in descending-I order over the ragged
-// batch, plus (kv head, sub-tile).
+// blockIdx -> (key block I of a query block, request r) in descending-I order
+// over the ragged batch, plus (kv head, sub-tile). Request r's query blocks
+// are its key blocks qb0 .. NBk - 1 (all of them in a whole prefill).
 __device__ __forceinline__ void decode_work(const AttnParams& p, int& I, int& r, int& h, int& sub) {
   const ReqTable& rt = p.rt;
   const int U = p.Hkv * p.subs;
@@ -273,7 +274,8 @@ __device__ __forceinline__ void decode_work(const AttnParams& p, int& I, int& r,
   // C(x) = number of (r, I') with I' > x; non-increasing. Smallest I with C(I) <= pk.
   auto C = [&](int x) {
     int s = 0;
-    for (int q = 0; q < rt.R; ++q) s += max(0, rt.blk_off[q + 1] - rt.blk_off[q] - 1 - x);
+    for (int q = 0; q < rt.R; ++q)
+      s += max(0, rt.kblk_off[q + 1] - rt.kblk_off[q] - 1 - max(x, rt.qb0[q] - 1));
     return s;
   };
   int lo = 0, hi = rt.nb_max - 1;
@@ -286,7 +288,7 @@ __device__ __forceinline__ void decode_work(const AttnParams& p, int& I, int& r,
   int j = pk - C(I);
   r = 0;
   for (int q = 0; q < rt.R; ++q) {
-    if (rt.blk_off[q + 1] - rt.blk_off[q] > I) {
+    if (rt.qb0[q] <= I && rt.kblk_off[q + 1] - rt.kblk_off[q] > I) {
       if (j == 0) { r = q; break; }
       --j;
     }
@@ -552,16 +554,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   int sub;
   decode_work(p, rc.I, rc.r, rc.h, sub);
   const ReqTable& rt = p.rt;
-  rc.tok_base = rt.tok_off[rc.r];
-  rc.L = rt.tok_off[rc.r + 1] - rt.tok_off[rc.r];
+  rc.tok_base = rt.ktok_off[rc.r];
+  rc.L = rt.ktok_off[rc.r + 1] - rt.ktok_off[rc.r];
   const int I = rc.I;
+  const int qi = I - rt.qb0[rc.r];  // query block of the call
   const int nI = min(BLK, rc.L - I * BLK);
-  const int64_t row = (int64_t)rc.h * p.NB_tot + rt.blk_off[rc.r] + I;
+  const int64_t row = (int64_t)rc.h * p.NBq_tot + rt.blk_off[rc.r] + qi;
   rc.n_exact = p.dense ? I + 1 : p.row_ptr[row + 1] - p.row_ptr[row];
   rc.cols = p.dense ? nullptr : p.col_idx + p.row_ptr[row];
   const bool do_corr = p.mean_correction && !p.dense && I > 0;
   rc.n_items = rc.n_exact + (do_corr ? (I + kPC - 1) / kPC : 0);
-  rc.pooled_row0 = (int64_t)rc.h * p.NB_tot + rt.blk_off[rc.r];
+  rc.pooled_row0 = (int64_t)rc.h * p.NBk_tot + rt.kblk_off[rc.r];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -573,7 +576,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   const int tq0 = prow0 % BLK;
   const int tq = tq0 + c;
   const bool q_valid = wave_active && tq < nI;
-  const int64_t tok = rc.tok_base + (int64_t)I * BLK + tq;
+  const int64_t tok = rt.tok_off[rc.r] + (int64_t)qi * BLK + tq;  // query token
   // K operand: row c of a 32-row tile, chunk hf (then + 128 bytes per 16 dims).
   const int lk = (c >> 2) * kQuad + (c & 3) * 16 + hf * 64;
   // V^T operand: lane j of 16-lane group gq reads dims 16(gq&1) + 4(j&3)..+3 of
@@ -709,14 +712,14 @@ void launch_attn_t(const AttnParams& p, dim3 grid, hipStream_t stream) {
 int attn_rows_per_wg() { return kRowsPerWG; }
 
 hipError_t launch_attn(const AttnParams& p, hipStream_t stream) {
-  const int64_t n_pool8 = p.kbar16 ? (int64_t)p.Hkv * p.NB_tot * kHeadDim / 8 : 0;
+  const int64_t n_pool8 = p.kbar16 ? (int64_t)p.Hkv * p.NBk_tot * kHeadDim / 8 : 0;
   const int64_t n_kv8 = p.fp8 ? p.kv_elems / 8 : 0;
   if (n_pool8 + n_kv8 > 0) {
     const int64_t work = 2 * n_pool8 + 2 * n_kv8;
     const int blocks = (int)(work < 8192 * 256 ? (work + 255) / 256 : 8192);
     hipLaunchKernelGGL(prep_kernel, dim3(blocks), dim3(256), 0, stream, p, n_pool8, n_kv8);
   }
-  const int64_t wgs = (int64_t)p.Hkv * p.NB_tot * p.subs;
+  const int64_t wgs = (int64_t)p.Hkv * p.NBq_tot * p.subs;
   dim3 grid((unsigned)wgs);
   if (p.B == 128) launch_attn_t<128>(p, grid, stream);
   else launch_attn_t<64>(p, grid, stream);

@@ -22,12 +22,18 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Ragged batch description, passed by value as a kernel argument. Built on the
-// host from the host-side cu_seqlens, so no device lookup table is needed.
+// host from the host-side cu_seqlens / cu_seqlens_k, so no device lookup table
+// is needed. Request r has Lk keys (positions 0 .. Lk-1) and its last Lq
+// positions as queries; qb0 = (Lk - Lq) / B is the key block of its first
+// query block (0 for a whole prefill).
 struct ReqTable {
   int32_t R;                         // requests
-  int32_t nb_max;                    // max_r NB_r
-  int32_t tok_off[kMaxSeqs + 1];     // cu_seqlens
-  int32_t blk_off[kMaxSeqs + 1];     // prefix sums of NB_r
+  int32_t nb_max;                    // max_r NBk_r
+  int32_t tok_off[kMaxSeqs + 1];     // query tokens: cu_seqlens
+  int32_t ktok_off[kMaxSeqs + 1];    // key tokens: cu_seqlens_k
+  int32_t blk_off[kMaxSeqs + 1];     // prefix sums of NBq_r (q_bar and CSR rows)
+  int32_t kblk_off[kMaxSeqs + 1];    // prefix sums of NBk_r (k_bar and v_bar rows)
+  int32_t qb0[kMaxSeqs];             // first query block's key-block id
 };
 
 // K/V addressing: contiguous [T, Hkv, d] or paged [pages, page_size, Hkv, d].
@@ -38,7 +44,7 @@ struct KVAddr {
   int32_t paged;
 };
 
-// Element offset of (request r, request-local token t, kv head h, dim 0).
+// Element offset of (request r, key position t, kv head h, dim 0).
 __device__ __forceinline__ int64_t kv_elem_offset(const KVAddr& a, const ReqTable& rt, int r, int t, int h,
                                                   int Hkv) {
   int64_t row;
@@ -46,7 +52,7 @@ __device__ __forceinline__ int64_t kv_elem_offset(const KVAddr& a, const ReqTabl
     const int page = a.page_table[(int64_t)r * a.max_pages + t / a.page_size];
     row = (int64_t)page * a.page_size + (t % a.page_size);
   } else {
-    row = (int64_t)rt.tok_off[r] + t;
+    row = (int64_t)rt.ktok_off[r] + t;
   }
   return (row * Hkv + h) * kHeadDim;
 }

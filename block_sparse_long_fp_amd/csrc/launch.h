@@ -19,7 +19,7 @@ struct PoolParams {
   const float* descale_q;
   const float* descale_k;
   const float* descale_v;
-  int32_t Hq, Hkv, G, B, NB_tot, fp8;
+  int32_t Hq, Hkv, G, B, NBq_tot, NBk_tot, fp8;
   KVAddr kv;
   ReqTable rt;
 };
@@ -32,13 +32,13 @@ struct SelectParams {
   float* zbuf;        // workspace: Hkv * pairs_tot floats
   float* rowmax;      // workspace: rows floats
   int32_t* counts;    // workspace: rows ints
-  int64_t pairs_tot;  // sum_r NB_r (NB_r + 1) / 2
+  int64_t pairs_tot;  // causal (query block, key block) pairs per KV head
   float sel_scale;
   float log_alpha;    // ln(alpha), fp32
   int32_t all_keep;   // alpha <= 0
   int32_t min_sparse_len;
   int32_t sink, window, last_n;  // forced keeps, in blocks
-  int32_t Hkv, NB_tot, B;
+  int32_t Hkv, NBq_tot, NBk_tot, B;
   ReqTable rt;
 };
 
@@ -61,7 +61,7 @@ struct AttnParams {
   const float* descale_k;
   const float* descale_v;
   float sm_scale;
-  int32_t Hq, Hkv, G, B, NB_tot, T;
+  int32_t Hq, Hkv, G, B, NBq_tot, NBk_tot, T;  // T: query tokens
   int32_t mean_correction;
   int32_t dense;        // 1: ignore the CSR, attend to every causal block
   int32_t subs;         // workgroups per (h, I) row: ceil(G * B / rows_per_wg)

@@ -5,7 +5,7 @@
 // queries and pools block-mean statistics) and Figure 4 (a pruned block is
 // represented by its mean key and mean value).
 //
-// Work split: one workgroup per (block b of the ragged batch, KV head h). Its
+// Work split: one workgroup per (key block b of the ragged batch, KV head h). Its
 // threads own "slots" (the G query heads of the group, then K, then V) times
 // 16-byte column chunks of the 128-wide head dim, and split the block's tokens
 // into interleaved groups; every load is a 16-byte (bf16) or 8-byte (fp8)
@@ -13,6 +13,10 @@
 // row, so each wave streams whole 128-byte lines. Partial sums meet in LDS in
 // a fixed order (deterministic), are divided by the element count and written
 // as fp32. The kernel is HBM-bound: it reads every input byte once.
+//
+// In chunked prefill a request's queries are its last positions; key blocks
+// before the chunk (J < qb0) pool K and V only, and key block J >= qb0 also
+// pools query block J - qb0 (the same positions, so the same token count).
 #include "common.h"
 #include "launch.h"
 
@@ -43,16 +47,19 @@ __device__ __forceinline__ void load_chunk(const void* base, int64_t elem, float
 template <bool FP8>
 __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolParams p) {
   extern __shared__ float part[];  // [groups][slots*kChunks][8]
-  const int b = blockIdx.x;        // global block id in [0, NB_tot)
+  const int b = blockIdx.x;        // global key block id in [0, NBk_tot)
   const int h = blockIdx.y;
   const ReqTable& rt = p.rt;
-  // request of this block: last r with blk_off[r] <= b
+  // request of this block: last r with kblk_off[r] <= b
   int r = 0;
-  while (r + 1 < rt.R && rt.blk_off[r + 1] <= b) ++r;
-  const int J = b - rt.blk_off[r];
-  const int L = rt.tok_off[r + 1] - rt.tok_off[r];
+  while (r + 1 < rt.R && rt.kblk_off[r + 1] <= b) ++r;
+  const int J = b - rt.kblk_off[r];
+  const int L = rt.ktok_off[r + 1] - rt.ktok_off[r];
   const int t0 = J * p.B;
   const int n = min(p.B, L - t0);
+  const int qi = J - rt.qb0[r];    // query block of the call at these positions
+  const bool has_q = qi >= 0;
+  const int64_t qtok0 = (int64_t)rt.tok_off[r] + (int64_t)qi * p.B;
 
   const int G = p.G;
   const int slots = G + 2;
@@ -70,8 +77,8 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolParams p) {
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
     if (slot < G) {
       const int g = h * G + slot;
-      for (int t = grp; t < n; t += groups) {
-        const int64_t e = ((int64_t)(rt.tok_off[r] + t0 + t) * p.Hq + g) * kHeadDim + chunk * 8;
+      for (int t = grp; has_q && t < n; t += groups) {
+        const int64_t e = ((qtok0 + t) * p.Hq + g) * kHeadDim + chunk * 8;
         float x[8];
         load_chunk<FP8>(p.q, e, x);
 #pragma unroll
@@ -94,7 +101,7 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolParams p) {
   __syncthreads();
 
   // Reduce: one thread per (output kind, chunk): kind 0 = q_bar, 1 = k_bar, 2 = v_bar.
-  if (tid < 3 * kChunks) {
+  if (tid < 3 * kChunks && (has_q || tid >= kChunks)) {
     const int kind = tid / kChunks;
     const int c = tid % kChunks;
     float s[8];
@@ -118,7 +125,8 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolParams p) {
       if (FP8) scale *= (kind == 1) ? *p.descale_k : *p.descale_v;
     }
     float* out = (kind == 0) ? p.q_bar : (kind == 1 ? p.k_bar : p.v_bar);
-    float4* o4 = reinterpret_cast<float4*>(out + ((int64_t)h * p.NB_tot + b) * kHeadDim + c * 8);
+    const int64_t orow = kind == 0 ? (int64_t)h * p.NBq_tot + rt.blk_off[r] + qi : (int64_t)h * p.NBk_tot + b;
+    float4* o4 = reinterpret_cast<float4*>(out + orow * kHeadDim + c * 8);
     o4[0] = make_float4(s[0] * scale, s[1] * scale, s[2] * scale, s[3] * scale);
     o4[1] = make_float4(s[4] * scale, s[5] * scale, s[6] * scale, s[7] * scale);
   }
@@ -133,7 +141,7 @@ size_t pool_lds_bytes(int G) {
 }
 
 hipError_t launch_pool(const PoolParams& p, hipStream_t stream) {
-  dim3 grid(p.NB_tot, p.Hkv);
+  dim3 grid(p.NBk_tot, p.Hkv);
   const size_t lds = pool_lds_bytes(p.G);
   if (p.fp8)
     hipLaunchKernelGGL(pool_kernel<true>, grid, dim3(kPoolThreads), lds, stream, p);

@@ -8,7 +8,9 @@
 // "A serving setup you can actually test", names the threshold and the minimum
 // sparse query length knobs.
 //
-// Row (h, I) of request r scores every causal key block J <= I with
+// Row (h, i) of request r is query block i of the call, at key block
+// I = qb0 + i of the request (qb0 > 0 in chunked prefill). It scores every
+// causal key block J <= I with
 // z_J = tau * q_bar[h,I] . k_bar[h,J] (fp32), takes the row max m, and keeps J
 // iff z_J - m >= ln(alpha) (the same as exp(z_J - m) >= alpha), plus the
 // forced blocks (the diagonal, and optionally sink / window / last-n rows).
@@ -36,20 +38,26 @@ constexpr int kTileJ = 32;       // key blocks per LDS chunk
 constexpr int kScoreThreads = 256;
 constexpr int kPad = kHeadDim + 4;
 
+// Scores of request r start at pair_offset(r) in a KV head's z slab; row i of
+// the request starts i * qb0 + i (i + 1) / 2 later (row i has qb0 + i + 1).
 __device__ __forceinline__ int64_t pair_offset(const ReqTable& rt, int r) {
   int64_t s = 0;
-  for (int i = 0; i < r; ++i) {
-    const int64_t nb = rt.blk_off[i + 1] - rt.blk_off[i];
-    s += nb * (nb + 1) / 2;
+  for (int q = 0; q < r; ++q) {
+    const int64_t nb = rt.blk_off[q + 1] - rt.blk_off[q];
+    s += nb * rt.qb0[q] + nb * (nb + 1) / 2;
   }
   return s;
 }
 
+__device__ __forceinline__ int64_t row_pair_offset(int i, int qb0) {
+  return (int64_t)i * qb0 + (int64_t)i * (i + 1) / 2;
+}
+
 // Blocks kept whatever their score: the diagonal, the attention sink (the
 // first p.sink blocks), the local window (p.window blocks left of the
-// diagonal) and every causal block of the request's last p.last_n query
-// blocks ([article] --flashprefill-attention-sink, --flashprefill-window,
-// --flashprefill-last-n-blocks; counts in blocks).
+// diagonal) and every causal block of the last p.last_n blocks of the
+// sequence so far, NB = NBk ([article] --flashprefill-attention-sink,
+// --flashprefill-window, --flashprefill-last-n-blocks; counts in blocks).
 __device__ __forceinline__ bool forced_keep(const SelectParams& p, int I, int J, int NB) {
   return J == I || J < p.sink || J >= I - p.window || I >= NB - p.last_n;
 }
@@ -73,15 +81,18 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(SelectParams p) {
     tile -= nt;
     ++r;
   }
-  const int NB = rt.blk_off[r + 1] - rt.blk_off[r];
-  const int I0 = tile * kTileI;
-  if (I0 >= NB) return;
+  const int NBq = rt.blk_off[r + 1] - rt.blk_off[r];
+  const int NB = rt.kblk_off[r + 1] - rt.kblk_off[r];
+  const int qb0 = rt.qb0[r];
+  const int i0 = tile * kTileI;
+  if (i0 >= NBq) return;
   const int tid = threadIdx.x;
   const int ti = tid >> 3;   // row within the tile
   const int jq = tid & 7;    // column phase
-  const int I = I0 + ti;
-  const bool row_ok = I < NB;
-  const int64_t row = (int64_t)h * p.NB_tot + rt.blk_off[r] + I;
+  const int i = i0 + ti;
+  const int I = qb0 + i;     // key block of the row's queries
+  const bool row_ok = i < NBq;
+  const int64_t row = (int64_t)h * p.NBq_tot + rt.blk_off[r] + i;
 
   if (request_dense(p, r)) {
     if (jq == 0 && row_ok) p.counts[row] = I + 1;
@@ -92,18 +103,18 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(SelectParams p) {
   for (int e = tid; e < kTileI * (kHeadDim / 4); e += kScoreThreads) {
     const int rr = e / (kHeadDim / 4), c4 = e % (kHeadDim / 4);
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (I0 + rr < NB) v = reinterpret_cast<const float4*>(p.q_bar + ((int64_t)h * p.NB_tot + rt.blk_off[r] + I0 + rr) * kHeadDim)[c4];
+    if (i0 + rr < NBq) v = reinterpret_cast<const float4*>(p.q_bar + ((int64_t)h * p.NBq_tot + rt.blk_off[r] + i0 + rr) * kHeadDim)[c4];
     *reinterpret_cast<float4*>(&qs[rr][c4 * 4]) = v;
   }
-  float* zrow = p.zbuf + (int64_t)h * p.pairs_tot + pair_offset(rt, r) + (int64_t)I * (I + 1) / 2;
-  const int Jend = min(NB, I0 + kTileI);  // exclusive bound of columns any row needs
+  float* zrow = p.zbuf + (int64_t)h * p.pairs_tot + pair_offset(rt, r) + row_pair_offset(i, qb0);
+  const int Jend = min(NB, qb0 + i0 + kTileI);  // exclusive bound of columns any row needs
   float m = -INFINITY;
   for (int J0 = 0; J0 < Jend; J0 += kTileJ) {
     __syncthreads();
     for (int e = tid; e < kTileJ * (kHeadDim / 4); e += kScoreThreads) {
       const int rr = e / (kHeadDim / 4), c4 = e % (kHeadDim / 4);
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (J0 + rr < NB) v = reinterpret_cast<const float4*>(p.k_bar + ((int64_t)h * p.NB_tot + rt.blk_off[r] + J0 + rr) * kHeadDim)[c4];
+      if (J0 + rr < NB) v = reinterpret_cast<const float4*>(p.k_bar + ((int64_t)h * p.NBk_tot + rt.kblk_off[r] + J0 + rr) * kHeadDim)[c4];
       *reinterpret_cast<float4*>(&ks[rr][c4 * 4]) = v;
     }
     __syncthreads();
@@ -187,20 +198,21 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(SelectParams p
   const ReqTable& rt = p.rt;
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * (kCompactThreads / 64) + (threadIdx.x >> 6);
-  const int64_t rows = (int64_t)p.Hkv * p.NB_tot;
+  const int64_t rows = (int64_t)p.Hkv * p.NBq_tot;
   if (row >= rows) return;
-  const int h = (int)(row / p.NB_tot);
-  const int b = (int)(row % p.NB_tot);
+  const int h = (int)(row / p.NBq_tot);
+  const int b = (int)(row % p.NBq_tot);
   int r = 0;
   while (r + 1 < rt.R && rt.blk_off[r + 1] <= b) ++r;
-  const int I = b - rt.blk_off[r];
-  const int NB = rt.blk_off[r + 1] - rt.blk_off[r];
+  const int i = b - rt.blk_off[r];
+  const int I = rt.qb0[r] + i;
+  const int NB = rt.kblk_off[r + 1] - rt.kblk_off[r];
   int32_t* out = p.col_idx + p.row_ptr[row];
   if (request_dense(p, r)) {
     for (int J = lane; J <= I; J += 64) out[J] = J;
     return;
   }
-  const float* zrow = p.zbuf + (int64_t)h * p.pairs_tot + pair_offset(rt, r) + (int64_t)I * (I + 1) / 2;
+  const float* zrow = p.zbuf + (int64_t)h * p.pairs_tot + pair_offset(rt, r) + row_pair_offset(i, rt.qb0[r]);
   const float m = p.rowmax[row];
   int base = 0;
   for (int J0 = 0; J0 <= I; J0 += 64) {
@@ -224,7 +236,7 @@ hipError_t launch_select(const SelectParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(score_kernel, dim3(tiles, p.Hkv), dim3(kScoreThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t rows = (int64_t)p.Hkv * p.NB_tot;
+  const int64_t rows = (int64_t)p.Hkv * p.NBq_tot;
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, p.counts, p.row_ptr, rows);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

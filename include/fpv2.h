@@ -4,8 +4,9 @@
  *
  * The method is FlashPrefill V2 as described in "FlashPrefill V2: Block-Sparse
  * Prefill Attention for Long-Context LLM Serving" (paper digest on
- * metallab.ai; cited below as [digest]) and in the nestfrontier.com article
- * "128K context now demands Hopper hardware" (cited as [article]).
+ * metallab.ai; cited below as [digest]), in the nestfrontier.com article
+ * "128K context now demands Hopper hardware" (cited as [article]) and in the
+ * ResearchPod episode on FlashPrefill V2 (researchpod.app; [podcast]).
  *
  * The prefill runs as three calls, in order, on one HIP stream:
  *   1. fp_pool_blocks     block-mean statistics of Q (GQA-packed), K and V
@@ -32,26 +33,38 @@
  *            anything; on failure it returns a non-zero fp_status, enqueues no
  *            work and writes no output. fp_last_error() then holds a message
  *            (per calling thread). A failed kernel launch returns FP_ERR_HIP.
- * Layouts:   T = total tokens over the ragged batch, Hq / Hkv query / KV
- *            heads, G = Hq / Hkv, d = head_dim (128), B = block_size.
- *            Request r holds tokens [cu_seqlens[r], cu_seqlens[r+1]); its
- *            blocks restart at its token 0: block J covers request-local
- *            tokens [J*B, min((J+1)*B, L_r)), NB_r = ceil(L_r / B).
- *            NB_tot = sum_r NB_r; blk_off[r] = sum_{r'<r} NB_r'.
- *            Q, O:          [T, Hq, d] row-major; query head g uses KV head g / G.
- *            K, V contiguous: [T, Hkv, d].
- *            K, V paged:    [num_pages, page_size, Hkv, d]; token t of request r
+ * Layouts:   Hq / Hkv query / KV heads, G = Hq / Hkv, d = head_dim (128),
+ *            B = block_size.
+ *            Request r has Lk_r keys (its sequence so far) and Lq_r <= Lk_r
+ *            queries, which are its LAST Lq_r tokens: query t (0-based in the
+ *            call) sits at sequence position off_r + t, off_r = Lk_r - Lq_r,
+ *            and attends to keys 0 .. off_r + t. Lq_r comes from cu_seqlens,
+ *            Lk_r from cu_seqlens_k (NULL: Lk_r = Lq_r, a whole prefill).
+ *            off_r > 0 is chunked prefill ([digest] Table 6: serving with 8K and
+ *            16K prefill chunks; [podcast]: block scoring runs once per chunk);
+ *            off_r must be a multiple of B, so the chunk's query blocks
+ *            coincide with key blocks.
+ *            Blocks restart at each request's token 0: key block J covers
+ *            positions [J*B, min((J+1)*B, Lk_r)), NBk_r = ceil(Lk_r / B); query
+ *            block i of the call is key block I = off_r / B + i, i < NBq_r =
+ *            ceil(Lq_r / B). Tq = sum_r Lq_r, Tk = sum_r Lk_r; blk_off[r] =
+ *            sum_{r'<r} NBq_r', kblk_off[r] = sum_{r'<r} NBk_r', NBq_tot and
+ *            NBk_tot the totals.
+ *            Q, O:          [Tq, Hq, d] row-major; query head g uses KV head g / G.
+ *            K, V contiguous: [Tk, Hkv, d], request r at rows cu_seqlens_k[r] ..
+ *            K, V paged:    [num_pages, page_size, Hkv, d]; position t of request r
  *                           is slot t % page_size of page
  *                           page_table[r * max_pages_per_seq + t / page_size]
  *                           ([digest] "What they did", Fix 3; Table 7: paged KV,
  *                           arbitrary page size).
- *            pooled q_bar, k_bar, v_bar: fp32 [Hkv, NB_tot, d], row
- *                           h * NB_tot + blk_off[r] + J.
- *            CSR:           one row per (h, r, I), row id h * NB_tot + blk_off[r] + I;
- *                           row_ptr int32 [Hkv * NB_tot + 1]; col_idx int32
- *                           request-local key-block ids, strictly ascending in a
- *                           row, the diagonal I always present.
- *            LSE:           fp32 [Hq, T], natural log of the full softmax
+ *            pooled q_bar:  fp32 [Hkv, NBq_tot, d], row h * NBq_tot + blk_off[r] + i.
+ *            pooled k_bar, v_bar: fp32 [Hkv, NBk_tot, d], row
+ *                           h * NBk_tot + kblk_off[r] + J.
+ *            CSR:           one row per (h, r, i), row id h * NBq_tot + blk_off[r] + i;
+ *                           row_ptr int32 [Hkv * NBq_tot + 1]; col_idx int32
+ *                           request-local key-block ids J <= I, strictly
+ *                           ascending in a row, the diagonal I always present.
+ *            LSE:           fp32 [Hq, Tq], natural log of the full softmax
  *                           denominator (exact terms plus surrogates).
  *            O:             bf16 for both input dtypes.
  */
@@ -65,7 +78,7 @@
 extern "C" {
 #endif
 
-#define FPV2_ABI_VERSION 3
+#define FPV2_ABI_VERSION 4
 
 /* Status codes. */
 typedef int32_t fp_status;
@@ -94,13 +107,13 @@ enum { FP_KV_CONTIGUOUS = 0, FP_KV_PAGED = 1 };
 
 /* Limits of this build. */
 #define FP_MAX_SEQS 128               /* requests per call                      */
-#define FP_MAX_BLOCKS_PER_SEQ 32768   /* NB_r; 4M tokens at B = 128             */
+#define FP_MAX_BLOCKS_PER_SEQ 32768   /* NBk_r; 4M tokens at B = 128            */
 #define FP_HEAD_DIM 128
 
 /* Problem description shared by all calls. */
 typedef struct fp_problem {
   int32_t num_seqs;              /* R, 1 .. FP_MAX_SEQS                           */
-  const int32_t* cu_seqlens;     /* HOST [R+1]; cu_seqlens[0] = 0, each L_r >= 1  */
+  const int32_t* cu_seqlens;     /* HOST [R+1] query offsets; [0] = 0, each Lq_r >= 1 */
   int32_t num_q_heads;           /* Hq >= 1                                        */
   int32_t num_kv_heads;          /* Hkv >= 1, Hq % Hkv == 0                        */
   int32_t head_dim;              /* d, must be 128                                 */
@@ -112,8 +125,10 @@ typedef struct fp_problem {
   int32_t kv_layout;             /* FP_KV_CONTIGUOUS or FP_KV_PAGED                */
   const int32_t* page_table;     /* DEVICE int32 [R, max_pages_per_seq] (paged)    */
   int32_t page_size;             /* tokens per page, >= 1 (paged)                  */
-  int32_t max_pages_per_seq;     /* row pitch of page_table, >= ceil(L_r/page_size) */
+  int32_t max_pages_per_seq;     /* row pitch of page_table, >= ceil(Lk_r/page_size) */
   int32_t num_pages;             /* pages in each of the K and V pools (paged)     */
+  const int32_t* cu_seqlens_k;   /* HOST [R+1] key offsets, or NULL (= cu_seqlens);  */
+                                 /* Lk_r >= Lq_r and (Lk_r - Lq_r) % B == 0          */
 } fp_problem;
 
 /* Block selection ([digest] abstract: max-based dynamic thresholding;
@@ -123,11 +138,12 @@ typedef struct fp_problem {
  * diagonal J = I always, and ([article] flags --flashprefill-attention-sink,
  * --flashprefill-window, --flashprefill-last-n-blocks; all counted in blocks,
  * 0 = off) J < sink_blocks, J >= I - window_blocks, and every J <= I when I is
- * one of the request's last last_n_blocks query blocks. */
+ * one of the last last_n_blocks blocks of the sequence so far (I >= NBk_r -
+ * last_n_blocks; in chunked prefill, the chunk's last blocks). */
 typedef struct fp_select_args {
   float alpha;                   /* threshold; alpha <= 0 keeps every causal block */
   float sel_scale;               /* score temperature tau, finite                  */
-  int32_t min_sparse_len;        /* requests with L_r < this keep every causal block */
+  int32_t min_sparse_len;        /* requests with Lq_r < this keep every causal block */
   int32_t sink_blocks;           /* >= 0 */
   int32_t window_blocks;         /* >= 0 */
   int32_t last_n_blocks;         /* >= 0 */
@@ -143,10 +159,12 @@ typedef struct fp_attn_args {
 
 /* Host-only queries (no GPU needed). */
 
-/* Sizes of the index: rows = Hkv * NB_tot, max_nnz = Hkv * sum_r NB_r(NB_r+1)/2
- * (every causal pair), num_blocks = NB_tot. Any output pointer may be NULL. */
+/* Sizes of the index and of the pooled statistics: rows = Hkv * NBq_tot,
+ * max_nnz = Hkv * sum_r sum_{i < NBq_r} (off_r / B + i + 1) (every causal pair),
+ * num_q_blocks = NBq_tot (rows of q_bar per head), num_k_blocks = NBk_tot (rows
+ * of k_bar and v_bar per head). Any output pointer may be NULL. */
 fp_status fp_index_shape(const fp_problem* p, int64_t* num_rows, int64_t* max_nnz,
-                         int64_t* num_blocks);
+                         int64_t* num_q_blocks, int64_t* num_k_blocks);
 
 /* Bytes of DEVICE workspace fp_select_blocks needs for this problem. */
 fp_status fp_select_workspace_bytes(const fp_problem* p, size_t* bytes);
@@ -163,11 +181,13 @@ fp_status fp_validate(const fp_problem* p, const fp_select_args* sel, const fp_a
 
 /* Stage 1a: pooled statistics ([digest] Figure 3: PackGQA packing and
  * block-mean pooling; Figure 4: mean key/value of a block).
- *   q_bar[h, b] = mean over the G heads of group h and the n_J tokens of block b,
- *   k_bar[h, b], v_bar[h, b] = mean over the n_J tokens of block b,
- * each as dequantised values for FP8, accumulated in fp32.
- * q, k, v: DEVICE inputs in the layouts above (k, v are the page pools when
- * paged). q_bar, k_bar, v_bar: DEVICE fp32 [Hkv, NB_tot, d] outputs. */
+ *   q_bar[h, i] = mean over the G heads of group h and the n tokens of query block i,
+ *   k_bar[h, J], v_bar[h, J] = mean over the n_J positions of key block J,
+ * each as dequantised values for FP8, accumulated in fp32. Every key block of
+ * the sequence so far is pooled (in chunked prefill the earlier chunks' blocks
+ * too). q, k, v: DEVICE inputs in the layouts above (k, v are the page pools
+ * when paged). q_bar: DEVICE fp32 [Hkv, NBq_tot, d] output; k_bar, v_bar:
+ * DEVICE fp32 [Hkv, NBk_tot, d] outputs. */
 fp_status fp_pool_blocks(const fp_problem* p, const void* q, const void* k, const void* v,
                          float* q_bar, float* k_bar, float* v_bar, void* stream);
 
@@ -190,7 +210,7 @@ fp_status fp_select_blocks(const fp_problem* p, const fp_select_args* sel, const
  * k_bar, v_bar: DEVICE fp32 from fp_pool_blocks (read only when
  * mean_correction = 1). row_ptr, col_idx: DEVICE CSR from fp_select_blocks
  * (or any CSR of the same shape with the diagonal in every row).
- * out: DEVICE bf16 [T, Hq, d]. lse: DEVICE fp32 [Hq, T], or NULL to skip.
+ * out: DEVICE bf16 [Tq, Hq, d]. lse: DEVICE fp32 [Hq, Tq], or NULL to skip.
  * workspace: DEVICE scratch of at least fp_attn_workspace_bytes(p, 1) bytes
  * (may be NULL when that is 0); contents on entry do not matter, garbage on
  * exit; the call must not overlap another call using the same workspace. */
@@ -199,7 +219,7 @@ fp_status fp_sparse_prefill(const fp_problem* p, const fp_attn_args* attn, const
                             const int32_t* row_ptr, const int32_t* col_idx, void* out, float* lse,
                             void* workspace, size_t workspace_bytes, void* stream);
 
-/* Dense causal attention over every key j <= i of the request (the comparator
+/* Dense causal attention over every key at or before each query (the comparator
  * for the sparse path; mean_correction is ignored). Same layouts as above;
  * workspace as above with fp_attn_workspace_bytes(p, 0). */
 fp_status fp_dense_prefill(const fp_problem* p, const fp_attn_args* attn, const void* q,

@@ -12,10 +12,14 @@ Sources (the pages this method is described on):
   [podcast] ResearchPod episode on FlashPrefill V2, researchpod.app (the
             block pre-scan with a simple average).
 
-What is computed, per request of L tokens (queries = keys = the L tokens):
+What is computed, per request of Lk key positions whose queries are the last
+Lq <= Lk positions (Lq = Lk for a whole prefill; Lq < Lk is one chunk of a
+chunked prefill, [digest] Table 6 and [podcast]: selection runs per chunk):
 
-1. Blocking: NB = ceil(L / B) blocks; block J holds tokens
-   [J*B, min((J+1)*B, L)), n_J of them.
+1. Blocking: NB = ceil(Lk / B) blocks; block J holds positions
+   [J*B, min((J+1)*B, Lk)), n_J of them. The chunk starts at a block
+   boundary, off = Lk - Lq = qb0 * B, so query block i of the chunk is block
+   I = qb0 + i.
 2. Pooling ([digest] Fig. 3 "pools block-mean statistics", Fig. 4 (k_J, v_J)
    means): kbar[h,J], vbar[h,J] = mean of K, V over block J; the grouped
    query heads of KV head h are packed ([digest] Fig. 3 PackGQA) and pooled
@@ -24,10 +28,10 @@ What is computed, per request of L tokens (queries = keys = the L tokens):
    threshold flag: a higher threshold keeps fewer blocks):
    z_J = tau * qbar[h,I] . kbar[h,J] for J <= I, m = max_J z_J, keep J iff
    exp(z_J - m) >= alpha; the diagonal block I is always kept. alpha <= 0,
-   or a request shorter than the minimum sparse length, keeps every causal
-   block. tau (``sel_scale``) defaults to 1.
+   or a request with fewer queries than the minimum sparse length, keeps
+   every causal block. tau (``sel_scale``) defaults to 1.
 4. Exact stream ([digest] Fig. 3 "exact path"): s_ij = sm * q_i . k_j for every
-   token j <= i of a selected block.
+   position j <= pos(i) of a selected block.
 5. Mean correction ([digest] Fig. 4): every pruned causal block J < I adds one
    surrogate logit sigma_iJ = sm * q_i . kbar_J + ln n_J with value vbar_J,
    i.e. |B_J| exp(sm q_i . kbar_J) on (vbar_J, 1) in numerator and denominator.
@@ -99,51 +103,59 @@ def forced_keep(I: int, NB: int, sink: int = 0, window: int = 0, last_n: int = 0
 
 def select_blocks(qbar: np.ndarray, kbar: np.ndarray, alpha: float, sel_scale: float = 1.0,
                   dense: bool = False, band_rel: float = 1e-4, sink: int = 0, window: int = 0,
-                  last_n: int = 0):
-    """Step 3: per (h, I) the ascending list of kept key blocks.
+                  last_n: int = 0, q_block0: int = 0):
+    """Step 3: per (h, i) the ascending list of kept key blocks of query block
+    i, which sits at key block I = q_block0 + i (q_block0 > 0 for a chunk).
 
     [digest] abstract and Table 9 (alpha, "max-based dynamic thresholding");
     the diagonal is always kept, and so are the forced blocks of
-    ``forced_keep`` (all off by default). Returns (sets, near): sets[h][I] is
-    an int64 array; ``near`` lists (h, I, J) whose exp(z - m) lies within
-    band_rel * alpha of alpha and that no rule forces, the pairs a float32
-    implementation may decide either way.
+    ``forced_keep`` (all off by default; NB there is the key block count).
+    Returns (sets, near): sets[h][i] is an int64 array of key block ids;
+    ``near`` lists (h, i, J) whose exp(z - m) lies within band_rel * alpha of
+    alpha and that no rule forces, the pairs a float32 implementation may
+    decide either way.
     """
-    Hkv, NB, d = qbar.shape
+    Hkv, NBq, d = qbar.shape
+    NB = kbar.shape[1]
     sets: List[List[np.ndarray]] = []
     near: List[Tuple[int, int, int]] = []
     for h in range(Hkv):
         rows = []
-        for I in range(NB):
+        for i in range(NBq):
+            I = q_block0 + i
             if dense or alpha <= 0.0:
                 rows.append(np.arange(I + 1, dtype=np.int64))
                 continue
-            z = sel_scale * (kbar[h, :I + 1, :] @ qbar[h, I, :])   # [I+1]
+            z = sel_scale * (kbar[h, :I + 1, :] @ qbar[h, i, :])   # [I+1]
             m = z.max()
             ratio = np.exp(z - m)
             forced = forced_keep(I, NB, sink, window, last_n)
             keep = (ratio >= alpha) | forced
             rows.append(np.nonzero(keep)[0].astype(np.int64))
             close = (np.abs(ratio - alpha) <= band_rel * alpha) & ~forced
-            near.extend((h, I, int(J)) for J in np.nonzero(close)[0])
+            near.extend((h, i, int(J)) for J in np.nonzero(close)[0])
         sets.append(rows)
     return sets, near
 
 
 def attend_row(Q: np.ndarray, K: np.ndarray, V: np.ndarray, kbar: np.ndarray, vbar: np.ndarray,
-               sel: np.ndarray, h: int, I: int, B: int, G: int, sm_scale: float, mean_correction: bool):
-    """Steps 4-6 for one packed row tile (KV head h, query block I).
+               sel: np.ndarray, h: int, I: int, B: int, G: int, sm_scale: float, mean_correction: bool,
+               q_off: int = 0):
+    """Steps 4-6 for one packed row tile (KV head h, the queries at block I).
 
-    Returns (o [n_I, G, d], lse [n_I, G]) for query heads h*G .. h*G+G-1.
+    Q holds the queries at positions q_off .. q_off + len(Q) - 1; K, V hold
+    positions 0 .. Lk - 1. Returns (o [n_I, G, d], lse [n_I, G]) for query
+    heads h*G .. h*G+G-1.
     """
-    L = Q.shape[0]
-    qs, nI = I * B, min(B, L - I * B)
+    L = K.shape[0]
+    nI = min(B, L - I * B)
+    qs = I * B - q_off                                                # row in Q
     q = Q[qs:qs + nI, h * G:(h + 1) * G, :]                          # [nI, G, d]
-    # Exact stream over the tokens of the selected blocks (Fig. 3 exact path).
+    # Exact stream over the positions of the selected blocks (Fig. 3 exact path).
     pos = np.concatenate([np.arange(J * B, min((J + 1) * B, L)) for J in sel])
     k_sel, v_sel = K[pos, h, :], V[pos, h, :]                         # [m, d]
     s = sm_scale * np.einsum("tgd,jd->tgj", q, k_sel)                 # [nI, G, m]
-    qpos = np.arange(qs, qs + nI)
+    qpos = np.arange(I * B, I * B + nI)
     s = np.where(pos[None, None, :] <= qpos[:, None, None], s, -np.inf)
     logits, values = [s], [v_sel]
     # Correction stream: one surrogate per pruned causal block (Fig. 4).
@@ -165,51 +177,57 @@ def attend_row(Q: np.ndarray, K: np.ndarray, V: np.ndarray, kbar: np.ndarray, vb
 
 def attend(Q: np.ndarray, K: np.ndarray, V: np.ndarray, kbar: np.ndarray, vbar: np.ndarray,
            sets, B: int, G: int, sm_scale: float, mean_correction: bool = True,
-           rows: Optional[Sequence[Tuple[int, int]]] = None):
-    """Steps 4-6 for one request: O [L, Hq, d], LSE [Hq, L].
+           rows: Optional[Sequence[Tuple[int, int]]] = None, q_off: int = 0):
+    """Steps 4-6 for one request: O [Lq, Hq, d], LSE [Hq, Lq].
 
-    ``rows`` restricts the work to some (h, I) tiles; other outputs stay NaN.
+    Queries sit at positions q_off .. (q_off a multiple of B); sets[h][i]
+    belongs to query block i, key block q_off / B + i. ``rows`` restricts the
+    work to some (h, i) tiles; other outputs stay NaN.
     """
-    L, Hq, d = Q.shape
+    Lq, Hq, d = Q.shape
     Hkv = Hq // G
-    NB = -(-L // B)
-    O = np.full((L, Hq, d), np.nan)
-    LSE = np.full((Hq, L), np.nan)
-    todo = rows if rows is not None else [(h, I) for h in range(Hkv) for I in range(NB)]
-    for h, I in todo:
-        o, lse = attend_row(Q, K, V, kbar, vbar, np.asarray(sets[h][I]), h, I, B, G, sm_scale,
-                            mean_correction)
-        qs = I * B
+    NBq = -(-Lq // B)
+    qb0 = q_off // B
+    O = np.full((Lq, Hq, d), np.nan)
+    LSE = np.full((Hq, Lq), np.nan)
+    todo = rows if rows is not None else [(h, i) for h in range(Hkv) for i in range(NBq)]
+    for h, i in todo:
+        o, lse = attend_row(Q, K, V, kbar, vbar, np.asarray(sets[h][i]), h, qb0 + i, B, G, sm_scale,
+                            mean_correction, q_off)
+        qs = i * B
         O[qs:qs + o.shape[0], h * G:(h + 1) * G, :] = o
         LSE[h * G:(h + 1) * G, qs:qs + o.shape[0]] = lse.T
     return O, LSE
 
 
-def attend_loop(Q, K, V, kbar, vbar, sets, B: int, G: int, sm_scale: float, mean_correction: bool = True):
+def attend_loop(Q, K, V, kbar, vbar, sets, B: int, G: int, sm_scale: float, mean_correction: bool = True,
+                q_off: int = 0):
     """Second, independent coding of steps 4-6: one query token at a time.
 
     Walks keys one by one in plain Python (tiny shapes only) with a streaming
     max/sum, so it shares neither the vectorised layout nor the single-pass
-    softmax of ``attend``.
+    softmax of ``attend``. Query t sits at position q_off + t.
     """
-    L, Hq, d = Q.shape
-    O = np.zeros((L, Hq, d))
-    LSE = np.zeros((Hq, L))
+    Lq, Hq, d = Q.shape
+    L = K.shape[0]
+    O = np.zeros((Lq, Hq, d))
+    LSE = np.zeros((Hq, Lq))
     for g in range(Hq):
         h = g // G
-        for i in range(L):
+        for t in range(Lq):
+            i = q_off + t                     # position of the query
             I = i // B
-            chosen = set(int(J) for J in sets[h][I])
+            chosen = set(int(J) for J in sets[h][I - q_off // B])
             terms = []  # (logit, value vector)
             for J in sorted(chosen):
                 for j in range(J * B, min((J + 1) * B, L)):
                     if j <= i:
-                        terms.append((sm_scale * float(np.dot(Q[i, g], K[j, h])), V[j, h]))
+                        terms.append((sm_scale * float(np.dot(Q[t, g], K[j, h])), V[j, h]))
             if mean_correction:
                 for J in range(I):
                     if J not in chosen:
                         nJ = min(B, L - J * B)
-                        terms.append((sm_scale * float(np.dot(Q[i, g], kbar[h, J])) + math.log(nJ), vbar[h, J]))
+                        terms.append((sm_scale * float(np.dot(Q[t, g], kbar[h, J])) + math.log(nJ), vbar[h, J]))
             m = -math.inf
             ssum = 0.0
             acc = np.zeros(d)
@@ -222,8 +240,8 @@ def attend_loop(Q, K, V, kbar, vbar, sets, B: int, G: int, sm_scale: float, mean
                 e = math.exp(logit - m)
                 ssum += e
                 acc += e * val
-            O[i, g] = acc / ssum
-            LSE[g, i] = m + math.log(ssum)
+            O[t, g] = acc / ssum
+            LSE[g, t] = m + math.log(ssum)
     return O, LSE
 
 
@@ -256,30 +274,35 @@ def csr_from_sets(all_sets: List[List[List[np.ndarray]]], Hkv: int):
 
 @dataclasses.dataclass
 class OracleResult:
-    qbar: np.ndarray            # [Hkv, NB_tot, d]
-    kbar: np.ndarray
+    qbar: np.ndarray            # [Hkv, NBq_tot, d]
+    kbar: np.ndarray            # [Hkv, NBk_tot, d]
     vbar: np.ndarray
-    row_ptr: np.ndarray         # [Hkv*NB_tot + 1]
+    row_ptr: np.ndarray         # [Hkv*NBq_tot + 1]
     col_idx: np.ndarray
     near: List[Tuple[int, int]]  # (global row, J) pairs inside the threshold band
-    O: Optional[np.ndarray]     # [T, Hq, d]
-    LSE: Optional[np.ndarray]   # [Hq, T]
-    sets: list                  # sets[r][h][I]
-    blk_off: List[int]
+    O: Optional[np.ndarray]     # [Tq, Hq, d]
+    LSE: Optional[np.ndarray]   # [Hq, Tq]
+    sets: list                  # sets[r][h][i]
+    blk_off: List[int]          # query-block offsets (CSR rows, q_bar rows)
+    kblk_off: List[int] = None  # key-block offsets (k_bar, v_bar rows)
 
 
 def prefill(Q: np.ndarray, K: np.ndarray, V: np.ndarray, cu_seqlens: Sequence[int], num_kv_heads: int,
             B: int, alpha: float, sel_scale: float = 1.0, min_sparse_len: int = 0,
             sm_scale: Optional[float] = None, mean_correction: bool = True, do_attend: bool = True,
             rows: Optional[Sequence[int]] = None, K_pages=None, V_pages=None, page_table=None,
-            page_size: int = 0, sink: int = 0, window: int = 0, last_n: int = 0) -> OracleResult:
+            page_size: int = 0, sink: int = 0, window: int = 0, last_n: int = 0,
+            cu_seqlens_k: Optional[Sequence[int]] = None) -> OracleResult:
     """The whole path over a ragged batch ([digest] Fix 3: continuous batching).
 
-    Q [T, Hq, d] and (contiguous) K, V [T, Hkv, d] hold the dequantised fp64
-    values. With ``page_table`` given, K and V are instead read per request
-    through the page table from ``K_pages``/``V_pages``. Requests shorter than
+    Q [Tq, Hq, d] and (contiguous) K, V [Tk, Hkv, d] hold the dequantised fp64
+    values; ``cu_seqlens`` are the query offsets, ``cu_seqlens_k`` the key
+    offsets (None: the same, a whole prefill); request r's queries are its last
+    positions (a chunk, [digest] Table 6). With ``page_table`` given, K and V
+    are instead read per request through the page table from
+    ``K_pages``/``V_pages``. Requests with fewer queries than
     ``min_sparse_len`` run dense ([article] minimum sparse query length flag).
-    ``rows`` limits attention to some global CSR rows (h*NB_tot + blk_off[r] + I).
+    ``rows`` limits attention to some global CSR rows (h*NBq_tot + blk_off[r] + i).
     ``sink``, ``window``, ``last_n``: forced keeps per request (``forced_keep``).
     """
     T, Hq, d = Q.shape
@@ -287,13 +310,19 @@ def prefill(Q: np.ndarray, K: np.ndarray, V: np.ndarray, cu_seqlens: Sequence[in
     G = Hq // Hkv
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
+    cuk = list(cu_seqlens) if cu_seqlens_k is None else list(cu_seqlens_k)
     R = len(cu_seqlens) - 1
-    NBs = [-(-(cu_seqlens[r + 1] - cu_seqlens[r]) // B) for r in range(R)]
-    blk_off = [0]
-    for nb in NBs:
-        blk_off.append(blk_off[-1] + nb)
-    NBt = blk_off[-1]
-    qbar = np.zeros((Hkv, NBt, d)); kbar = np.zeros((Hkv, NBt, d)); vbar = np.zeros((Hkv, NBt, d))
+    Lqs = [cu_seqlens[r + 1] - cu_seqlens[r] for r in range(R)]
+    Lks = [cuk[r + 1] - cuk[r] for r in range(R)]
+    for r in range(R):
+        if Lks[r] < Lqs[r] or (Lks[r] - Lqs[r]) % B:
+            raise ValueError(f"request {r}: the chunk must end the sequence and start on a block boundary")
+    blk_off, kblk_off = [0], [0]
+    for r in range(R):
+        blk_off.append(blk_off[-1] + -(-Lqs[r] // B))
+        kblk_off.append(kblk_off[-1] + -(-Lks[r] // B))
+    NBt, NBk = blk_off[-1], kblk_off[-1]
+    qbar = np.zeros((Hkv, NBt, d)); kbar = np.zeros((Hkv, NBk, d)); vbar = np.zeros((Hkv, NBk, d))
     all_sets, near = [], []
     O = np.full((T, Hq, d), np.nan) if do_attend else None
     LSE = np.full((Hq, T), np.nan) if do_attend else None
@@ -306,25 +335,28 @@ def prefill(Q: np.ndarray, K: np.ndarray, V: np.ndarray, cu_seqlens: Sequence[in
             want.setdefault(r, []).append((h, rem - blk_off[r]))
     for r in range(R):
         s, e = cu_seqlens[r], cu_seqlens[r + 1]
-        L = e - s
+        Lk = Lks[r]
+        q_off = Lk - Lqs[r]
         q = Q[s:e]
         if page_table is not None:
-            k = gather_paged(K_pages, page_table[r], L, page_size)
-            v = gather_paged(V_pages, page_table[r], L, page_size)
+            k = gather_paged(K_pages, page_table[r], Lk, page_size)
+            v = gather_paged(V_pages, page_table[r], Lk, page_size)
         else:
-            k, v = K[s:e], V[s:e]
+            k, v = K[cuk[r]:cuk[r + 1]], V[cuk[r]:cuk[r + 1]]
         qb, kb, vb = pool_queries(q, B, G), pool_keys(k, B), pool_keys(v, B)
         a, b = blk_off[r], blk_off[r + 1]
-        qbar[:, a:b], kbar[:, a:b], vbar[:, a:b] = qb, kb, vb
-        dense = L < min_sparse_len
-        sets, nr = select_blocks(qb, kb, alpha, sel_scale, dense=dense, sink=sink, window=window, last_n=last_n)
+        qbar[:, a:b] = qb
+        kbar[:, kblk_off[r]:kblk_off[r + 1]], vbar[:, kblk_off[r]:kblk_off[r + 1]] = kb, vb
+        dense = Lqs[r] < min_sparse_len
+        sets, nr = select_blocks(qb, kb, alpha, sel_scale, dense=dense, sink=sink, window=window, last_n=last_n,
+                                 q_block0=q_off // B)
         all_sets.append(sets)
-        near.extend((h * NBt + a + I, J) for (h, I, J) in nr)
+        near.extend((h * NBt + a + i, J) for (h, i, J) in nr)
         if do_attend:
             rr = None if want is None else want.get(r, [])
             if rr is None or rr:
-                o, lse = attend(q, k, v, kb, vb, sets, B, G, sm_scale, mean_correction, rows=rr)
+                o, lse = attend(q, k, v, kb, vb, sets, B, G, sm_scale, mean_correction, rows=rr, q_off=q_off)
                 O[s:e] = o
                 LSE[:, s:e] = lse
     row_ptr, col_idx = csr_from_sets(all_sets, Hkv)
-    return OracleResult(qbar, kbar, vbar, row_ptr, col_idx, near, O, LSE, all_sets, blk_off)
+    return OracleResult(qbar, kbar, vbar, row_ptr, col_idx, near, O, LSE, all_sets, blk_off, kblk_off)

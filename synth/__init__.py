@@ -8,6 +8,7 @@ the two sides see the same bytes.
 from .generators import (  # noqa: F401
     CONFIGS,
     Workload,
+    chunk_of,
     make_workload,
     planted_prefill,
     fp8_e4m3_encode,

@@ -132,6 +132,9 @@ class Workload:
     page_table: Optional[torch.Tensor] = None
     page_size: int = 0
     planted: Optional[list] = None  # per request, per KV head: planted block ids
+    # chunked prefill (optional): key offsets [R+1]; q then holds only each
+    # request's last queries (a chunk), k / v every key position so far
+    cu_seqlens_k: Optional[List[int]] = None
 
     @property
     def dtype(self) -> str:
@@ -150,9 +153,17 @@ class Workload:
     def paged(self) -> bool:
         return self.page_table is not None
 
+    @property
+    def key_seqlens(self) -> List[int]:
+        c = self.cu_seqlens_k or self.cu_seqlens
+        return [c[i + 1] - c[i] for i in range(len(c) - 1)]
+
     def dense_equiv_flops(self) -> float:
-        """4 * d * Hq * sum(L^2) / 2: causal dense attention FLOPs (QK^T and PV)."""
-        return 4.0 * self.head_dim * self.num_q_heads * sum(L * L for L in self.seqlens) / 2.0
+        """4 * d * Hq * sum(Lq * off + Lq^2 / 2): causal dense attention FLOPs
+        (QK^T and PV) of queries at the end of Lk = off + Lq keys; L^2 / 2 per
+        request for a whole prefill."""
+        return 4.0 * self.head_dim * self.num_q_heads * sum(
+            Lq * (Lk - Lq) + Lq * Lq / 2.0 for Lq, Lk in zip(self.seqlens, self.key_seqlens))
 
 
 # --------------------------------------------------------------------------
@@ -237,6 +248,35 @@ def paginate(kv: torch.Tensor, cu_seqlens: List[int], page_size: int, perm: np.n
             pages[phys, : b - a] = kv[a:b]
             table[r, p] = phys
     return pages, table
+
+
+def chunk_of(wl: Workload, start: int, length: int) -> Workload:
+    """One chunk of a chunked prefill of a whole-prefill workload: per request,
+    the queries at positions [start, min(start + length, L_r)) against keys
+    [0, min(start + length, L_r)). Requests with L_r <= start drop out.
+    ``start`` must be a multiple of the block size (chunks start on block
+    boundaries). Contiguous K / V keep each request's key prefix; paged K / V
+    keep the pools and the surviving requests' page-table rows."""
+    if wl.cu_seqlens_k is not None:
+        raise ValueError("already chunked")
+    if start % wl.block_size:
+        raise ValueError("chunks start on block boundaries")
+    cu = wl.cu_seqlens
+    keep = [r for r in range(len(cu) - 1) if cu[r + 1] - cu[r] > start]
+    qs, ks, vs, cq, ck = [], [], [], [0], [0]
+    for r in keep:
+        L = cu[r + 1] - cu[r]
+        end = min(start + length, L)
+        qs.append(wl.q[cu[r] + start:cu[r] + end])
+        ks.append(wl.k[cu[r]:cu[r] + end])
+        vs.append(wl.v[cu[r]:cu[r] + end])
+        cq.append(cq[-1] + end - start)
+        ck.append(ck[-1] + end)
+    out = dataclasses.replace(wl, q=torch.cat(qs), k=torch.cat(ks), v=torch.cat(vs), cu_seqlens=cq,
+                              cu_seqlens_k=ck, planted=None)
+    if wl.page_table is not None:
+        out.page_table = wl.page_table[keep].contiguous()
+    return out
 
 
 # Named workloads. ``L`` etc. can be overridden to make smaller parity cases of

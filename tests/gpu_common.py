@@ -31,7 +31,7 @@ def upload(wl, device="cuda:0", paged: Optional[bool] = None):
                     for s in (wl.descale_q, wl.descale_k, wl.descale_v)]
     prob = fp.Problem(wl.cu_seqlens, wl.num_q_heads, wl.num_kv_heads, wl.block_size, wl.head_dim,
                       fp.FP_FP8_E4M3 if wl.dtype == "fp8" else fp.FP_BF16, descales, table,
-                      wl.page_size if paged else 0, k.shape[0] if paged else 0)
+                      wl.page_size if paged else 0, k.shape[0] if paged else 0, wl.cu_seqlens_k)
     return prob, q, k, v
 
 
@@ -81,7 +81,8 @@ def run_oracle(wl, alpha=None, mean_correction=True, do_attend=True, rows=None, 
         kw = dict(K_pages=kp, V_pages=vp, page_table=wl.page_table.numpy(), page_size=wl.page_size)
         K = V = None
     return oracle.prefill(Q, K, V, wl.cu_seqlens, wl.num_kv_heads, wl.block_size, alpha, wl.sel_scale, msl,
-                          1.0 / math.sqrt(wl.head_dim), mean_correction, do_attend, rows, **kw, **(forced or {}))
+                          1.0 / math.sqrt(wl.head_dim), mean_correction, do_attend, rows, **kw, **(forced or {}),
+                          cu_seqlens_k=wl.cu_seqlens_k)
 
 
 def csr_rows(row_ptr, col_idx):

@@ -55,12 +55,39 @@ def test_attention_workspace_sizes():
 
 def test_index_shape_and_workspace():
     p = _prob()
-    rows, nnz, nb = fp.index_shape(p)
+    rows, nnz, nb, nbk = fp.index_shape(p)
     nbs = [8, 16]
     assert nb == 24 and rows == 8 * 24
     assert nnz == 8 * sum(n * (n + 1) // 2 for n in nbs)
     ws = fp.select_workspace_bytes(p)
     assert ws >= 4 * (nnz + 2 * rows)
+
+
+def test_chunked_index_shape():
+    # Request 0: a 1000-token chunk after 2048 earlier tokens (qb0 = 16, 8
+    # query blocks, 24 key blocks); request 1: a whole 640-token prefill.
+    p = _prob(cu_seqlens=[0, 1000, 1640], cu_seqlens_k=[0, 3048, 3688])
+    rows, nnz, nbq, nbk = fp.index_shape(p)
+    assert (nbq, nbk) == (8 + 5, 24 + 5) and rows == 8 * 13
+    assert nnz == 8 * (sum(16 + i + 1 for i in range(8)) + 5 * 6 // 2)
+    def a256(x):
+        return (x + 255) // 256 * 256
+    assert fp.attn_workspace_bytes(p, True) == 2 * a256(8 * nbk * 128 * 2)
+    ds = [torch.ones(1) for _ in range(3)]
+    p8 = _prob(cu_seqlens=[0, 1000, 1640], cu_seqlens_k=[0, 3048, 3688], dtype=fp.FP_FP8_E4M3, descales=ds)
+    # FP8 copies cover every key token (Tk = 3688), not only the chunk
+    assert fp.attn_workspace_bytes(p8, False) == 2 * a256(3688 * 8 * 128 * 2)
+
+
+@pytest.mark.parametrize("cuk", [
+    [0, 999, 1640],     # fewer keys than queries
+    [0, 1100, 1740],    # chunk offset 100 is not a multiple of 128
+    [5, 1000, 1640],    # does not start at 0
+])
+def test_chunked_validation(cuk):
+    with pytest.raises(fp.FpError) as e:
+        fp.validate(_prob(cu_seqlens=[0, 1000, 1640], cu_seqlens_k=cuk))
+    assert e.value.code == 2
 
 
 def test_index_memory_matches_the_pages_order_of_magnitude():
@@ -70,7 +97,7 @@ def test_index_memory_matches_the_pages_order_of_magnitude():
     # causal block of 128 tokens, per KV head) times the density gives the
     # same order: 4 * 1024*1025/2 * 0.05 * 4 B ~ 0.4 MB, far under the mask.
     p = _prob(cu_seqlens=[0, 131072], num_q_heads=32, num_kv_heads=4, block_size=128)
-    rows, nnz, nb = fp.index_shape(p)
+    rows, nnz, nb, nbk = fp.index_shape(p)
     mask_bytes = 32 * 1024 * 1024
     assert mask_bytes == 32 * 2 ** 20
     assert nnz * 4 * 0.05 < 6e6 < mask_bytes
@@ -140,7 +167,7 @@ def test_compute_calls_reject_before_launch():
     vp = ctypes.c_void_p
     fake = vp(0x1000)
     assert L.fp_pool_blocks(p.ref, None, fake, fake, fake, fake, fake, None) == 1
-    rows, nnz, nb = fp.index_shape(p)
+    rows, nnz, nb, nbk = fp.index_shape(p)
     ws = fp.select_workspace_bytes(p)
     assert L.fp_select_blocks(p.ref, ctypes.byref(sel), fake, fake, fake, fake, nnz - 1, fake, ws, None) == 7
     assert L.fp_select_blocks(p.ref, ctypes.byref(sel), fake, fake, fake, fake, nnz, fake, ws - 1, None) == 8

@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _check_full(wl, alpha=None, mean_correction=True, paged=None, min_sparse_len=None, forced=None):
-    print(f"[parity] {wl.name} L={wl.seqlens} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} B={wl.block_size} "
+    print(f"[parity] {wl.name} L={wl.seqlens} Lk={wl.key_seqlens} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} B={wl.block_size} "
           f"dtype={wl.dtype} alpha={alpha if alpha is not None else wl.alpha} mc={mean_correction} "
           f"paged={paged if paged is not None else wl.paged} forced={forced}", flush=True)
     gpu = run_gpu(wl, alpha, mean_correction, paged, min_sparse_len=min_sparse_len, forced=forced)
@@ -33,11 +33,14 @@ def _check_full(wl, alpha=None, mean_correction=True, paged=None, min_sparse_len
     LSE = np.full((wl.num_q_heads, Q.shape[0]), np.nan)
     import math
     G = wl.num_q_heads // wl.num_kv_heads
+    cuk = wl.cu_seqlens_k or wl.cu_seqlens
     for r in range(len(wl.seqlens)):
         s, e = wl.cu_seqlens[r], wl.cu_seqlens[r + 1]
-        a, b = orc.blk_off[r], orc.blk_off[r + 1]
-        o, l = oracle.attend(Q[s:e], K[s:e], V[s:e], orc.kbar[:, a:b], orc.vbar[:, a:b], sets[r], wl.block_size, G,
-                             1.0 / math.sqrt(wl.head_dim), mean_correction)
+        ks, ke = cuk[r], cuk[r + 1]
+        a, b = orc.kblk_off[r], orc.kblk_off[r + 1]
+        o, l = oracle.attend(Q[s:e], K[ks:ke], V[ks:ke], orc.kbar[:, a:b], orc.vbar[:, a:b], sets[r],
+                             wl.block_size, G, 1.0 / math.sqrt(wl.head_dim), mean_correction,
+                             q_off=(ke - ks) - (e - s))
         O[s:e], LSE[:, s:e] = o, l
     o_err, l_err = compare_outputs(gpu["out"], gpu["lse"], O, LSE, O_TOL[wl.dtype])
     print(f"[parity] ok: nnz={gpu['row_ptr'][-1]} near_rows={n_near} O_err={o_err:.2e} LSE_err={l_err:.2e}",
@@ -158,3 +161,59 @@ def test_runs_are_bitwise_deterministic():
     b = run_gpu(wl)
     for key in a:
         assert np.array_equal(a[key], b[key]), key
+
+
+# ---------------------------------------------------------------- chunked prefill
+
+def _with_whole_request(chunk, whole):
+    """Append a whole-prompt request (keys = queries) to a chunked batch."""
+    import dataclasses
+    Tq, Tk = chunk.cu_seqlens[-1], chunk.cu_seqlens_k[-1]
+    L = whole.cu_seqlens[-1]
+    return dataclasses.replace(chunk, q=torch.cat([chunk.q, whole.q]), k=torch.cat([chunk.k, whole.k]),
+                               v=torch.cat([chunk.v, whole.v]), cu_seqlens=chunk.cu_seqlens + [Tq + L],
+                               cu_seqlens_k=chunk.cu_seqlens_k + [Tk + L])
+
+
+def test_chunked_prefill_ragged():
+    """Chunked prefill ([digest] Table 6): a 1000-query chunk after 2048
+    earlier positions of one request, the short last chunk (552 queries) of
+    another, and a ragged whole prompt, in one batch; then the dense kernel
+    on the same batch against the oracle with every block kept."""
+    wl = synth.make_workload("llama_32k", lengths=[3048, 2600], Hq=8, Hkv=2, n_planted=4, kind="varlen",
+                             seeds_base=20, page_size=0, min_sparse_len=0)
+    whole = synth.make_workload("llama_32k", L=777, Hq=8, Hkv=2, n_planted=2)
+    batch = _with_whole_request(synth.chunk_of(wl, 2048, 1000), whole)
+    assert batch.seqlens == [1000, 552, 777] and batch.key_seqlens == [3048, 2600, 777]
+    _check_full(batch)
+    dn = run_gpu(batch, dense=True)
+    orc = run_oracle(batch, alpha=0.0)
+    compare_outputs(dn["out"], dn["lse"], orc.O, orc.LSE, O_TOL["bf16"])
+
+
+def test_chunked_prefill_paged_fp8_and_forced():
+    wl = synth.make_workload("qwen4b_varlen_paged", lengths=[2900, 1500], Hq=8, Hkv=2, min_sparse_len=0,
+                             page_size=48, n_planted=3)
+    _check_full(synth.chunk_of(wl, 1024, 1024), forced=dict(sink=1, window=2, last_n=2))
+    wl8 = synth.make_workload("qwen30b_128k_fp8", L=3500, Hq=16, Hkv=2, n_planted=6)
+    _check_full(synth.chunk_of(wl8, 2560, 2048))
+
+
+def test_chunked_rows_equal_whole_prefill_bitwise():
+    """A chunk's rows see the same pooled statistics, the same selection and
+    the same items in the same order as in one prefill of the whole prompt,
+    so the GPU path gives bitwise the same outputs for them."""
+    wl = synth.make_workload("llama_32k", L=3000, Hq=8, Hkv=2, n_planted=6)
+    whole = run_gpu(wl)
+    B, start = wl.block_size, 1536
+    ch = run_gpu(synth.chunk_of(wl, start, 4096))
+    assert np.array_equal(ch["out"], whole["out"][start:])
+    assert np.array_equal(ch["lse"], whole["lse"][:, start:])
+    assert np.array_equal(ch["k_bar"], whole["k_bar"]) and np.array_equal(ch["v_bar"], whole["v_bar"])
+    nb, qb0 = -(-3000 // B), start // B
+    for h in range(wl.num_kv_heads):
+        assert np.array_equal(ch["q_bar"][h], whole["q_bar"][h, qb0:])
+        for i in range(nb - qb0):
+            a = ch["col_idx"][ch["row_ptr"][h * (nb - qb0) + i]:ch["row_ptr"][h * (nb - qb0) + i + 1]]
+            gr = h * nb + qb0 + i
+            assert np.array_equal(a, whole["col_idx"][whole["row_ptr"][gr]:whole["row_ptr"][gr + 1]])

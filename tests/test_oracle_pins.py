@@ -390,3 +390,76 @@ def test_forced_keeps_rules(sink, window, last_n):
             assert set(forced[h][I].tolist()) == set(plain[h][I].tolist()) | set(only[h][I].tolist())
     for h, I, J in near:
         assert J not in set(only[h][I].tolist())
+
+
+# ---------------------------------------------------------------- chunked prefill
+
+def test_chunked_alpha_zero_equals_dense_over_the_prefix():
+    """A chunk's queries sit at the end of the key sequence (bottom-right causal
+    alignment): with every block kept, query t of a chunk of Lq after off
+    earlier positions attends to keys 0 .. off + t, which the library routine
+    computes here from an explicit mask."""
+    Lk, Lq, Hq, Hkv, d, B = 100, 36, 4, 2, 8, 16        # off = 64 = 4 blocks
+    Q, K, V = _rand((Lq, Hq, d), 60), _rand((Lk, Hkv, d), 61), _rand((Lk, Hkv, d), 62)
+    sm = 1.0 / math.sqrt(d)
+    res = oracle.prefill(Q, K, V, [0, Lq], Hkv, B, 0.0, sm_scale=sm, cu_seqlens_k=[0, Lk])
+    G = Hq // Hkv
+    off = Lk - Lq
+    mask = np.where(np.arange(Lk)[None, :] <= off + np.arange(Lq)[:, None], 0.0, -np.inf)[None]
+    o, lse = sdpa_with_lse(Q.transpose(1, 0, 2).copy(), np.repeat(K, G, axis=1).transpose(1, 0, 2).copy(),
+                           np.repeat(V, G, axis=1).transpose(1, 0, 2).copy(), mask, sm)
+    assert np.allclose(res.O, o.transpose(1, 0, 2), atol=1e-10)
+    assert np.allclose(res.LSE, lse, atol=1e-10)
+    # rows of query block i hold key blocks 0 .. 4 + i
+    NBq = -(-Lq // B)
+    assert res.row_ptr[-1] == Hkv * sum(off // B + i + 1 for i in range(NBq))
+    assert res.qbar.shape[1] == NBq and res.kbar.shape[1] == -(-Lk // B)
+
+
+@pytest.mark.parametrize("alpha,mc,last_n", [(0.5, True, 0), (0.3, False, 0), (0.5, True, 2)])
+def test_chunked_rows_equal_the_whole_prefill(alpha, mc, last_n):
+    """Every quantity of a row depends only on its own queries and on keys at
+    or before them, so the last Lq positions run as a chunk give the same
+    pooled query, the same selected blocks and the same outputs as in one
+    prefill of the whole sequence (the forced last-n rule counts from the end
+    of the keys in both). Checked for two requests of a ragged batch."""
+    Hq, Hkv, d, B = 4, 2, 8, 16
+    Lks, Lqs = [150, 90], [54, 90]                      # request 0 chunked at 96, request 1 whole
+    T = sum(Lks)
+    Q, K, V = _rand((T, Hq, d), 63), _rand((T, Hkv, d), 64), _rand((T, Hkv, d), 65)
+    sm = 1.0 / math.sqrt(d)
+    cuk = [0, Lks[0], T]
+    full = oracle.prefill(Q, K, V, cuk, Hkv, B, alpha, sm_scale=sm, mean_correction=mc, last_n=last_n)
+    qsel = np.concatenate([np.arange(Lks[0] - Lqs[0], Lks[0]), np.arange(Lks[0], T)])
+    cuq = [0, Lqs[0], Lqs[0] + Lqs[1]]
+    ch = oracle.prefill(Q[qsel], K, V, cuq, Hkv, B, alpha, sm_scale=sm, mean_correction=mc, last_n=last_n,
+                        cu_seqlens_k=cuk)
+    assert np.array_equal(ch.O, full.O[qsel]) and np.array_equal(ch.LSE, full.LSE[:, qsel])
+    assert np.array_equal(ch.kbar, full.kbar) and np.array_equal(ch.vbar, full.vbar)
+    NBf, NBc = full.blk_off[-1], ch.blk_off[-1]
+    qb0 = [(Lks[r] - Lqs[r]) // B for r in range(2)]
+    for h in range(Hkv):
+        for r in range(2):
+            for i in range(ch.blk_off[r + 1] - ch.blk_off[r]):
+                gc = h * NBc + ch.blk_off[r] + i
+                gf = h * NBf + full.blk_off[r] + qb0[r] + i
+                assert np.array_equal(ch.qbar[h, ch.blk_off[r] + i], full.qbar[h, full.blk_off[r] + qb0[r] + i])
+                assert np.array_equal(ch.col_idx[ch.row_ptr[gc]:ch.row_ptr[gc + 1]],
+                                      full.col_idx[full.row_ptr[gf]:full.row_ptr[gf + 1]])
+    assert ch.row_ptr[-1] < full.row_ptr[-1]
+
+
+def test_chunked_loop_coding_agrees():
+    Lk, Lq, Hq, Hkv, d, B = 77, 29, 4, 2, 8, 8          # off = 48 = 6 blocks
+    Q, K, V = _rand((Lq, Hq, d), 66), _rand((Lk, Hkv, d), 67), _rand((Lk, Hkv, d), 68)
+    sm = 1.0 / math.sqrt(d)
+    res = oracle.prefill(Q, K, V, [0, Lq], Hkv, B, 0.5, sm_scale=sm, cu_seqlens_k=[0, Lk])
+    o, lse = oracle.attend_loop(Q, K, V, res.kbar, res.vbar, res.sets[0], B, Hq // Hkv, sm, True, q_off=Lk - Lq)
+    assert np.allclose(res.O, o, atol=1e-12, rtol=0)
+    assert np.allclose(res.LSE, lse, atol=1e-12, rtol=0)
+
+
+def test_chunked_rejects_misaligned_chunks():
+    Q, K, V = _rand((10, 2, 8), 69), _rand((30, 1, 8), 70), _rand((30, 1, 8), 71)
+    with pytest.raises(ValueError):
+        oracle.prefill(Q, K, V, [0, 10], 1, 8, 0.5, cu_seqlens_k=[0, 30])   # off = 20, not a multiple of 8
