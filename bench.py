@@ -79,6 +79,8 @@ def parse():
     ap.add_argument("--window", type=int, default=0, help="forced keep: key blocks left of the diagonal")
     ap.add_argument("--last-n", type=int, default=0, help="forced keep: dense last query blocks")
     ap.add_argument("--no-mean-correction", action="store_true", help="drop pruned blocks (the ablation)")
+    ap.add_argument("--chunk", type=int, default=0,
+                    help="chunked prefill: run the prompt as consecutive chunks of this many queries")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=16, help="attention rows the CPU baseline computes")
@@ -108,6 +110,8 @@ def csr_work(row_ptr, col_idx, wl, blk_off, mean_correction=True):
     packed rows; full tile on the diagonal). Per pruned causal (h, I, J < I):
     4 * d * (G * n_I) FLOPs (one pooled column). Also returns the strict
     causal count (diagonal tile halved) and the kept fraction over causal pairs.
+    Query block i of a request sits at key block I = qb0 + i (qb0 > 0 for a
+    chunk of a chunked prefill).
     """
     d, B = wl.head_dim, wl.block_size
     G = wl.num_q_heads // wl.num_kv_heads
@@ -116,10 +120,11 @@ def csr_work(row_ptr, col_idx, wl, blk_off, mean_correction=True):
     flops = 0.0
     strict = 0.0
     pairs = 0
-    for r, L in enumerate(wl.seqlens):
+    for r, (Lq, Lk) in enumerate(zip(wl.seqlens, wl.key_seqlens)):
         nb = blk_off[r + 1] - blk_off[r]
-        nI = np.minimum(B, L - np.arange(nb) * B).astype(np.float64)
-        dense_req = L < wl.min_sparse_len
+        I = (Lk - Lq) // B + np.arange(nb)
+        nI = np.minimum(B, Lk - I * B).astype(np.float64)
+        dense_req = Lq < wl.min_sparse_len
         for h in range(wl.num_kv_heads):
             rows = h * NBt + blk_off[r] + np.arange(nb)
             c = counts[rows].astype(np.float64)
@@ -128,20 +133,23 @@ def csr_work(row_ptr, col_idx, wl, blk_off, mean_correction=True):
             flops += 4 * d * G * float(exact.sum())
             strict += 4 * d * G * float(((c - 1) * nI * B + nI * (nI + 1) / 2).sum())
             if mean_correction and not dense_req:
-                pruned = np.arange(nb) - (c - 1)
+                pruned = I - (c - 1)
                 flops += 4 * d * G * float((pruned * nI).sum())
                 strict += 4 * d * G * float((pruned * nI).sum())
-            pairs += nb * (nb + 1) // 2
+            pairs += int((I + 1).sum())
     kept = float(row_ptr[-1]) / float(pairs)
     return flops, strict, kept
 
 
 def stage1_bytes(wl):
-    """Algorithmic HBM bytes of pooling: read Q, K, V once; write 3 pooled tensors."""
+    """Algorithmic HBM bytes of pooling: read the queries and every key and value
+    position once; write the pooled tensors."""
     e = 1 if wl.dtype == "fp8" else 2
-    T, d = wl.total_tokens, wl.head_dim
-    nbt = sum(-(-L // wl.block_size) for L in wl.seqlens)
-    return T * (wl.num_q_heads + 2 * wl.num_kv_heads) * d * e + 3 * wl.num_kv_heads * nbt * d * 4
+    d, B = wl.head_dim, wl.block_size
+    nbq = sum(-(-L // B) for L in wl.seqlens)
+    nbk = sum(-(-L // B) for L in wl.key_seqlens)
+    return (sum(wl.seqlens) * wl.num_q_heads + 2 * sum(wl.key_seqlens) * wl.num_kv_heads) * d * e + \
+        (nbq + 2 * nbk) * wl.num_kv_heads * d * 4
 
 
 def cpu_baseline(wl, row_ptr, n_rows, seed=0, mean_correction=True, forced=None):
@@ -195,6 +203,97 @@ def cpu_baseline(wl, row_ptr, n_rows, seed=0, mean_correction=True, forced=None)
                         f"{t_att:.0f} s; input conversion {t_conv:.1f} s not counted"))
 
 
+def run_chunked(args, wl, fp, torch, q, k, v, descales):
+    """The whole prompt as consecutive chunks of ``args.chunk`` queries, each
+    against every key position so far (chunked prefill: pool, select and
+    attend once per chunk). A step is one pass over all chunks; the record
+    has the same fields as a whole-prefill run, summed over the chunks."""
+    import synth
+    if len(wl.seqlens) != 1 or wl.paged:
+        sys.exit("--chunk needs a single-request contiguous workload")
+    L, C = wl.seqlens[0], args.chunk
+    if C % wl.block_size:
+        sys.exit("--chunk must be a multiple of the block size")
+    starts = list(range(0, L, C))
+    dt = fp.FP_FP8_E4M3 if wl.dtype == "fp8" else fp.FP_BF16
+    sel = fp.select_args(wl.alpha, wl.sel_scale, wl.min_sparse_len, args.sink, args.window, args.last_n)
+    att = fp.attn_args(0.0, not args.no_mean_correction)
+    jobs = []
+    for s0 in starts:
+        c = min(C, L - s0)
+        prob = fp.Problem([0, c], wl.num_q_heads, wl.num_kv_heads, wl.block_size, wl.head_dim, dt, descales,
+                          cu_seqlens_k=[0, s0 + c])
+        jobs.append((s0, c, prob, fp.Buffers(prob, q.device)))
+    torch.cuda.synchronize()
+
+    def step(evs=None):
+        for n, (s0, c, prob, b) in enumerate(jobs):
+            ev = None if evs is None else evs[n]
+            qc = q[s0:s0 + c]
+            if ev is not None:
+                ev[0].record()
+            fp.pool_blocks(prob, qc, k, v, b.q_bar, b.k_bar, b.v_bar)
+            if ev is not None:
+                ev[1].record()
+            fp.select_blocks(prob, sel, b.q_bar, b.k_bar, b.row_ptr, b.col_idx, b.workspace)
+            if ev is not None:
+                ev[2].record()
+            fp.sparse_prefill(prob, att, qc, k, v, b.k_bar, b.v_bar, b.row_ptr, b.col_idx, b.out, b.lse,
+                              b.attn_workspace)
+            if ev is not None:
+                ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in jobs] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    def stage(a, b):
+        return float(np.mean([sum(e[a].elapsed_time(e[b]) for e in se) for se in evs]))
+    pool_ms, sel_ms, att_ms = stage(0, 1), stage(1, 2), stage(2, 3)
+    ms = float(np.mean([se[0][0].elapsed_time(se[-1][3]) for se in evs]))
+    flops = strict = 0.0
+    nnz = pairs = 0
+    for s0, c, prob, b in jobs:
+        cw = synth.chunk_of(wl, s0, c)
+        rp = b.row_ptr.cpu().numpy().astype(np.int64)
+        nbq = -(-c // wl.block_size)
+        f, st, _ = csr_work(rp, None, cw, np.array([0, nbq]), not args.no_mean_correction)
+        flops, strict = flops + f, strict + st
+        nnz += int(rp[-1])
+        qb0 = s0 // wl.block_size
+        pairs += wl.num_kv_heads * sum(qb0 + i + 1 for i in range(nbq))
+    dense_eq = wl.dense_equiv_flops()
+    peak = PEAK_TFLOPS[wl.dtype]
+    achieved = flops / (att_ms * 1e-3) / 1e12
+    rec = {
+        "metric": METRIC,
+        "value": dense_eq / (ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s (dense-equivalent)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "seq_lens": wl.seqlens, "chunk_tokens": C, "chunks": len(jobs),
+                   "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads, "block_size": wl.block_size,
+                   "alpha": wl.alpha, "mean_correction": not args.no_mean_correction,
+                   "kept_fraction": nnz / max(pairs, 1), "nnz": nnz},
+        "ms_per_layer": ms,
+        "stages_ms": {"pool": pool_ms, "select": sel_ms, "attention": att_ms},
+        "attn_mfma_frac_computed": achieved / peak,
+        "attn_flops_computed": flops,
+        "attn_flops_causal_strict": strict,
+        "dense_equiv_flops": dense_eq,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": None, "kernel": "attn_kernel (fp_sparse_prefill)"},
+        "wall_s_timed": wall,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_probe:
@@ -226,6 +325,9 @@ def main():
     if wl.dtype == "fp8":
         descales = [torch.tensor([s], dtype=torch.float32, device=dev) for s in
                     (wl.descale_q, wl.descale_k, wl.descale_v)]
+    if args.chunk:
+        run_chunked(args, wl, fp, torch, q, k, v, descales)
+        return
     prob = fp.Problem(wl.cu_seqlens, wl.num_q_heads, wl.num_kv_heads, wl.block_size, wl.head_dim,
                       fp.FP_FP8_E4M3 if wl.dtype == "fp8" else fp.FP_BF16, descales, table,
                       wl.page_size, k.shape[0] if wl.paged else 0)
