@@ -81,6 +81,8 @@ def parse():
     ap.add_argument("--no-mean-correction", action="store_true", help="drop pruned blocks (the ablation)")
     ap.add_argument("--chunk", type=int, default=0,
                     help="chunked prefill: run the prompt as consecutive chunks of this many queries")
+    ap.add_argument("--chunk-repool", action="store_true",
+                    help="with --chunk: pool every key block so far in each chunk (no reuse)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=16, help="attention rows the CPU baseline computes")
@@ -218,12 +220,17 @@ def run_chunked(args, wl, fp, torch, q, k, v, descales):
     dt = fp.FP_FP8_E4M3 if wl.dtype == "fp8" else fp.FP_BF16
     sel = fp.select_args(wl.alpha, wl.sel_scale, wl.min_sparse_len, args.sink, args.window, args.last_n)
     att = fp.attn_args(0.0, not args.no_mean_correction)
+    NB = -(-L // wl.block_size)
     jobs = []
     for s0 in starts:
         c = min(C, L - s0)
         prob = fp.Problem([0, c], wl.num_q_heads, wl.num_kv_heads, wl.block_size, wl.head_dim, dt, descales,
-                          cu_seqlens_k=[0, s0 + c])
+                          cu_seqlens_k=[0, s0 + c], pooled_pitch=NB)
         jobs.append((s0, c, prob, fp.Buffers(prob, q.device)))
+    # one k_bar / v_bar for the whole prompt: each chunk pools only its own key
+    # blocks into it (unless --chunk-repool, which pools every block so far)
+    k_bar, v_bar = jobs[0][3].k_bar, jobs[0][3].v_bar
+    pool = fp.pool_blocks if args.chunk_repool else fp.pool_chunk_blocks
     torch.cuda.synchronize()
 
     def step(evs=None):
@@ -232,13 +239,13 @@ def run_chunked(args, wl, fp, torch, q, k, v, descales):
             qc = q[s0:s0 + c]
             if ev is not None:
                 ev[0].record()
-            fp.pool_blocks(prob, qc, k, v, b.q_bar, b.k_bar, b.v_bar)
+            pool(prob, qc, k, v, b.q_bar, k_bar, v_bar)
             if ev is not None:
                 ev[1].record()
-            fp.select_blocks(prob, sel, b.q_bar, b.k_bar, b.row_ptr, b.col_idx, b.workspace)
+            fp.select_blocks(prob, sel, b.q_bar, k_bar, b.row_ptr, b.col_idx, b.workspace)
             if ev is not None:
                 ev[2].record()
-            fp.sparse_prefill(prob, att, qc, k, v, b.k_bar, b.v_bar, b.row_ptr, b.col_idx, b.out, b.lse,
+            fp.sparse_prefill(prob, att, qc, k, v, k_bar, v_bar, b.row_ptr, b.col_idx, b.out, b.lse,
                               b.attn_workspace)
             if ev is not None:
                 ev[3].record()
@@ -278,6 +285,7 @@ def run_chunked(args, wl, fp, torch, q, k, v, descales):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
         "data": "synthetic",
         "config": {"workload": wl.name, "seq_lens": wl.seqlens, "chunk_tokens": C, "chunks": len(jobs),
+                   "chunk_pooling": "repool" if args.chunk_repool else "reuse",
                    "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads, "block_size": wl.block_size,
                    "alpha": wl.alpha, "mean_correction": not args.no_mean_correction,
                    "kept_fraction": nnz / max(pairs, 1), "nnz": nnz},

@@ -6,7 +6,7 @@ library has not been built, importing the compute functions raises at call
 time with a message that says so; there is no fallback path.
 
 Entry points mirror the C ABI in include/fpv2.h:
-  pool_blocks, select_blocks, sparse_prefill, dense_prefill
+  pool_blocks, pool_chunk_blocks, select_blocks, sparse_prefill, dense_prefill
 plus the convenience ``prefill`` that allocates outputs and runs all three
 stages, and the host-only ``index_shape`` / ``select_workspace_bytes`` /
 ``attn_workspace_bytes`` / ``validate``.
@@ -59,6 +59,7 @@ class _Problem(ctypes.Structure):
         ("max_pages_per_seq", ctypes.c_int32),
         ("num_pages", ctypes.c_int32),
         ("cu_seqlens_k", ctypes.POINTER(ctypes.c_int32)),
+        ("pooled_pitch", ctypes.c_int32),
     ]
 
 
@@ -88,6 +89,7 @@ def lib() -> ctypes.CDLL:
         L.fp_select_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
         L.fp_validate.argtypes = [P, ctypes.POINTER(_SelectArgs), ctypes.POINTER(_AttnArgs)]
         L.fp_pool_blocks.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+        L.fp_pool_chunk_blocks.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
         L.fp_select_blocks.argtypes = [P, ctypes.POINTER(_SelectArgs), vp, vp, vp, vp, ctypes.c_int64, vp,
                                        ctypes.c_size_t, vp]
         L.fp_attn_workspace_bytes.argtypes = [P, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
@@ -95,7 +97,8 @@ def lib() -> ctypes.CDLL:
                                         ctypes.c_size_t, vp]
         L.fp_dense_prefill.argtypes = [P, ctypes.POINTER(_AttnArgs), vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         for f in ("fp_index_shape", "fp_select_workspace_bytes", "fp_attn_workspace_bytes", "fp_validate",
-                  "fp_pool_blocks", "fp_select_blocks", "fp_sparse_prefill", "fp_dense_prefill"):
+                  "fp_pool_blocks", "fp_pool_chunk_blocks", "fp_select_blocks", "fp_sparse_prefill",
+                  "fp_dense_prefill"):
             getattr(L, f).restype = ctypes.c_int32
         L.fp_status_string.argtypes = [ctypes.c_int32]
         L.fp_status_string.restype = ctypes.c_char_p
@@ -127,12 +130,13 @@ class Problem:
 
     ``cu_seqlens`` are the query offsets; ``cu_seqlens_k`` (None: the same) the
     key offsets. In chunked prefill request r's queries are the last
-    Lq_r = cu_seqlens[r+1] - cu_seqlens[r] of its Lk_r keys."""
+    Lq_r = cu_seqlens[r+1] - cu_seqlens[r] of its Lk_r keys. ``pooled_pitch``:
+    rows per KV head of k_bar / v_bar (0: the problem's key-block count)."""
 
     def __init__(self, cu_seqlens: Sequence[int], num_q_heads: int, num_kv_heads: int, block_size: int,
                  head_dim: int = 128, dtype: int = FP_BF16, descales: Optional[Sequence[torch.Tensor]] = None,
                  page_table: Optional[torch.Tensor] = None, page_size: int = 0, num_pages: int = 0,
-                 cu_seqlens_k: Optional[Sequence[int]] = None):
+                 cu_seqlens_k: Optional[Sequence[int]] = None, pooled_pitch: int = 0):
         cu = [int(x) for x in cu_seqlens]
         self.cu_seqlens = cu
         self.cu_seqlens_k = cu if cu_seqlens_k is None else [int(x) for x in cu_seqlens_k]
@@ -144,6 +148,7 @@ class Problem:
         if cu_seqlens_k is not None:
             self._cuk = (ctypes.c_int32 * len(self.cu_seqlens_k))(*self.cu_seqlens_k)
             s.cu_seqlens_k = ctypes.cast(self._cuk, ctypes.POINTER(ctypes.c_int32))
+        s.pooled_pitch = pooled_pitch
         s.num_q_heads, s.num_kv_heads, s.head_dim, s.block_size = num_q_heads, num_kv_heads, head_dim, block_size
         s.dtype = dtype
         if descales is not None:
@@ -214,6 +219,13 @@ def pool_blocks(prob: Problem, q, k, v, q_bar, k_bar, v_bar, stream=None):
                                 _stream(stream)))
 
 
+def pool_chunk_blocks(prob: Problem, q, k, v, q_bar, k_bar, v_bar, stream=None):
+    """fp_pool_chunk_blocks: pools q_bar and only the key blocks the chunk
+    adds; k_bar / v_bar rows of earlier blocks must hold earlier calls' values."""
+    _check(lib().fp_pool_chunk_blocks(prob.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(q_bar), _ptr(k_bar),
+                                      _ptr(v_bar), _stream(stream)))
+
+
 def select_blocks(prob: Problem, sel: _SelectArgs, q_bar, k_bar, row_ptr, col_idx, workspace, stream=None):
     _check(lib().fp_select_blocks(prob.ref, ctypes.byref(sel), _ptr(q_bar), _ptr(k_bar), _ptr(row_ptr),
                                   _ptr(col_idx), col_idx.numel(), _ptr(workspace), workspace.numel(),
@@ -248,9 +260,10 @@ class Buffers:
         T = prob.cu_seqlens[-1]
         Hq = prob.s.num_q_heads
         f32 = dict(dtype=torch.float32, device=device)
+        kp = prob.s.pooled_pitch or nbk
         self.q_bar = torch.empty((Hkv, nbq, head_dim), **f32)
-        self.k_bar = torch.empty((Hkv, nbk, head_dim), **f32)
-        self.v_bar = torch.empty((Hkv, nbk, head_dim), **f32)
+        self.k_bar = torch.empty((Hkv, kp, head_dim), **f32)
+        self.v_bar = torch.empty((Hkv, kp, head_dim), **f32)
         self.row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=device)
         self.col_idx = torch.empty(max(nnz, 1), dtype=torch.int32, device=device)
         self.workspace = torch.empty(select_workspace_bytes(prob), dtype=torch.uint8, device=device)

@@ -38,6 +38,7 @@ struct Shape {
   int64_t NBq_tot, NBk_tot;
   int64_t pairs;  // causal (query block, key block) pairs per KV head
   int nb_max;     // max_r NBk_r
+  int64_t kpitch; // rows per KV head of k_bar / v_bar
 };
 
 // Key offsets of the problem: cu_seqlens_k, or cu_seqlens for a whole prefill.
@@ -109,8 +110,11 @@ fp_status check_problem(const fp_problem* p, Shape* sh) {
   } else if (p->kv_layout != FP_KV_CONTIGUOUS) {
     return fail(FP_ERR_LAYOUT, "kv_layout=%d unknown", p->kv_layout);
   }
+  if (p->pooled_pitch != 0 && p->pooled_pitch < nbk_tot)
+    return fail(FP_ERR_SHAPE, "pooled_pitch=%d < %lld key blocks", p->pooled_pitch, (long long)nbk_tot);
   s.NBq_tot = nbq_tot;
   s.NBk_tot = nbk_tot;
+  s.kpitch = p->pooled_pitch ? p->pooled_pitch : nbk_tot;
   s.pairs = pairs;
   s.nb_max = nb_max;
   if (sh) *sh = s;
@@ -194,7 +198,7 @@ AttnWs attn_ws_layout(const fp_problem* p, const Shape& s, bool sparse) {
   AttnWs w{};
   const int64_t kv_rows = p->kv_layout == FP_KV_PAGED ? (int64_t)p->num_pages * p->page_size : s.Tk;
   w.kv_elems = kv_rows * p->num_kv_heads * p->head_dim;
-  const size_t pool = sparse ? align256((size_t)p->num_kv_heads * s.NBk_tot * p->head_dim * 2) : 0;
+  const size_t pool = sparse ? align256((size_t)p->num_kv_heads * s.kpitch * p->head_dim * 2) : 0;
   const size_t kv = p->dtype == FP_FP8_E4M3 ? align256((size_t)w.kv_elems * 2) : 0;
   w.kbar16 = 0;
   w.vbar16 = pool;
@@ -252,12 +256,12 @@ fp_status fp_validate(const fp_problem* p, const fp_select_args* sel, const fp_a
   return ok();
 }
 
-fp_status fp_pool_blocks(const fp_problem* p, const void* q, const void* k, const void* v, float* q_bar,
-                         float* k_bar, float* v_bar, void* stream) {
+static fp_status run_pool(const fp_problem* p, const void* q, const void* k, const void* v, float* q_bar,
+                          float* k_bar, float* v_bar, void* stream, bool chunk_only) {
   Shape s;
   fp_status st = check_problem(p, &s);
   if (st) return st;
-  if (!q || !k || !v || !q_bar || !k_bar || !v_bar) return fail(FP_ERR_NULL, "fp_pool_blocks: NULL buffer");
+  if (!q || !k || !v || !q_bar || !k_bar || !v_bar) return fail(FP_ERR_NULL, "pooling: NULL buffer");
   PoolParams pp{};
   pp.q = q; pp.k = k; pp.v = v;
   pp.q_bar = q_bar; pp.k_bar = k_bar; pp.v_bar = v_bar;
@@ -265,10 +269,22 @@ fp_status fp_pool_blocks(const fp_problem* p, const void* q, const void* k, cons
   pp.Hq = p->num_q_heads; pp.Hkv = p->num_kv_heads; pp.G = p->num_q_heads / p->num_kv_heads;
   pp.B = p->block_size; pp.NBq_tot = (int32_t)s.NBq_tot; pp.NBk_tot = (int32_t)s.NBk_tot;
   pp.fp8 = p->dtype == FP_FP8_E4M3;
+  pp.kpitch = (int32_t)s.kpitch;
+  pp.chunk_only = chunk_only ? 1 : 0;
   pp.kv = make_kv(p);
   pp.rt = make_table(p, s);
   if (pool_lds_bytes(pp.G) > 64 * 1024) return fail(FP_ERR_UNSUPPORTED, "GQA ratio %d too large for pooling", pp.G);
   return hip_status(launch_pool(pp, (hipStream_t)stream), "pool launch");
+}
+
+fp_status fp_pool_blocks(const fp_problem* p, const void* q, const void* k, const void* v, float* q_bar,
+                         float* k_bar, float* v_bar, void* stream) {
+  return run_pool(p, q, k, v, q_bar, k_bar, v_bar, stream, false);
+}
+
+fp_status fp_pool_chunk_blocks(const fp_problem* p, const void* q, const void* k, const void* v, float* q_bar,
+                               float* k_bar, float* v_bar, void* stream) {
+  return run_pool(p, q, k, v, q_bar, k_bar, v_bar, stream, true);
 }
 
 fp_status fp_select_blocks(const fp_problem* p, const fp_select_args* sel, const float* q_bar, const float* k_bar,
@@ -302,6 +318,7 @@ fp_status fp_select_blocks(const fp_problem* p, const fp_select_args* sel, const
   sp.last_n = sel->last_n_blocks;
   sp.Hkv = p->num_kv_heads; sp.NBq_tot = (int32_t)s.NBq_tot; sp.NBk_tot = (int32_t)s.NBk_tot;
   sp.B = p->block_size;
+  sp.kpitch = (int32_t)s.kpitch;
   sp.rt = make_table(p, s);
   return hip_status(launch_select(sp, (hipStream_t)stream), "select launch");
 }
@@ -342,6 +359,7 @@ static fp_status run_attention(const fp_problem* p, const fp_attn_args* attn, co
   ap.Hq = p->num_q_heads; ap.Hkv = p->num_kv_heads; ap.G = p->num_q_heads / p->num_kv_heads;
   ap.B = p->block_size; ap.NBq_tot = (int32_t)s.NBq_tot; ap.NBk_tot = (int32_t)s.NBk_tot;
   ap.T = (int32_t)s.Tq;
+  ap.kpitch = (int32_t)s.kpitch;
   ap.mean_correction = dense ? 0 : attn->mean_correction;
   ap.dense = dense ? 1 : 0;
   ap.subs = (ap.G * ap.B + attn_rows_per_wg() - 1) / attn_rows_per_wg();

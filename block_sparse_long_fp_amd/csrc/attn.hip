@@ -92,7 +92,7 @@ struct RowCtx {
   int n_exact;          // CSR entries (key blocks) of the row
   int n_items;          // plus the correction chunks
   const int32_t* cols;  // CSR row (nullptr in dense mode)
-  int64_t pooled_row0;  // row h * NBk_tot + kblk_off[r] of k_bar / v_bar
+  int64_t pooled_row0;  // row h * kpitch + kblk_off[r] of k_bar / v_bar
   int64_t tok_base;     // first key token of the request (contiguous K / V)
 };
 
@@ -564,7 +564,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   rc.cols = p.dense ? nullptr : p.col_idx + p.row_ptr[row];
   const bool do_corr = p.mean_correction && !p.dense && I > 0;
   rc.n_items = rc.n_exact + (do_corr ? (I + kPC - 1) / kPC : 0);
-  rc.pooled_row0 = (int64_t)rc.h * p.NBk_tot + rt.kblk_off[rc.r];
+  rc.pooled_row0 = (int64_t)rc.h * p.kpitch + rt.kblk_off[rc.r];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -712,7 +712,7 @@ void launch_attn_t(const AttnParams& p, dim3 grid, hipStream_t stream) {
 int attn_rows_per_wg() { return kRowsPerWG; }
 
 hipError_t launch_attn(const AttnParams& p, hipStream_t stream) {
-  const int64_t n_pool8 = p.kbar16 ? (int64_t)p.Hkv * p.NBk_tot * kHeadDim / 8 : 0;
+  const int64_t n_pool8 = p.kbar16 ? (int64_t)p.Hkv * p.kpitch * kHeadDim / 8 : 0;
   const int64_t n_kv8 = p.fp8 ? p.kv_elems / 8 : 0;
   if (n_pool8 + n_kv8 > 0) {
     const int64_t work = 2 * n_pool8 + 2 * n_kv8;

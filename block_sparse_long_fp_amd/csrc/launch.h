@@ -20,6 +20,8 @@ struct PoolParams {
   const float* descale_k;
   const float* descale_v;
   int32_t Hq, Hkv, G, B, NBq_tot, NBk_tot, fp8;
+  int32_t kpitch;       // rows per KV head of k_bar / v_bar (>= NBk_tot)
+  int32_t chunk_only;   // 1: pool only key blocks J >= qb0 (grid over query blocks)
   KVAddr kv;
   ReqTable rt;
 };
@@ -39,6 +41,7 @@ struct SelectParams {
   int32_t min_sparse_len;
   int32_t sink, window, last_n;  // forced keeps, in blocks
   int32_t Hkv, NBq_tot, NBk_tot, B;
+  int32_t kpitch;     // rows per KV head of k_bar (>= NBk_tot)
   ReqTable rt;
 };
 
@@ -62,6 +65,7 @@ struct AttnParams {
   const float* descale_v;
   float sm_scale;
   int32_t Hq, Hkv, G, B, NBq_tot, NBk_tot, T;  // T: query tokens
+  int32_t kpitch;       // rows per KV head of k_bar / v_bar (>= NBk_tot)
   int32_t mean_correction;
   int32_t dense;        // 1: ignore the CSR, attend to every causal block
   int32_t subs;         // workgroups per (h, I) row: ceil(G * B / rows_per_wg)

@@ -17,6 +17,8 @@
 // In chunked prefill a request's queries are its last positions; key blocks
 // before the chunk (J < qb0) pool K and V only, and key block J >= qb0 also
 // pools query block J - qb0 (the same positions, so the same token count).
+// The chunk-only variant (fp_pool_chunk_blocks) runs one workgroup per query
+// block and so pools only the key blocks J >= qb0 the chunk adds.
 #include "common.h"
 #include "launch.h"
 
@@ -47,13 +49,20 @@ __device__ __forceinline__ void load_chunk(const void* base, int64_t elem, float
 template <bool FP8>
 __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolParams p) {
   extern __shared__ float part[];  // [groups][slots*kChunks][8]
-  const int b = blockIdx.x;        // global key block id in [0, NBk_tot)
   const int h = blockIdx.y;
   const ReqTable& rt = p.rt;
-  // request of this block: last r with kblk_off[r] <= b
+  // blockIdx.x: a global key block id in [0, NBk_tot), or with chunk_only a
+  // global query block id in [0, NBq_tot) whose key block is pooled.
   int r = 0;
-  while (r + 1 < rt.R && rt.kblk_off[r + 1] <= b) ++r;
-  const int J = b - rt.kblk_off[r];
+  int J;
+  if (p.chunk_only) {
+    while (r + 1 < rt.R && rt.blk_off[r + 1] <= (int)blockIdx.x) ++r;
+    J = rt.qb0[r] + (int)blockIdx.x - rt.blk_off[r];
+  } else {
+    while (r + 1 < rt.R && rt.kblk_off[r + 1] <= (int)blockIdx.x) ++r;
+    J = (int)blockIdx.x - rt.kblk_off[r];
+  }
+  const int b = rt.kblk_off[r] + J;  // global key block id
   const int L = rt.ktok_off[r + 1] - rt.ktok_off[r];
   const int t0 = J * p.B;
   const int n = min(p.B, L - t0);
@@ -125,7 +134,7 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolParams p) {
       if (FP8) scale *= (kind == 1) ? *p.descale_k : *p.descale_v;
     }
     float* out = (kind == 0) ? p.q_bar : (kind == 1 ? p.k_bar : p.v_bar);
-    const int64_t orow = kind == 0 ? (int64_t)h * p.NBq_tot + rt.blk_off[r] + qi : (int64_t)h * p.NBk_tot + b;
+    const int64_t orow = kind == 0 ? (int64_t)h * p.NBq_tot + rt.blk_off[r] + qi : (int64_t)h * p.kpitch + b;
     float4* o4 = reinterpret_cast<float4*>(out + orow * kHeadDim + c * 8);
     o4[0] = make_float4(s[0] * scale, s[1] * scale, s[2] * scale, s[3] * scale);
     o4[1] = make_float4(s[4] * scale, s[5] * scale, s[6] * scale, s[7] * scale);
@@ -141,7 +150,7 @@ size_t pool_lds_bytes(int G) {
 }
 
 hipError_t launch_pool(const PoolParams& p, hipStream_t stream) {
-  dim3 grid(p.NBk_tot, p.Hkv);
+  dim3 grid(p.chunk_only ? p.NBq_tot : p.NBk_tot, p.Hkv);
   const size_t lds = pool_lds_bytes(p.G);
   if (p.fp8)
     hipLaunchKernelGGL(pool_kernel<true>, grid, dim3(kPoolThreads), lds, stream, p);

@@ -15,13 +15,14 @@
 // iff z_J - m >= ln(alpha) (the same as exp(z_J - m) >= alpha), plus the
 // forced blocks (the diagonal, and optionally sink / window / last-n rows).
 //
-// Three kernels, no host round trip:
+// Four kernels, no host round trip:
 //   score_kernel    one workgroup per (KV head, tile of 32 query blocks of one
-//                   request): q_bar tile and 32-row k_bar chunks staged in LDS,
-//                   each thread owns one row and every 8th column, so its
-//                   running max and its keep count need no other thread until
-//                   an 8-lane shuffle reduction. z goes to the workspace so
-//                   the count and the compaction see the same fp32 values.
+//                   request, tile of 64 key blocks): both pooled tiles staged
+//                   in LDS as fp32, each thread computes a 2 x 4 block of
+//                   scores, every score summed over the head dim in the same
+//                   order (so a score does not depend on its tile), and z goes
+//                   to the workspace. Tiles wholly above the diagonal exit.
+//   rowstat_kernel  one wave per row: row max of z, then the keep count.
 //   scan_kernel     one workgroup: exclusive prefix sum of the row counts
 //                   into row_ptr (wave shuffles, then a carry across chunks).
 //   compact_kernel  one wave per row: ballot of the keep flags of 64 columns,
@@ -33,8 +34,8 @@ namespace fpv2 {
 
 namespace {
 
-constexpr int kTileI = 32;       // query blocks per score workgroup
-constexpr int kTileJ = 32;       // key blocks per LDS chunk
+constexpr int kTileI = 32;       // query blocks per score tile
+constexpr int kTileJ = 64;       // key blocks per score tile
 constexpr int kScoreThreads = 256;
 constexpr int kPad = kHeadDim + 4;
 
@@ -71,8 +72,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(SelectParams p) {
   __shared__ float qs[kTileI][kPad];
   __shared__ float ks[kTileJ][kPad];
   const ReqTable& rt = p.rt;
-  const int h = blockIdx.y;
-  // Map blockIdx.x to (request, tile): tiles are numbered request by request.
+  const int h = blockIdx.z;
+  // Map blockIdx.x to (request, query tile): tiles are numbered request by request.
   int r = 0, tile = blockIdx.x;
   for (;;) {
     const int nb = rt.blk_off[r + 1] - rt.blk_off[r];
@@ -85,75 +86,99 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(SelectParams p) {
   const int NB = rt.kblk_off[r + 1] - rt.kblk_off[r];
   const int qb0 = rt.qb0[r];
   const int i0 = tile * kTileI;
-  if (i0 >= NBq) return;
+  const int J0 = blockIdx.y * kTileJ;
+  // Rows i0 .. i0 + 31 need columns J <= qb0 + i (and J < NB).
+  const int i_last = min(NBq, i0 + kTileI) - 1;
+  if (i0 >= NBq || J0 > qb0 + i_last || request_dense(p, r)) return;
   const int tid = threadIdx.x;
-  const int ti = tid >> 3;   // row within the tile
-  const int jq = tid & 7;    // column phase
-  const int i = i0 + ti;
-  const int I = qb0 + i;     // key block of the row's queries
-  const bool row_ok = i < NBq;
-  const int64_t row = (int64_t)h * p.NBq_tot + rt.blk_off[r] + i;
 
-  if (request_dense(p, r)) {
-    if (jq == 0 && row_ok) p.counts[row] = I + 1;
-    return;
-  }
-
-  // q_bar tile -> LDS
+  const float* qsrc = p.q_bar + ((int64_t)h * p.NBq_tot + rt.blk_off[r]) * kHeadDim;
+  const float* ksrc = p.k_bar + ((int64_t)h * p.kpitch + rt.kblk_off[r]) * kHeadDim;
   for (int e = tid; e < kTileI * (kHeadDim / 4); e += kScoreThreads) {
     const int rr = e / (kHeadDim / 4), c4 = e % (kHeadDim / 4);
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (i0 + rr < NBq) v = reinterpret_cast<const float4*>(p.q_bar + ((int64_t)h * p.NBq_tot + rt.blk_off[r] + i0 + rr) * kHeadDim)[c4];
+    if (i0 + rr < NBq) v = reinterpret_cast<const float4*>(qsrc + (int64_t)(i0 + rr) * kHeadDim)[c4];
     *reinterpret_cast<float4*>(&qs[rr][c4 * 4]) = v;
   }
-  float* zrow = p.zbuf + (int64_t)h * p.pairs_tot + pair_offset(rt, r) + row_pair_offset(i, qb0);
-  const int Jend = min(NB, qb0 + i0 + kTileI);  // exclusive bound of columns any row needs
-  float m = -INFINITY;
-  for (int J0 = 0; J0 < Jend; J0 += kTileJ) {
-    __syncthreads();
-    for (int e = tid; e < kTileJ * (kHeadDim / 4); e += kScoreThreads) {
-      const int rr = e / (kHeadDim / 4), c4 = e % (kHeadDim / 4);
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (J0 + rr < NB) v = reinterpret_cast<const float4*>(p.k_bar + ((int64_t)h * p.NBk_tot + rt.kblk_off[r] + J0 + rr) * kHeadDim)[c4];
-      *reinterpret_cast<float4*>(&ks[rr][c4 * 4]) = v;
-    }
-    __syncthreads();
-    if (row_ok) {
+  for (int e = tid; e < kTileJ * (kHeadDim / 4); e += kScoreThreads) {
+    const int rr = e / (kHeadDim / 4), c4 = e % (kHeadDim / 4);
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (J0 + rr < NB) v = reinterpret_cast<const float4*>(ksrc + (int64_t)(J0 + rr) * kHeadDim)[c4];
+    *reinterpret_cast<float4*>(&ks[rr][c4 * 4]) = v;
+  }
+  __syncthreads();
+
+  // Thread (ri, cj) owns rows ri, ri + 16 and columns cj + 16 u, u = 0..3.
+  const int ri = tid >> 4, cj = tid & 15;
+  float acc[2][4];
 #pragma unroll
-      for (int u = 0; u < kTileJ / 8; ++u) {
-        const int jj = jq + 8 * u;
-        const int J = J0 + jj;
-        if (J <= I) {
-          float acc = 0.f;
-#pragma unroll 8
-          for (int c = 0; c < kHeadDim; c += 4) {
-            const float4 a = *reinterpret_cast<const float4*>(&qs[ti][c]);
-            const float4 b = *reinterpret_cast<const float4*>(&ks[jj][c]);
-            acc = fmaf(a.x, b.x, acc);
-            acc = fmaf(a.y, b.y, acc);
-            acc = fmaf(a.z, b.z, acc);
-            acc = fmaf(a.w, b.w, acc);
-          }
-          const float z = p.sel_scale * acc;
-          zrow[J] = z;
-          m = fmaxf(m, z);
-        }
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[a][u] = 0.f;
+#pragma unroll 4
+  for (int c = 0; c < kHeadDim; c += 4) {
+    float4 qv[2], kv[4];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) qv[a] = *reinterpret_cast<const float4*>(&qs[ri + 16 * a][c]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) kv[u] = *reinterpret_cast<const float4*>(&ks[cj + 16 * u][c]);
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        acc[a][u] = fmaf(qv[a].x, kv[u].x, acc[a][u]);
+        acc[a][u] = fmaf(qv[a].y, kv[u].y, acc[a][u]);
+        acc[a][u] = fmaf(qv[a].z, kv[u].z, acc[a][u]);
+        acc[a][u] = fmaf(qv[a].w, kv[u].w, acc[a][u]);
       }
+  }
+  float* zh = p.zbuf + (int64_t)h * p.pairs_tot + pair_offset(rt, r);
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int i = i0 + ri + 16 * a;
+    if (i >= NBq) continue;
+    float* zrow = zh + row_pair_offset(i, qb0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int J = J0 + cj + 16 * u;
+      if (J <= qb0 + i) zrow[J] = p.sel_scale * acc[a][u];
     }
   }
-  // Row max over the 8 threads of the row (lanes 8k .. 8k+7 of one wave).
-  m = fmaxf(m, __shfl_xor(m, 1));
-  m = fmaxf(m, __shfl_xor(m, 2));
-  m = fmaxf(m, __shfl_xor(m, 4));
-  // Count: each thread re-reads the z values it wrote itself.
-  int cnt = 0;
-  if (row_ok) {
-    for (int J = jq; J <= I; J += 8) cnt += ((zrow[J] - m) >= p.log_alpha) || forced_keep(p, I, J, NB);
+}
+
+constexpr int kRowThreads = 256;
+
+// Row max and keep count of every row, one wave per row, from the stored
+// scores (so the count sees exactly the values the compaction will).
+__global__ __launch_bounds__(kRowThreads) void rowstat_kernel(SelectParams p) {
+  const ReqTable& rt = p.rt;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * (kRowThreads / 64) + (threadIdx.x >> 6);
+  const int64_t rows = (int64_t)p.Hkv * p.NBq_tot;
+  if (row >= rows) return;
+  const int h = (int)(row / p.NBq_tot);
+  const int b = (int)(row % p.NBq_tot);
+  int r = 0;
+  while (r + 1 < rt.R && rt.blk_off[r + 1] <= b) ++r;
+  const int i = b - rt.blk_off[r];
+  const int I = rt.qb0[r] + i;
+  const int NB = rt.kblk_off[r + 1] - rt.kblk_off[r];
+  if (request_dense(p, r)) {
+    if (lane == 0) p.counts[row] = I + 1;
+    return;
   }
-  cnt += __shfl_xor(cnt, 1);
-  cnt += __shfl_xor(cnt, 2);
-  cnt += __shfl_xor(cnt, 4);
-  if (row_ok && jq == 0) {
+  const float* zrow = p.zbuf + (int64_t)h * p.pairs_tot + pair_offset(rt, r) + row_pair_offset(i, rt.qb0[r]);
+  float m = -INFINITY;
+  for (int J = lane; J <= I; J += 64) m = fmaxf(m, zrow[J]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  int cnt = 0;
+  for (int J0 = 0; J0 <= I; J0 += 64) {
+    const int J = J0 + lane;
+    const bool keep = (J <= I) && (((zrow[J] - m) >= p.log_alpha) || forced_keep(p, I, J, NB));
+    cnt += __popcll(__ballot(keep));
+  }
+  if (lane == 0) {
     p.counts[row] = cnt;
     p.rowmax[row] = m;
   }
@@ -233,10 +258,15 @@ hipError_t launch_select(const SelectParams& p, hipStream_t stream) {
     const int nb = p.rt.blk_off[r + 1] - p.rt.blk_off[r];
     tiles += (nb + kTileI - 1) / kTileI;
   }
-  hipLaunchKernelGGL(score_kernel, dim3(tiles, p.Hkv), dim3(kScoreThreads), 0, stream, p);
+  const int jtiles = (p.rt.nb_max + kTileJ - 1) / kTileJ;
+  hipLaunchKernelGGL(score_kernel, dim3(tiles, jtiles, p.Hkv), dim3(kScoreThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)p.Hkv * p.NBq_tot;
+  const int64_t row_wgs = (rows + (kRowThreads / 64) - 1) / (kRowThreads / 64);
+  hipLaunchKernelGGL(rowstat_kernel, dim3((unsigned)row_wgs), dim3(kRowThreads), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, p.counts, p.row_ptr, rows);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

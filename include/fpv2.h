@@ -58,8 +58,8 @@
  *                           ([digest] "What they did", Fix 3; Table 7: paged KV,
  *                           arbitrary page size).
  *            pooled q_bar:  fp32 [Hkv, NBq_tot, d], row h * NBq_tot + blk_off[r] + i.
- *            pooled k_bar, v_bar: fp32 [Hkv, NBk_tot, d], row
- *                           h * NBk_tot + kblk_off[r] + J.
+ *            pooled k_bar, v_bar: fp32 [Hkv, P, d], row h * P + kblk_off[r] + J,
+ *                           P = pooled_pitch (NBk_tot when 0).
  *            CSR:           one row per (h, r, i), row id h * NBq_tot + blk_off[r] + i;
  *                           row_ptr int32 [Hkv * NBq_tot + 1]; col_idx int32
  *                           request-local key-block ids J <= I, strictly
@@ -78,7 +78,7 @@
 extern "C" {
 #endif
 
-#define FPV2_ABI_VERSION 4
+#define FPV2_ABI_VERSION 5
 
 /* Status codes. */
 typedef int32_t fp_status;
@@ -129,6 +129,9 @@ typedef struct fp_problem {
   int32_t num_pages;             /* pages in each of the K and V pools (paged)     */
   const int32_t* cu_seqlens_k;   /* HOST [R+1] key offsets, or NULL (= cu_seqlens);  */
                                  /* Lk_r >= Lq_r and (Lk_r - Lq_r) % B == 0          */
+  int32_t pooled_pitch;          /* rows per KV head of k_bar / v_bar: 0 means      */
+                                 /* NBk_tot, else >= NBk_tot (a buffer sized for a  */
+                                 /* whole prompt, reused across its chunks)         */
 } fp_problem;
 
 /* Block selection ([digest] abstract: max-based dynamic thresholding;
@@ -187,9 +190,21 @@ fp_status fp_validate(const fp_problem* p, const fp_select_args* sel, const fp_a
  * the sequence so far is pooled (in chunked prefill the earlier chunks' blocks
  * too). q, k, v: DEVICE inputs in the layouts above (k, v are the page pools
  * when paged). q_bar: DEVICE fp32 [Hkv, NBq_tot, d] output; k_bar, v_bar:
- * DEVICE fp32 [Hkv, NBk_tot, d] outputs. */
+ * DEVICE fp32 [Hkv, P, d] outputs (P = pooled_pitch). */
 fp_status fp_pool_blocks(const fp_problem* p, const void* q, const void* k, const void* v,
                          float* q_bar, float* k_bar, float* v_bar, void* stream);
+
+/* Stage 1a for one chunk of a chunked prefill: as fp_pool_blocks, but pools
+ * only the key blocks the chunk adds, J >= off_r / B. The blocks before the
+ * chunk are complete and their means do not change, so their k_bar / v_bar
+ * rows are neither read nor written here: they must already hold the values
+ * an earlier call wrote (typically the previous chunk's call on the same
+ * buffers, with a pooled_pitch that fits the whole prompt). The pages note
+ * that per-chunk selection repeats Stage 1 for every chunk ([podcast]);
+ * this call keeps that repeated work proportional to the chunk. With
+ * off_r = 0 it equals fp_pool_blocks. */
+fp_status fp_pool_chunk_blocks(const fp_problem* p, const void* q, const void* k, const void* v,
+                               float* q_bar, float* k_bar, float* v_bar, void* stream);
 
 /* Stage 1b: scoring, threshold and CSR build ([digest] abstract; Table 7).
  * q_bar, k_bar: DEVICE outputs of fp_pool_blocks. row_ptr: DEVICE int32

@@ -79,6 +79,19 @@ def test_chunked_index_shape():
     assert fp.attn_workspace_bytes(p8, False) == 2 * a256(3688 * 8 * 128 * 2)
 
 
+def test_pooled_pitch():
+    # a pitch below the key-block count is rejected; a larger one sizes the
+    # pooled copies of the attention workspace
+    with pytest.raises(fp.FpError) as e:
+        fp.validate(_prob(pooled_pitch=23))
+    assert e.value.code == 2
+    def a256(x):
+        return (x + 255) // 256 * 256
+    assert fp.attn_workspace_bytes(_prob(pooled_pitch=100), True) == 2 * a256(8 * 100 * 128 * 2)
+    b = fp.Problem([0, 1000], 32, 8, 128, cu_seqlens_k=[0, 3048], pooled_pitch=40)
+    assert fp.index_shape(b)[2:] == (8, 24)
+
+
 @pytest.mark.parametrize("cuk", [
     [0, 999, 1640],     # fewer keys than queries
     [0, 1100, 1740],    # chunk offset 100 is not a multiple of 128

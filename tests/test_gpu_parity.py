@@ -217,3 +217,42 @@ def test_chunked_rows_equal_whole_prefill_bitwise():
             a = ch["col_idx"][ch["row_ptr"][h * (nb - qb0) + i]:ch["row_ptr"][h * (nb - qb0) + i + 1]]
             gr = h * nb + qb0 + i
             assert np.array_equal(a, whole["col_idx"][whole["row_ptr"][gr]:whole["row_ptr"][gr + 1]])
+
+
+def test_chunk_pooling_reuses_earlier_blocks():
+    """fp_pool_chunk_blocks pools only the key blocks a chunk adds: on buffers
+    sized for the whole prompt (pooled_pitch), rows of earlier blocks are left
+    as they were, and a sequence of chunks, each pooled that way, then
+    selected and attended, gives bitwise the whole prefill's outputs."""
+    import block_sparse_long_fp_amd as fp
+    wl = synth.make_workload("llama_32k", L=3000, Hq=8, Hkv=2, n_planted=6)
+    whole = run_gpu(wl)
+    B, C, L = wl.block_size, 1024, 3000
+    NB = -(-L // B)
+    dev = "cuda:0"
+    q, k, v = wl.q.to(dev), wl.k.to(dev), wl.v.to(dev)
+    kbar = torch.full((2, NB, 128), 7.0, device=dev)
+    vbar = torch.full((2, NB, 128), 7.0, device=dev)
+    for s0 in range(0, L, C):
+        c = min(C, L - s0)
+        print(f"[parity] chunk at {s0}, {c} queries", flush=True)
+        prob = fp.Problem([0, c], 8, 2, B, cu_seqlens_k=[0, s0 + c], pooled_pitch=NB)
+        bufs = fp.Buffers(prob, dev)
+        # a fresh buffer: rows before the chunk keep a sentinel
+        sk = torch.full((2, NB, 128), 3.0, device=dev)
+        sv = torch.full((2, NB, 128), 3.0, device=dev)
+        fp.pool_chunk_blocks(prob, q[s0:s0 + c], k, v, bufs.q_bar, sk, sv)
+        fp.pool_chunk_blocks(prob, q[s0:s0 + c], k, v, bufs.q_bar, kbar, vbar)
+        fp.select_blocks(prob, fp.select_args(wl.alpha), bufs.q_bar, kbar, bufs.row_ptr, bufs.col_idx,
+                         bufs.workspace)
+        fp.sparse_prefill(prob, fp.attn_args(), q[s0:s0 + c], k, v, kbar, vbar, bufs.row_ptr, bufs.col_idx,
+                          bufs.out, bufs.lse, bufs.attn_workspace)
+        torch.cuda.synchronize()
+        qb0, nbk = s0 // B, -(-(s0 + c) // B)
+        assert (sk[:, :qb0] == 3.0).all() and (sv[:, :qb0] == 3.0).all()
+        assert (sk[:, nbk:] == 3.0).all()
+        assert np.array_equal(sk[:, qb0:nbk].cpu().numpy(), whole["k_bar"][:, qb0:nbk])
+        assert np.array_equal(sv[:, qb0:nbk].cpu().numpy(), whole["v_bar"][:, qb0:nbk])
+        assert np.array_equal(bufs.out.float().cpu().numpy(), whole["out"][s0:s0 + c])
+        assert np.array_equal(bufs.lse.cpu().numpy(), whole["lse"][:, s0:s0 + c])
+    assert np.array_equal(kbar.cpu().numpy(), whole["k_bar"])
