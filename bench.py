@@ -75,12 +75,16 @@ def parse():
     ap.add_argument("--seq-len", type=int, default=None,
                     help="override the sequence length of a single-request workload (same recipe and seed)")
     ap.add_argument("--alpha", type=float, default=None)
+    ap.add_argument("--kv-heads", type=int, default=None,
+                    help="one GPU's share under head sharding: this many KV heads (same GQA ratio)")
     ap.add_argument("--sink", type=int, default=0, help="forced keep: first key blocks of each request")
     ap.add_argument("--window", type=int, default=0, help="forced keep: key blocks left of the diagonal")
     ap.add_argument("--last-n", type=int, default=0, help="forced keep: dense last query blocks")
     ap.add_argument("--no-mean-correction", action="store_true", help="drop pruned blocks (the ablation)")
     ap.add_argument("--chunk", type=int, default=0,
                     help="chunked prefill: run the prompt as consecutive chunks of this many queries")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="split-KV parts per attention row (0: the library's automatic choice)")
     ap.add_argument("--chunk-repool", action="store_true",
                     help="with --chunk: pool every key block so far in each chunk (no reuse)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -219,14 +223,14 @@ def run_chunked(args, wl, fp, torch, q, k, v, descales):
     starts = list(range(0, L, C))
     dt = fp.FP_FP8_E4M3 if wl.dtype == "fp8" else fp.FP_BF16
     sel = fp.select_args(wl.alpha, wl.sel_scale, wl.min_sparse_len, args.sink, args.window, args.last_n)
-    att = fp.attn_args(0.0, not args.no_mean_correction)
+    att = fp.attn_args(0.0, not args.no_mean_correction, args.splits)
     NB = -(-L // wl.block_size)
     jobs = []
     for s0 in starts:
         c = min(C, L - s0)
         prob = fp.Problem([0, c], wl.num_q_heads, wl.num_kv_heads, wl.block_size, wl.head_dim, dt, descales,
                           cu_seqlens_k=[0, s0 + c], pooled_pitch=NB)
-        jobs.append((s0, c, prob, fp.Buffers(prob, q.device)))
+        jobs.append((s0, c, prob, fp.Buffers(prob, q.device, attn=att)))
     # one k_bar / v_bar for the whole prompt: each chunk pools only its own key
     # blocks into it (unless --chunk-repool, which pools every block so far)
     k_bar, v_bar = jobs[0][3].k_bar, jobs[0][3].v_bar
@@ -286,6 +290,7 @@ def run_chunked(args, wl, fp, torch, q, k, v, descales):
         "data": "synthetic",
         "config": {"workload": wl.name, "seq_lens": wl.seqlens, "chunk_tokens": C, "chunks": len(jobs),
                    "chunk_pooling": "repool" if args.chunk_repool else "reuse",
+                   "num_splits": [fp.attn_num_splits(j[2], att) for j in jobs],
                    "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads, "block_size": wl.block_size,
                    "alpha": wl.alpha, "mean_correction": not args.no_mean_correction,
                    "kept_fraction": nnz / max(pairs, 1), "nnz": nnz},
@@ -318,6 +323,10 @@ def main():
 
     t0 = time.perf_counter()
     over = {} if args.alpha is None else {"alpha": args.alpha}
+    if args.kv_heads is not None:
+        base = synth.CONFIGS[args.workload]
+        over["Hkv"] = args.kv_heads
+        over["Hq"] = args.kv_heads * (base["Hq"] // base["Hkv"])
     if args.seq_len is not None:
         over["L"] = args.seq_len
         over["n_planted"] = max(1, args.seq_len // 2048)  # the recipe's one planted block per 2048 tokens
@@ -339,9 +348,9 @@ def main():
     prob = fp.Problem(wl.cu_seqlens, wl.num_q_heads, wl.num_kv_heads, wl.block_size, wl.head_dim,
                       fp.FP_FP8_E4M3 if wl.dtype == "fp8" else fp.FP_BF16, descales, table,
                       wl.page_size, k.shape[0] if wl.paged else 0)
-    bufs = fp.Buffers(prob, dev)
+    att = fp.attn_args(0.0, not args.no_mean_correction, args.splits)
+    bufs = fp.Buffers(prob, dev, attn=att)
     sel = fp.select_args(wl.alpha, wl.sel_scale, wl.min_sparse_len, args.sink, args.window, args.last_n)
-    att = fp.attn_args(0.0, not args.no_mean_correction)
     torch.cuda.synchronize()
 
     def step(ev=None):
@@ -387,7 +396,7 @@ def main():
     dense_ms = None
     if not args.no_dense:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        dws = fp.attn_workspace_bytes(prob, False)
+        dws = fp.attn_workspace_bytes(prob, False, att)
         dws = torch.empty(dws, dtype=torch.uint8, device="cuda:0") if dws else None
         fp.dense_prefill(prob, att, q, k, v, bufs.out, bufs.lse, dws)
         torch.cuda.synchronize()
@@ -420,6 +429,7 @@ def main():
             "alpha": wl.alpha,
             "forced_keep_blocks": {"sink": args.sink, "window": args.window, "last_n": args.last_n},
             "mean_correction": not args.no_mean_correction,
+            "num_splits": fp.attn_num_splits(prob, att),
             "sel_scale": wl.sel_scale,
             "min_sparse_len": wl.min_sparse_len,
             "paged": wl.paged,

@@ -70,7 +70,7 @@ class _SelectArgs(ctypes.Structure):
 
 
 class _AttnArgs(ctypes.Structure):
-    _fields_ = [("sm_scale", ctypes.c_float), ("mean_correction", ctypes.c_int32)]
+    _fields_ = [("sm_scale", ctypes.c_float), ("mean_correction", ctypes.c_int32), ("num_splits", ctypes.c_int32)]
 
 
 _lib = None
@@ -92,11 +92,14 @@ def lib() -> ctypes.CDLL:
         L.fp_pool_chunk_blocks.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
         L.fp_select_blocks.argtypes = [P, ctypes.POINTER(_SelectArgs), vp, vp, vp, vp, ctypes.c_int64, vp,
                                        ctypes.c_size_t, vp]
-        L.fp_attn_workspace_bytes.argtypes = [P, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+        L.fp_attn_workspace_bytes.argtypes = [P, ctypes.POINTER(_AttnArgs), ctypes.c_int32,
+                                              ctypes.POINTER(ctypes.c_size_t)]
+        L.fp_attn_num_splits.argtypes = [P, ctypes.POINTER(_AttnArgs), ctypes.POINTER(ctypes.c_int32)]
         L.fp_sparse_prefill.argtypes = [P, ctypes.POINTER(_AttnArgs), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                         ctypes.c_size_t, vp]
         L.fp_dense_prefill.argtypes = [P, ctypes.POINTER(_AttnArgs), vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
-        for f in ("fp_index_shape", "fp_select_workspace_bytes", "fp_attn_workspace_bytes", "fp_validate",
+        for f in ("fp_index_shape", "fp_select_workspace_bytes", "fp_attn_workspace_bytes", "fp_attn_num_splits",
+                  "fp_validate",
                   "fp_pool_blocks", "fp_pool_chunk_blocks", "fp_select_blocks", "fp_sparse_prefill",
                   "fp_dense_prefill"):
             getattr(L, f).restype = ctypes.c_int32
@@ -184,16 +187,25 @@ def select_workspace_bytes(prob: Problem) -> int:
     return n.value
 
 
-def attn_workspace_bytes(prob: Problem, sparse: bool = True) -> int:
+def attn_workspace_bytes(prob: Problem, sparse: bool = True, attn: Optional["_AttnArgs"] = None) -> int:
+    """Attention workspace bytes for these args (None: defaults, automatic split)."""
     n = ctypes.c_size_t()
-    _check(lib().fp_attn_workspace_bytes(prob.ref, 1 if sparse else 0, ctypes.byref(n)))
+    _check(lib().fp_attn_workspace_bytes(prob.ref, ctypes.byref(attn) if attn is not None else None,
+                                         1 if sparse else 0, ctypes.byref(n)))
     return n.value
 
 
-def _attn_workspace(prob: Problem, sparse: bool, workspace, device):
+def attn_num_splits(prob: Problem, attn: Optional["_AttnArgs"] = None) -> int:
+    """The split-KV part count the attention calls use for these args."""
+    n = ctypes.c_int32()
+    _check(lib().fp_attn_num_splits(prob.ref, ctypes.byref(attn) if attn is not None else None, ctypes.byref(n)))
+    return n.value
+
+
+def _attn_workspace(prob: Problem, sparse: bool, workspace, device, attn=None):
     """The caller's workspace, or a fresh torch allocation of the needed size."""
     if workspace is None:
-        n = attn_workspace_bytes(prob, sparse)
+        n = attn_workspace_bytes(prob, sparse, attn)
         if n > 0:
             workspace = torch.empty(n, dtype=torch.uint8, device=device)
     return workspace
@@ -205,8 +217,9 @@ def select_args(alpha: float, sel_scale: float = 1.0, min_sparse_len: int = 0, s
     return _SelectArgs(alpha, sel_scale, min_sparse_len, sink, window, last_n)
 
 
-def attn_args(sm_scale: float = 0.0, mean_correction: bool = True) -> _AttnArgs:
-    return _AttnArgs(sm_scale, 1 if mean_correction else 0)
+def attn_args(sm_scale: float = 0.0, mean_correction: bool = True, num_splits: int = 0) -> _AttnArgs:
+    """fp_attn_args; num_splits 0 = automatic split-KV, 1 = none, k = k parts."""
+    return _AttnArgs(sm_scale, 1 if mean_correction else 0, num_splits)
 
 
 def validate(prob: Problem, sel: Optional[_SelectArgs] = None, attn: Optional[_AttnArgs] = None):
@@ -236,7 +249,7 @@ def sparse_prefill(prob: Problem, attn: _AttnArgs, q, k, v, k_bar, v_bar, row_pt
                    workspace=None, stream=None):
     """fp_sparse_prefill; ``workspace`` (uint8 device tensor of at least
     attn_workspace_bytes(prob, True) bytes) is allocated here when None."""
-    workspace = _attn_workspace(prob, True, workspace, out.device)
+    workspace = _attn_workspace(prob, True, workspace, out.device, attn)
     nbytes = 0 if workspace is None else workspace.numel()
     _check(lib().fp_sparse_prefill(prob.ref, ctypes.byref(attn), _ptr(q), _ptr(k), _ptr(v), _ptr(k_bar),
                                    _ptr(v_bar), _ptr(row_ptr), _ptr(col_idx), _ptr(out), _ptr(lse),
@@ -245,7 +258,7 @@ def sparse_prefill(prob: Problem, attn: _AttnArgs, q, k, v, k_bar, v_bar, row_pt
 
 def dense_prefill(prob: Problem, attn: _AttnArgs, q, k, v, out, lse=None, workspace=None, stream=None):
     """fp_dense_prefill; ``workspace`` as in sparse_prefill (only FP8 needs one)."""
-    workspace = _attn_workspace(prob, False, workspace, out.device)
+    workspace = _attn_workspace(prob, False, workspace, out.device, attn)
     nbytes = 0 if workspace is None else workspace.numel()
     _check(lib().fp_dense_prefill(prob.ref, ctypes.byref(attn), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                                   _ptr(workspace), nbytes, _stream(stream)))
@@ -254,7 +267,7 @@ def dense_prefill(prob: Problem, attn: _AttnArgs, q, k, v, out, lse=None, worksp
 class Buffers:
     """Device buffers of one prefill problem (allocated with torch)."""
 
-    def __init__(self, prob: Problem, device, head_dim: int = 128):
+    def __init__(self, prob: Problem, device, head_dim: int = 128, attn: Optional[_AttnArgs] = None):
         rows, nnz, nbq, nbk = index_shape(prob)
         Hkv = prob.s.num_kv_heads
         T = prob.cu_seqlens[-1]
@@ -267,7 +280,7 @@ class Buffers:
         self.row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=device)
         self.col_idx = torch.empty(max(nnz, 1), dtype=torch.int32, device=device)
         self.workspace = torch.empty(select_workspace_bytes(prob), dtype=torch.uint8, device=device)
-        self.attn_workspace = torch.empty(max(attn_workspace_bytes(prob, True), 1), dtype=torch.uint8,
+        self.attn_workspace = torch.empty(max(attn_workspace_bytes(prob, True, attn), 1), dtype=torch.uint8,
                                           device=device)
         self.out = torch.empty((T, Hq, head_dim), dtype=torch.bfloat16, device=device)
         self.lse = torch.empty((Hq, T), **f32)
@@ -275,13 +288,14 @@ class Buffers:
 
 def run_prefill(prob: Problem, bufs: Buffers, q, k, v, alpha: float, sel_scale: float = 1.0,
                 min_sparse_len: int = 0, sm_scale: float = 0.0, mean_correction: bool = True, stream=None,
-                sink: int = 0, window: int = 0, last_n: int = 0):
-    """All three stages on preallocated buffers (nothing allocated here)."""
+                sink: int = 0, window: int = 0, last_n: int = 0, num_splits: int = 0):
+    """All three stages on preallocated buffers (nothing allocated here; the
+    buffers must have been sized with the same num_splits)."""
     pool_blocks(prob, q, k, v, bufs.q_bar, bufs.k_bar, bufs.v_bar, stream)
     select_blocks(prob, select_args(alpha, sel_scale, min_sparse_len, sink, window, last_n), bufs.q_bar, bufs.k_bar,
                   bufs.row_ptr, bufs.col_idx, bufs.workspace, stream)
-    sparse_prefill(prob, attn_args(sm_scale, mean_correction), q, k, v, bufs.k_bar, bufs.v_bar, bufs.row_ptr,
-                   bufs.col_idx, bufs.out, bufs.lse, bufs.attn_workspace, stream)
+    sparse_prefill(prob, attn_args(sm_scale, mean_correction, num_splits), q, k, v, bufs.k_bar, bufs.v_bar,
+                   bufs.row_ptr, bufs.col_idx, bufs.out, bufs.lse, bufs.attn_workspace, stream)
     return bufs
 
 

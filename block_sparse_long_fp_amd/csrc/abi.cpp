@@ -137,7 +137,31 @@ fp_status check_attn(const fp_attn_args* a) {
   if (!std::isfinite(a->sm_scale) || a->sm_scale < 0.f) return fail(FP_ERR_ARG, "sm_scale must be finite and >= 0");
   if (a->mean_correction != 0 && a->mean_correction != 1)
     return fail(FP_ERR_ARG, "mean_correction=%d must be 0 or 1", a->mean_correction);
+  if (a->num_splits < 0 || a->num_splits > FP_MAX_SPLITS)
+    return fail(FP_ERR_ARG, "num_splits=%d outside [0, %d]", a->num_splits, FP_MAX_SPLITS);
   return FP_OK;
+}
+
+// Split-KV parts per row. Automatic: none when the launch already has a
+// workgroup for each of the 256 CUs (one resident workgroup per CU); else
+// just enough parts to fill them once, at most FP_MAX_SPLITS and at most the
+// longest request's key-block count. Each part costs an fp32 partial output
+// written and read back, so more parts than that lose time (measured:
+// a 128K prompt in 8K chunks on one KV head runs attention 31 % faster with
+// 2 parts, and slower again with 8; 8 KV heads, 256 workgroups or more, only
+// lose by splitting).
+constexpr int64_t kSplitTarget = 256;
+
+int choose_splits(const fp_problem* p, const Shape& s, const fp_attn_args* a) {
+  if (a && a->num_splits > 0) return a->num_splits;
+  const int G = p->num_q_heads / p->num_kv_heads;
+  const int64_t subs = (G * p->block_size + attn_rows_per_wg() - 1) / attn_rows_per_wg();
+  const int64_t wgs = (int64_t)p->num_kv_heads * s.NBq_tot * subs;
+  if (wgs >= kSplitTarget) return 1;
+  int64_t n = (kSplitTarget + wgs - 1) / wgs;
+  if (n > FP_MAX_SPLITS) n = FP_MAX_SPLITS;
+  if (n > s.nb_max) n = s.nb_max;
+  return n < 1 ? 1 : (int)n;
 }
 
 ReqTable make_table(const fp_problem* p, const Shape& s) {
@@ -187,24 +211,32 @@ WsLayout ws_layout(const fp_problem* p, const Shape& s) {
   return w;
 }
 
-// Attention workspace: bf16 k_bar, v_bar (sparse calls) and, for FP8, bf16
-// copies of the K and V codes in the caller's layout.
+// Attention workspace: bf16 k_bar, v_bar (sparse calls), for FP8 bf16 copies
+// of the K and V codes in the caller's layout, and with split-KV the parts'
+// fp32 outputs [splits, Tq, Hq, d] and log2-sum-exps [splits, Tq, Hq].
 struct AttnWs {
-  size_t kbar16, vbar16, kk, vv, total;
+  size_t kbar16, vbar16, kk, vv, opart, lsepart, total;
   int64_t kv_elems;
+  int splits;
 };
 
-AttnWs attn_ws_layout(const fp_problem* p, const Shape& s, bool sparse) {
+AttnWs attn_ws_layout(const fp_problem* p, const Shape& s, bool sparse, int splits) {
   AttnWs w{};
   const int64_t kv_rows = p->kv_layout == FP_KV_PAGED ? (int64_t)p->num_pages * p->page_size : s.Tk;
   w.kv_elems = kv_rows * p->num_kv_heads * p->head_dim;
+  w.splits = splits;
   const size_t pool = sparse ? align256((size_t)p->num_kv_heads * s.kpitch * p->head_dim * 2) : 0;
   const size_t kv = p->dtype == FP_FP8_E4M3 ? align256((size_t)w.kv_elems * 2) : 0;
+  const size_t rows = (size_t)s.Tq * p->num_q_heads;
+  const size_t op = splits > 1 ? align256((size_t)splits * rows * p->head_dim * 4) : 0;
+  const size_t lp = splits > 1 ? align256((size_t)splits * rows * 4) : 0;
   w.kbar16 = 0;
   w.vbar16 = pool;
   w.kk = 2 * pool;
   w.vv = 2 * pool + kv;
-  w.total = 2 * pool + 2 * kv;
+  w.opart = 2 * pool + 2 * kv;
+  w.lsepart = w.opart + op;
+  w.total = w.lsepart + lp;
   return w;
 }
 
@@ -239,12 +271,23 @@ fp_status fp_select_workspace_bytes(const fp_problem* p, size_t* bytes) {
   return ok();
 }
 
-fp_status fp_attn_workspace_bytes(const fp_problem* p, int32_t sparse, size_t* bytes) {
+fp_status fp_attn_workspace_bytes(const fp_problem* p, const fp_attn_args* attn, int32_t sparse, size_t* bytes) {
   Shape s;
   fp_status st = check_problem(p, &s);
   if (st) return st;
+  if (attn && (st = check_attn(attn))) return st;
   if (!bytes) return fail(FP_ERR_NULL, "bytes is NULL");
-  *bytes = attn_ws_layout(p, s, sparse != 0).total;
+  *bytes = attn_ws_layout(p, s, sparse != 0, choose_splits(p, s, attn)).total;
+  return ok();
+}
+
+fp_status fp_attn_num_splits(const fp_problem* p, const fp_attn_args* attn, int32_t* splits) {
+  Shape s;
+  fp_status st = check_problem(p, &s);
+  if (st) return st;
+  if (attn && (st = check_attn(attn))) return st;
+  if (!splits) return fail(FP_ERR_NULL, "splits is NULL");
+  *splits = choose_splits(p, s, attn);
   return ok();
 }
 
@@ -337,7 +380,7 @@ static fp_status run_attention(const fp_problem* p, const fp_attn_args* attn, co
     if (attn->mean_correction && (!k_bar || !v_bar))
       return fail(FP_ERR_NULL, "fp_sparse_prefill: mean correction needs k_bar and v_bar");
   }
-  const AttnWs aw = attn_ws_layout(p, s, !dense);
+  const AttnWs aw = attn_ws_layout(p, s, !dense, choose_splits(p, s, attn));
   if (aw.total > 0 && (!workspace || workspace_bytes < aw.total))
     return fail(FP_ERR_WORKSPACE, "attention workspace %zu bytes < %zu needed", workspace ? workspace_bytes : (size_t)0,
                 aw.total);
@@ -363,6 +406,9 @@ static fp_status run_attention(const fp_problem* p, const fp_attn_args* attn, co
   ap.mean_correction = dense ? 0 : attn->mean_correction;
   ap.dense = dense ? 1 : 0;
   ap.subs = (ap.G * ap.B + attn_rows_per_wg() - 1) / attn_rows_per_wg();
+  ap.splits = aw.splits;
+  ap.o_part = aw.splits > 1 ? reinterpret_cast<float*>(ws + aw.opart) : nullptr;
+  ap.lse_part = aw.splits > 1 ? reinterpret_cast<float*>(ws + aw.lsepart) : nullptr;
   ap.fp8 = p->dtype == FP_FP8_E4M3;
   ap.kv = make_kv(p);
   ap.rt = make_table(p, s);

@@ -48,6 +48,12 @@
 //   * Workgroups run heaviest first (query block index descending over the
 //     ragged batch), and consecutive ids cycle over KV heads so the
 //     round-robin XCD dispatch spreads each head's K/V over the L2s.
+//   * Split-KV ([digest] Table 7: count-balanced CSR splits): when a launch
+//     has too few rows to fill the chip, each row's item list is cut into
+//     `splits` consecutive parts of equal cost (an exact block counts 2, a
+//     64-column correction chunk 1), one workgroup per part. A part writes its
+//     normalised fp32 output and its log2-sum-exp to the workspace, and
+//     merge_kernel combines the parts by their log-sum-exp.
 #include "common.h"
 #include "launch.h"
 
@@ -262,15 +268,17 @@ __device__ __forceinline__ void attend_item(WaveState<BLK>& ws, const uint8_t* k
 }
 
 // blockIdx -> (key block I of a query block, request r) in descending-I order
-// over the ragged batch, plus (kv head, sub-tile). Request r's query blocks
-// are its key blocks qb0 .. NBk - 1 (all of them in a whole prefill).
-__device__ __forceinline__ void decode_work(const AttnParams& p, int& I, int& r, int& h, int& sub) {
+// over the ragged batch, plus (kv head, sub-tile, split). Request r's query
+// blocks are its key blocks qb0 .. NBk - 1 (all of them in a whole prefill).
+__device__ __forceinline__ void decode_work(const AttnParams& p, int& I, int& r, int& h, int& sub, int& split) {
   const ReqTable& rt = p.rt;
-  const int U = p.Hkv * p.subs;
+  const int U = p.Hkv * p.subs * p.splits;
   const int pk = blockIdx.x / U;
   const int rem = blockIdx.x - pk * U;
   h = rem % p.Hkv;
-  sub = rem / p.Hkv;
+  const int rem2 = rem / p.Hkv;
+  sub = rem2 % p.subs;
+  split = rem2 / p.subs;
   // C(x) = number of (r, I') with I' > x; non-increasing. Smallest I with C(I) <= pk.
   auto C = [&](int x) {
     int s = 0;
@@ -358,6 +366,21 @@ __device__ __forceinline__ void issue_item(const AttnParams& p, const RowCtx& rc
       bias[tid] = bv;
     }
   }
+}
+
+// Count-balanced split of a row's items: exact items (the first n_exact)
+// cost 2, correction chunks 1; split s of S takes the items whose cost
+// prefix starts in [s C / S, (s+1) C / S), C the row's total cost.
+__device__ __forceinline__ int item_at_cost(int n_exact, int n_items, int64_t t) {
+  // first item whose cost prefix is >= t
+  if (t <= 2 * (int64_t)n_exact) return (int)((t + 1) / 2);
+  return (int)min((int64_t)n_items, n_exact + (t - 2 * (int64_t)n_exact));
+}
+
+__device__ __forceinline__ void split_range(int n_exact, int n_items, int s, int S, int& e0, int& e1) {
+  const int64_t C = 2 * (int64_t)n_exact + (n_items - n_exact);
+  e0 = item_at_cost(n_exact, n_items, C * s / S);
+  e1 = item_at_cost(n_exact, n_items, C * (s + 1) / S);
 }
 
 // Waits for this wave's tile DMA, then for every wave of the workgroup.
@@ -551,8 +574,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   uint8_t* const vt1 = reinterpret_cast<uint8_t*>(v_lds1);
 
   RowCtx rc;
-  int sub;
-  decode_work(p, rc.I, rc.r, rc.h, sub);
+  int sub, split;
+  decode_work(p, rc.I, rc.r, rc.h, sub, split);
   const ReqTable& rt = p.rt;
   rc.tok_base = rt.ktok_off[rc.r];
   rc.L = rt.ktok_off[rc.r + 1] - rt.ktok_off[rc.r];
@@ -634,20 +657,46 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
     __syncthreads();
   }
 
-  const int N = rc.n_items;
-  // The row's off-diagonal kept blocks run first through an instantiation of
-  // the item code without any score adjustment; the diagonal block and the
-  // correction chunks follow through the general one. Item e always lives in
-  // tile set e & 1.
-  issue_item<BLK, PAGED>(p, rc, colcache, selbits, 0, kt0, vt0, bias0, tid, w, lane, voff_kv, voff_pool);
-  tiles_ready();
-  ItemLoop<BLK, PAGED> L{p, rc, colcache, selbits, kt0, kt1, vt0, vt1, bias0, bias1, N, tid, w, lane,
-                         voff_kv, voff_pool, wave_active, tq0, tq, sl2, lk, lv, hf};
-  L.template run<true>(ws, 0, rc.n_exact - 1);
-  L.template run<false>(ws, rc.n_exact - 1, N);
+  // Items [e0, e1) of this split (all items without split-KV). The row's
+  // off-diagonal kept blocks run first through an instantiation of the item
+  // code without any score adjustment; the diagonal block and the correction
+  // chunks follow through the general one. Item e always lives in tile set
+  // e & 1.
+  int e0 = 0, e1 = rc.n_items;
+  if (p.splits > 1) split_range(rc.n_exact, rc.n_items, split, p.splits, e0, e1);
+  if (e0 < e1) {
+    const bool odd = e0 & 1;
+    issue_item<BLK, PAGED>(p, rc, colcache, selbits, e0, odd ? kt1 : kt0, odd ? vt1 : vt0, odd ? bias1 : bias0,
+                           tid, w, lane, voff_kv, voff_pool);
+    tiles_ready();
+    ItemLoop<BLK, PAGED> L{p, rc, colcache, selbits, kt0, kt1, vt0, vt1, bias0, bias1, e1, tid, w, lane,
+                           voff_kv, voff_pool, wave_active, tq0, tq, sl2, lk, lv, hf};
+    L.template run<true>(ws, e0, min(e1, rc.n_exact - 1));
+    L.template run<false>(ws, max(e0, rc.n_exact - 1), e1);
+  }
 
   if (!wave_active) return;
   const float l_tot = sum_halves(ws.l);
+  if (p.splits > 1) {
+    // Partial result of this split: o / l and log2(l) + m (-inf when the
+    // split saw no key), in the workspace for merge_kernel.
+    if (q_valid) {
+      const int64_t prow = ((int64_t)split * p.T + tok) * p.Hq + g;
+      const float inv = l_tot > 0.f ? oscale / l_tot : 0.f;
+      float* orow = p.o_part + prow * kHeadDim;
+#pragma unroll
+      for (int dt = 0; dt < kHeadDim / 32; ++dt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float4 v = make_float4(ws.o[dt][4 * i + 0] * inv, ws.o[dt][4 * i + 1] * inv,
+                                       ws.o[dt][4 * i + 2] * inv, ws.o[dt][4 * i + 3] * inv);
+          *reinterpret_cast<float4*>(orow + dt * 32 + i * 8 + hf * 4) = v;
+        }
+      }
+      if (hf == 0) p.lse_part[prow] = l_tot > 0.f ? ws.m + __log2f(l_tot) : -INFINITY;
+    }
+    return;
+  }
   if (q_valid) {
     const float inv = oscale / l_tot;
     uint16_t* orow = p.out + (tok * p.Hq + g) * kHeadDim;
@@ -701,6 +750,42 @@ __global__ __launch_bounds__(256) void prep_kernel(AttnParams p, int64_t n_pool8
   }
 }
 
+// Split-KV merge: for each (query token, query head), the parts' log2-sum-
+// exps L_s give weights 2^(L_s - M) / sum_s 2^(L_s - M); O is the weighted
+// sum of the parts' normalised outputs (bf16 out) and LSE = (M + log2 of the
+// weight sum) * ln 2. 32 lanes per row, four dims each.
+__global__ __launch_bounds__(256) void merge_kernel(AttnParams p) {
+  const int64_t rows = (int64_t)p.T * p.Hq;
+  const int64_t row = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  const int c = (threadIdx.x & 31) * 4;
+  if (row >= rows) return;
+  float M = -INFINITY;
+  for (int s = 0; s < p.splits; ++s) M = fmaxf(M, p.lse_part[(int64_t)s * rows + row]);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float wsum = 0.f;
+  for (int s = 0; s < p.splits; ++s) {
+    const float ls = p.lse_part[(int64_t)s * rows + row];
+    if (ls == -INFINITY) continue;
+    const float wgt = __builtin_amdgcn_exp2f(ls - M);
+    const float4 o = *reinterpret_cast<const float4*>(p.o_part + ((int64_t)s * rows + row) * kHeadDim + c);
+    acc.x = fmaf(wgt, o.x, acc.x);
+    acc.y = fmaf(wgt, o.y, acc.y);
+    acc.z = fmaf(wgt, o.z, acc.z);
+    acc.w = fmaf(wgt, o.w, acc.w);
+    wsum += wgt;
+  }
+  const float inv = 1.f / wsum;
+  uint2 pk;
+  pk.x = pack_bf16x2(acc.x * inv, acc.y * inv);
+  pk.y = pack_bf16x2(acc.z * inv, acc.w * inv);
+  *reinterpret_cast<uint2*>(p.out + row * kHeadDim + c) = pk;
+  if (p.lse != nullptr && c == 0) {
+    const int64_t tok = row / p.Hq;
+    const int g = (int)(row % p.Hq);
+    p.lse[(int64_t)g * p.T + tok] = (M + __log2f(wsum)) * kLn2;
+  }
+}
+
 template <int BLK>
 void launch_attn_t(const AttnParams& p, dim3 grid, hipStream_t stream) {
   if (p.kv.paged) hipLaunchKernelGGL((attn_kernel<BLK, true>), grid, dim3(kThreads), 0, stream, p);
@@ -719,10 +804,16 @@ hipError_t launch_attn(const AttnParams& p, hipStream_t stream) {
     const int blocks = (int)(work < 8192 * 256 ? (work + 255) / 256 : 8192);
     hipLaunchKernelGGL(prep_kernel, dim3(blocks), dim3(256), 0, stream, p, n_pool8, n_kv8);
   }
-  const int64_t wgs = (int64_t)p.Hkv * p.NBq_tot * p.subs;
+  const int64_t wgs = (int64_t)p.Hkv * p.NBq_tot * p.subs * p.splits;
   dim3 grid((unsigned)wgs);
   if (p.B == 128) launch_attn_t<128>(p, grid, stream);
   else launch_attn_t<64>(p, grid, stream);
+  if (p.splits > 1) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t rows = (int64_t)p.T * p.Hq;
+    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((rows + 7) / 8)), dim3(256), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

@@ -69,6 +69,9 @@ struct AttnParams {
   int32_t mean_correction;
   int32_t dense;        // 1: ignore the CSR, attend to every causal block
   int32_t subs;         // workgroups per (h, I) row: ceil(G * B / rows_per_wg)
+  int32_t splits;       // split-KV parts per row (1: no split)
+  float* o_part;        // workspace (splits > 1): [splits, T, Hq, d] normalised partial outputs
+  float* lse_part;      // workspace (splits > 1): [splits, T, Hq] partial log2-sum-exps
   int32_t fp8;
   KVAddr kv;
   ReqTable rt;

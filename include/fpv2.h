@@ -78,7 +78,7 @@
 extern "C" {
 #endif
 
-#define FPV2_ABI_VERSION 5
+#define FPV2_ABI_VERSION 6
 
 /* Status codes. */
 typedef int32_t fp_status;
@@ -158,7 +158,13 @@ typedef struct fp_attn_args {
   int32_t mean_correction;       /* 1: each pruned causal block J < I adds the     */
                                  /* logit sm*q.k_bar_J + ln n_J on value v_bar_J;  */
                                  /* 0: pruned blocks are dropped (the ablation)    */
+  int32_t num_splits;            /* split-KV parts per row ([digest] Table 7:      */
+                                 /* count-balanced CSR splits), 0 .. FP_MAX_SPLITS; */
+                                 /* 0 = chosen from the problem's size (more parts */
+                                 /* when a launch has few rows), 1 = no split      */
 } fp_attn_args;
+
+#define FP_MAX_SPLITS 16
 
 /* Host-only queries (no GPU needed). */
 
@@ -173,10 +179,16 @@ fp_status fp_index_shape(const fp_problem* p, int64_t* num_rows, int64_t* max_nn
 fp_status fp_select_workspace_bytes(const fp_problem* p, size_t* bytes);
 
 /* Bytes of DEVICE workspace fp_sparse_prefill (sparse = 1) or fp_dense_prefill
- * (sparse = 0) needs: bf16 copies of k_bar and v_bar for the correction
- * (sparse only), and for FP8 bf16 copies of the K and V codes (exact). 0 for
- * a dense bf16 problem. */
-fp_status fp_attn_workspace_bytes(const fp_problem* p, int32_t sparse, size_t* bytes);
+ * (sparse = 0) needs with these attention args (NULL: defaults, automatic
+ * split): bf16 copies of k_bar and v_bar for the correction (sparse only), for
+ * FP8 bf16 copies of the K and V codes (exact), and with split-KV the parts'
+ * fp32 outputs and log-sum-exps. 0 for an unsplit dense bf16 problem. */
+fp_status fp_attn_workspace_bytes(const fp_problem* p, const fp_attn_args* attn, int32_t sparse,
+                                  size_t* bytes);
+
+/* The split-KV part count the attention calls will use for these args
+ * (resolves num_splits = 0). */
+fp_status fp_attn_num_splits(const fp_problem* p, const fp_attn_args* attn, int32_t* splits);
 
 /* Validate a problem and (optionally, may be NULL) selection/attention args
  * exactly as the compute calls do, without touching any device pointer. */
@@ -226,7 +238,7 @@ fp_status fp_select_blocks(const fp_problem* p, const fp_select_args* sel, const
  * mean_correction = 1). row_ptr, col_idx: DEVICE CSR from fp_select_blocks
  * (or any CSR of the same shape with the diagonal in every row).
  * out: DEVICE bf16 [Tq, Hq, d]. lse: DEVICE fp32 [Hq, Tq], or NULL to skip.
- * workspace: DEVICE scratch of at least fp_attn_workspace_bytes(p, 1) bytes
+ * workspace: DEVICE scratch of at least fp_attn_workspace_bytes(p, attn, 1) bytes
  * (may be NULL when that is 0); contents on entry do not matter, garbage on
  * exit; the call must not overlap another call using the same workspace. */
 fp_status fp_sparse_prefill(const fp_problem* p, const fp_attn_args* attn, const void* q,
@@ -236,7 +248,7 @@ fp_status fp_sparse_prefill(const fp_problem* p, const fp_attn_args* attn, const
 
 /* Dense causal attention over every key at or before each query (the comparator
  * for the sparse path; mean_correction is ignored). Same layouts as above;
- * workspace as above with fp_attn_workspace_bytes(p, 0). */
+ * workspace as above with fp_attn_workspace_bytes(p, attn, 0). */
 fp_status fp_dense_prefill(const fp_problem* p, const fp_attn_args* attn, const void* q,
                            const void* k, const void* v, void* out, float* lse, void* workspace,
                            size_t workspace_bytes, void* stream);

@@ -34,6 +34,9 @@ def test_exports_every_declared_symbol():
     assert fp.lib().fp_abi_version() == ver
 
 
+ONE = fp.attn_args(num_splits=1) if os.path.exists(fp.LIB_PATH) else None   # no split-KV
+
+
 def _prob(**kw):
     base = dict(cu_seqlens=[0, 1000, 3000], num_q_heads=32, num_kv_heads=8, block_size=128)
     base.update(kw)
@@ -45,12 +48,12 @@ def test_attention_workspace_sizes():
         return (x + 255) // 256 * 256
     p = _prob()
     nb, T, Hkv, d = 24, 3000, 8, 128
-    assert fp.attn_workspace_bytes(p, True) == 2 * a256(Hkv * nb * d * 2)
-    assert fp.attn_workspace_bytes(p, False) == 0
+    assert fp.attn_workspace_bytes(p, True, ONE) == 2 * a256(Hkv * nb * d * 2)
+    assert fp.attn_workspace_bytes(p, False, ONE) == 0
     ds = [torch.ones(1) for _ in range(3)]
     p8 = _prob(dtype=fp.FP_FP8_E4M3, descales=ds)
-    assert fp.attn_workspace_bytes(p8, True) == 2 * a256(Hkv * nb * d * 2) + 2 * a256(T * Hkv * d * 2)
-    assert fp.attn_workspace_bytes(p8, False) == 2 * a256(T * Hkv * d * 2)
+    assert fp.attn_workspace_bytes(p8, True, ONE) == 2 * a256(Hkv * nb * d * 2) + 2 * a256(T * Hkv * d * 2)
+    assert fp.attn_workspace_bytes(p8, False, ONE) == 2 * a256(T * Hkv * d * 2)
 
 
 def test_index_shape_and_workspace():
@@ -72,11 +75,39 @@ def test_chunked_index_shape():
     assert nnz == 8 * (sum(16 + i + 1 for i in range(8)) + 5 * 6 // 2)
     def a256(x):
         return (x + 255) // 256 * 256
-    assert fp.attn_workspace_bytes(p, True) == 2 * a256(8 * nbk * 128 * 2)
+    assert fp.attn_workspace_bytes(p, True, ONE) == 2 * a256(8 * nbk * 128 * 2)
     ds = [torch.ones(1) for _ in range(3)]
     p8 = _prob(cu_seqlens=[0, 1000, 1640], cu_seqlens_k=[0, 3048, 3688], dtype=fp.FP_FP8_E4M3, descales=ds)
     # FP8 copies cover every key token (Tk = 3688), not only the chunk
-    assert fp.attn_workspace_bytes(p8, False) == 2 * a256(3688 * 8 * 128 * 2)
+    assert fp.attn_workspace_bytes(p8, False, ONE) == 2 * a256(3688 * 8 * 128 * 2)
+
+
+def test_split_kv_choice_and_workspace():
+    def a256(x):
+        return (x + 255) // 256 * 256
+    # 8 KV heads x 24 query blocks x 2 workgroups per row = 384 workgroups
+    # fill the 256 CUs: no split. 2 KV heads: 96 workgroups, so 3 parts; the
+    # workspace gains the parts' fp32 outputs and log-sum-exps
+    assert fp.attn_num_splits(_prob()) == 1
+    p = _prob(num_q_heads=8, num_kv_heads=2)
+    assert fp.attn_num_splits(p) == 3 and fp.attn_num_splits(p, fp.attn_args(num_splits=5)) == 5
+    T, Hq = 3000, 8
+    base = fp.attn_workspace_bytes(p, True, ONE)
+    assert base == 2 * a256(2 * 24 * 128 * 2)
+    assert fp.attn_workspace_bytes(p, True) == base + a256(3 * T * Hq * 128 * 4) + a256(3 * T * Hq * 4)
+    assert fp.attn_workspace_bytes(p, False) == a256(3 * T * Hq * 128 * 4) + a256(3 * T * Hq * 4)
+    # a 128K prompt has enough rows: no split; a one-block problem cannot split
+    assert fp.attn_num_splits(_prob(cu_seqlens=[0, 131072])) == 1
+    assert fp.attn_num_splits(_prob(cu_seqlens=[0, 100])) == 1
+    # 16 at most; out of range is rejected
+    assert fp.attn_num_splits(_prob(cu_seqlens=[0, 4096], num_q_heads=1, num_kv_heads=1, block_size=64)) == 4
+    assert fp.attn_num_splits(_prob(cu_seqlens=[0, 8192], num_q_heads=1, num_kv_heads=1)) == 4
+    assert fp.attn_num_splits(_prob(cu_seqlens=[0, 4000], num_q_heads=1, num_kv_heads=1, block_size=64)) == 5
+    assert fp.attn_num_splits(_prob(cu_seqlens=[0, 1024], num_q_heads=1, num_kv_heads=1, block_size=64)) == 16
+    for bad in (-1, 17):
+        with pytest.raises(fp.FpError) as e:
+            fp.validate(p, None, fp.attn_args(num_splits=bad))
+        assert e.value.code == 9
 
 
 def test_pooled_pitch():
@@ -87,7 +118,7 @@ def test_pooled_pitch():
     assert e.value.code == 2
     def a256(x):
         return (x + 255) // 256 * 256
-    assert fp.attn_workspace_bytes(_prob(pooled_pitch=100), True) == 2 * a256(8 * 100 * 128 * 2)
+    assert fp.attn_workspace_bytes(_prob(pooled_pitch=100), True, ONE) == 2 * a256(8 * 100 * 128 * 2)
     b = fp.Problem([0, 1000], 32, 8, 128, cu_seqlens_k=[0, 3048], pooled_pitch=40)
     assert fp.index_shape(b)[2:] == (8, 24)
 
@@ -185,8 +216,8 @@ def test_compute_calls_reject_before_launch():
     assert L.fp_select_blocks(p.ref, ctypes.byref(sel), fake, fake, fake, fake, nnz - 1, fake, ws, None) == 7
     assert L.fp_select_blocks(p.ref, ctypes.byref(sel), fake, fake, fake, fake, nnz, fake, ws - 1, None) == 8
     assert L.fp_select_blocks(p.ref, ctypes.byref(sel), fake, fake, fake, fake, nnz, None, ws, None) == 8
-    aws = fp.attn_workspace_bytes(p, True)
-    assert aws > 0 and fp.attn_workspace_bytes(p, False) == 0  # bf16: only the pooled copies
+    aws = fp.attn_workspace_bytes(p, True, ONE)
+    assert aws > 0 and fp.attn_workspace_bytes(p, False, ONE) == 0  # bf16: only the pooled copies
     assert L.fp_sparse_prefill(p.ref, ctypes.byref(attn), fake, fake, fake, None, fake, fake, fake, fake, None,
                                fake, aws, None) == 1
     assert L.fp_sparse_prefill(p.ref, ctypes.byref(attn), fake, fake, fake, fake, fake, None, fake, fake, None,

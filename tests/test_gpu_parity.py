@@ -17,11 +17,12 @@ import oracle
 pytestmark = pytest.mark.gpu
 
 
-def _check_full(wl, alpha=None, mean_correction=True, paged=None, min_sparse_len=None, forced=None):
+def _check_full(wl, alpha=None, mean_correction=True, paged=None, min_sparse_len=None, forced=None, num_splits=0):
     print(f"[parity] {wl.name} L={wl.seqlens} Lk={wl.key_seqlens} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} B={wl.block_size} "
           f"dtype={wl.dtype} alpha={alpha if alpha is not None else wl.alpha} mc={mean_correction} "
           f"paged={paged if paged is not None else wl.paged} forced={forced}", flush=True)
-    gpu = run_gpu(wl, alpha, mean_correction, paged, min_sparse_len=min_sparse_len, forced=forced)
+    gpu = run_gpu(wl, alpha, mean_correction, paged, min_sparse_len=min_sparse_len, forced=forced,
+                  num_splits=num_splits)
     orc = run_oracle(wl, alpha, mean_correction, do_attend=False, paged=paged, min_sparse_len=min_sparse_len,
                      forced=forced)
     compare_pooled(gpu, orc)
@@ -99,9 +100,10 @@ def test_paged_equals_contiguous_bitwise():
 
 
 def test_alpha_zero_sparse_equals_dense_kernel_and_oracle():
+    # unsplit, so both calls process each row's key blocks in one sequence
     wl = synth.make_workload("llama_32k", L=1800, Hq=8, Hkv=2, n_planted=4)
-    sp = run_gpu(wl, alpha=0.0)
-    dn = run_gpu(wl, dense=True)
+    sp = run_gpu(wl, alpha=0.0, num_splits=1)
+    dn = run_gpu(wl, dense=True, num_splits=1)
     nb = -(-1800 // 128)
     assert sp["row_ptr"][-1] == 2 * nb * (nb + 1) // 2
     assert np.array_equal(sp["out"], dn["out"]) and np.array_equal(sp["lse"], dn["lse"])
@@ -204,9 +206,9 @@ def test_chunked_rows_equal_whole_prefill_bitwise():
     the same items in the same order as in one prefill of the whole prompt,
     so the GPU path gives bitwise the same outputs for them."""
     wl = synth.make_workload("llama_32k", L=3000, Hq=8, Hkv=2, n_planted=6)
-    whole = run_gpu(wl)
+    whole = run_gpu(wl, num_splits=1)
     B, start = wl.block_size, 1536
-    ch = run_gpu(synth.chunk_of(wl, start, 4096))
+    ch = run_gpu(synth.chunk_of(wl, start, 4096), num_splits=1)
     assert np.array_equal(ch["out"], whole["out"][start:])
     assert np.array_equal(ch["lse"], whole["lse"][:, start:])
     assert np.array_equal(ch["k_bar"], whole["k_bar"]) and np.array_equal(ch["v_bar"], whole["v_bar"])
@@ -226,7 +228,7 @@ def test_chunk_pooling_reuses_earlier_blocks():
     selected and attended, gives bitwise the whole prefill's outputs."""
     import block_sparse_long_fp_amd as fp
     wl = synth.make_workload("llama_32k", L=3000, Hq=8, Hkv=2, n_planted=6)
-    whole = run_gpu(wl)
+    whole = run_gpu(wl, num_splits=1)
     B, C, L = wl.block_size, 1024, 3000
     NB = -(-L // B)
     dev = "cuda:0"
@@ -245,8 +247,8 @@ def test_chunk_pooling_reuses_earlier_blocks():
         fp.pool_chunk_blocks(prob, q[s0:s0 + c], k, v, bufs.q_bar, kbar, vbar)
         fp.select_blocks(prob, fp.select_args(wl.alpha), bufs.q_bar, kbar, bufs.row_ptr, bufs.col_idx,
                          bufs.workspace)
-        fp.sparse_prefill(prob, fp.attn_args(), q[s0:s0 + c], k, v, kbar, vbar, bufs.row_ptr, bufs.col_idx,
-                          bufs.out, bufs.lse, bufs.attn_workspace)
+        fp.sparse_prefill(prob, fp.attn_args(num_splits=1), q[s0:s0 + c], k, v, kbar, vbar, bufs.row_ptr,
+                          bufs.col_idx, bufs.out, bufs.lse, bufs.attn_workspace)
         torch.cuda.synchronize()
         qb0, nbk = s0 // B, -(-(s0 + c) // B)
         assert (sk[:, :qb0] == 3.0).all() and (sv[:, :qb0] == 3.0).all()
@@ -256,3 +258,34 @@ def test_chunk_pooling_reuses_earlier_blocks():
         assert np.array_equal(bufs.out.float().cpu().numpy(), whole["out"][s0:s0 + c])
         assert np.array_equal(bufs.lse.cpu().numpy(), whole["lse"][:, s0:s0 + c])
     assert np.array_equal(kbar.cpu().numpy(), whole["k_bar"])
+
+
+# ---------------------------------------------------------------- split-KV
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7])
+def test_split_kv_parts(splits):
+    """[digest] Table 7, count-balanced CSR splits: each row's items cut into
+    parts of equal cost, merged by log-sum-exp; any part count gives the
+    oracle's result (parts with no key leave their weight at zero)."""
+    wl = synth.make_workload("llama_32k", L=2700, Hq=8, Hkv=2, n_planted=6)
+    _check_full(wl, num_splits=splits)
+
+
+def test_split_kv_close_to_unsplit_and_dense():
+    wl = synth.make_workload("llama_32k", L=2000, Hq=4, Hkv=1, n_planted=4)
+    a = run_gpu(wl, num_splits=1)
+    b = run_gpu(wl, num_splits=5)
+    assert np.array_equal(a["col_idx"], b["col_idx"])
+    assert np.abs(a["out"] - b["out"]).max() <= 1e-2
+    assert np.abs(a["lse"] - b["lse"]).max() <= 1e-4 * max(1.0, np.abs(a["lse"]).max())
+    dn = run_gpu(wl, dense=True, num_splits=4)
+    orc = run_oracle(wl, alpha=0.0)
+    compare_outputs(dn["out"], dn["lse"], orc.O, orc.LSE, O_TOL["bf16"])
+
+
+def test_split_kv_chunk_paged_fp8():
+    wl = synth.make_workload("qwen4b_varlen_paged", lengths=[2900, 1500], Hq=8, Hkv=2, min_sparse_len=0,
+                             page_size=48, n_planted=3)
+    _check_full(synth.chunk_of(wl, 1024, 1024), num_splits=4)
+    wl8 = synth.make_workload("qwen30b_128k_fp8", L=3500, Hq=16, Hkv=2, n_planted=6)
+    _check_full(synth.chunk_of(wl8, 2560, 2048), num_splits=3)
