@@ -75,6 +75,7 @@ def parse():
     ap.add_argument("--seq-len", type=int, default=None,
                     help="override the sequence length of a single-request workload (same recipe and seed)")
     ap.add_argument("--alpha", type=float, default=None)
+    ap.add_argument("--block-size", type=int, default=None, help="override the workload's block size (64 or 128)")
     ap.add_argument("--kv-heads", type=int, default=None,
                     help="one GPU's share under head sharding: this many KV heads (same GQA ratio)")
     ap.add_argument("--sink", type=int, default=0, help="forced keep: first key blocks of each request")
@@ -323,6 +324,8 @@ def main():
 
     t0 = time.perf_counter()
     over = {} if args.alpha is None else {"alpha": args.alpha}
+    if args.block_size is not None:
+        over["B"] = args.block_size
     if args.kv_heads is not None:
         base = synth.CONFIGS[args.workload]
         over["Hkv"] = args.kv_heads

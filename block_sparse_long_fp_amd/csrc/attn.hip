@@ -64,6 +64,7 @@ namespace {
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kRowsPerWG = kWaves * 32;
+constexpr int kSlab = 4 * kWaves;       // tile rows one DMA instruction of every wave fills
 constexpr int kPC = 64;                 // pooled columns per correction item
 constexpr int kQuad = 4 * 256 + 64;     // LDS bytes of a group of four 256-byte rows
 constexpr int kColCache = 1024;         // CSR columns cached in LDS
@@ -71,6 +72,18 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegBig = -1.0e30f;
 constexpr float kSlack = 8.0f;          // lazy-rescale threshold of the running max (log2)
+
+// Eight probabilities as one bf16 P operand, added in fp32 to the row sum.
+// (Summing the rounded bf16 values instead, two per v_dot2_f32_bf16, saves
+// 16 VALU instructions per half but moves the log-sum-exp by up to 2^-9
+// relative, outside a 1e-3 bound for rows with few keys.)
+__device__ __forceinline__ bf16x8 pack_probs(const float (&pv)[8], float& lsum) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) lsum += pv[t];
+  const bf16x4 lo = __builtin_convertvector(f32x4{pv[0], pv[1], pv[2], pv[3]}, bf16x4);
+  const bf16x4 hi = __builtin_convertvector(f32x4{pv[4], pv[5], pv[6], pv[7]}, bf16x4);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
@@ -188,17 +201,15 @@ __device__ __forceinline__ void attend_item(WaveState<BLK>& ws, const uint8_t* k
     for (int j = 0; j < kDepth; ++j)
       kf[j] = *reinterpret_cast<const bf16x8*>(kh + (j & 1) * 8 * kQuad + (j >> 1) * 128);
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_setprio(1);
-    f32x16 s[2] = {f32x16{}, f32x16{}};
+    f32x16 s[2];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      s[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j % kDepth], ws.qf[j >> 1], s[j & 1], 0, 0, 0);
+      s[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j % kDepth], ws.qf[j >> 1], j < 2 ? f32x16{} : s[j & 1], 0, 0, 0);
       if (j + kDepth < NJ)
         kf[j % kDepth] =
             *reinterpret_cast<const bf16x8*>(kh + ((j + kDepth) & 1) * 8 * kQuad + ((j + kDepth) >> 1) * 128);
       __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_s_setprio(0);
     // The first V operands load while the softmax runs.
     const uint8_t* vh = vt + lv + (2 * hh) * 8 * kQuad;
     bf16x8 vf[kDepth];
@@ -252,18 +263,12 @@ __device__ __forceinline__ void attend_item(WaveState<BLK>& ws, const uint8_t* k
         float pv[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) pv[t] = __builtin_amdgcn_exp2f(fmaf(s[t2][8 * s2 + t], sc, neg_m));
-#pragma unroll
-        for (int t = 0; t < 8; ++t) lsum += pv[t];
-        const bf16x4 lo = __builtin_convertvector(f32x4{pv[0], pv[1], pv[2], pv[3]}, bf16x4);
-        const bf16x4 hi = __builtin_convertvector(f32x4{pv[4], pv[5], pv[6], pv[7]}, bf16x4);
-        pf[t2][s2] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        pf[t2][s2] = pack_probs(pv, lsum);
       }
     }
     ws.l += lsum;
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_setprio(1);
     pv_jobs<16, kDepth>(ws.o, vf, pf, vh);
-    __builtin_amdgcn_s_setprio(0);
   }
 }
 
@@ -304,8 +309,8 @@ __device__ __forceinline__ void decode_work(const AttnParams& p, int& I, int& r,
 }
 
 // Starts the DMA of item e into one K tile, one V tile and (pooled items) one
-// bias row. Wave w, instruction u writes the 1 KiB group 8u + w of the tile:
-// lane l fetches 16-byte chunk l/4 of tile row 32u + 4w + l%4.
+// bias row. Wave w, instruction u writes the 1 KiB group kWaves u + w of the
+// tile: lane l fetches 16-byte chunk l/4 of tile row kSlab u + 4w + l%4.
 template <int BLK, bool PAGED>
 __device__ __forceinline__ void issue_item(const AttnParams& p, const RowCtx& rc, const int32_t* colcache,
                                            const uint32_t* selbits, int e, uint8_t* kt, uint8_t* vt, float* bias,
@@ -319,28 +324,28 @@ __device__ __forceinline__ void issue_item(const AttnParams& p, const RowCtx& rc
       const uint8_t* kb = static_cast<const uint8_t*>(p.kk) + row0;
       const uint8_t* vb = static_cast<const uint8_t*>(p.vv) + row0;
 #pragma unroll
-      for (int u = 0; u < BLK / 32; ++u) {
-        const int nrec = uniform(min(max(lrem - 32 * u, 0), 32) * rstride);
-        const int64_t du = (int64_t)(32 * u) * rstride;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(kb + du, nrec), (lds_ptr)(kt + (8 * u + w) * kQuad), 16,
-                                                 voff_kv, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(vb + du, nrec), (lds_ptr)(vt + (8 * u + w) * kQuad), 16,
-                                                 voff_kv, 0, 0, 0);
+      for (int u = 0; u < BLK / kSlab; ++u) {
+        const int nrec = uniform(min(max(lrem - kSlab * u, 0), kSlab) * rstride);
+        const int64_t du = (int64_t)(kSlab * u) * rstride;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(kb + du, nrec),
+                                                 (lds_ptr)(kt + (kWaves * u + w) * kQuad), 16, voff_kv, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(vb + du, nrec),
+                                                 (lds_ptr)(vt + (kWaves * u + w) * kQuad), 16, voff_kv, 0, 0, 0);
       }
     } else {
       // Rows past the request repeat its last token (masked by the causal
       // mask of the diagonal item); each lane looks up its row's page.
 #pragma unroll
-      for (int u = 0; u < BLK / 32; ++u) {
-        const int rr = min(32 * u + 4 * w + (lane & 3), lrem - 1);
+      for (int u = 0; u < BLK / kSlab; ++u) {
+        const int rr = min(kSlab * u + 4 * w + (lane & 3), lrem - 1);
         const int t = J * BLK + rr;
         const int page = p.kv.page_table[(int64_t)rc.r * p.kv.max_pages + t / p.kv.page_size];
         const int64_t off = (((int64_t)page * p.kv.page_size + t % p.kv.page_size) * p.Hkv + rc.h) * (kHeadDim * 2) +
                             (lane >> 2) * 16;
         __builtin_amdgcn_global_load_lds((gbl_ptr)(static_cast<const uint8_t*>(p.kk) + off),
-                                         (lds_ptr)(kt + (8 * u + w) * kQuad), 16, 0, 0);
+                                         (lds_ptr)(kt + (kWaves * u + w) * kQuad), 16, 0, 0);
         __builtin_amdgcn_global_load_lds((gbl_ptr)(static_cast<const uint8_t*>(p.vv) + off),
-                                         (lds_ptr)(vt + (8 * u + w) * kQuad), 16, 0, 0);
+                                         (lds_ptr)(vt + (kWaves * u + w) * kQuad), 16, 0, 0);
       }
     }
   } else {
@@ -351,13 +356,13 @@ __device__ __forceinline__ void issue_item(const AttnParams& p, const RowCtx& rc
     const uint8_t* kb = reinterpret_cast<const uint8_t*>(p.kbar16) + row0;
     const uint8_t* vb = reinterpret_cast<const uint8_t*>(p.vbar16) + row0;
 #pragma unroll
-    for (int u = 0; u < kPC / 32; ++u) {
-      const int nrec = uniform(min(max(rc.I - c0 - 32 * u, 0), 32) * (kHeadDim * 2));
-      const int du = 32 * u * (kHeadDim * 2);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(kb + du, nrec), (lds_ptr)(kt + (8 * u + w) * kQuad), 16,
-                                               voff_pool, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(vb + du, nrec), (lds_ptr)(vt + (8 * u + w) * kQuad), 16,
-                                               voff_pool, 0, 0, 0);
+    for (int u = 0; u < kPC / kSlab; ++u) {
+      const int nrec = uniform(min(max(rc.I - c0 - kSlab * u, 0), kSlab) * (kHeadDim * 2));
+      const int du = kSlab * u * (kHeadDim * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(kb + du, nrec), (lds_ptr)(kt + (kWaves * u + w) * kQuad),
+                                               16, voff_pool, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(vb + du, nrec), (lds_ptr)(vt + (kWaves * u + w) * kQuad),
+                                               16, voff_pool, 0, 0, 0);
     }
     if (tid < kPC) {
       const int Jc = c0 + tid;
@@ -411,16 +416,12 @@ __device__ __forceinline__ void qk_half(const bf16x8 (&qf)[kHeadDim / 16], const
 #pragma unroll
   for (int j = 0; j < DEPTH; ++j) kf[j] = k_operand(kh, j);
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_setprio(1);
-  s[0] = f32x16{};
-  s[1] = f32x16{};
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    s[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j % DEPTH], qf[j >> 1], s[j & 1], 0, 0, 0);
+    s[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j % DEPTH], qf[j >> 1], j < 2 ? f32x16{} : s[j & 1], 0, 0, 0);
     if (j + DEPTH < NJ) kf[j % DEPTH] = k_operand(kh, j + DEPTH);
     __builtin_amdgcn_sched_barrier(0);
   }
-  __builtin_amdgcn_s_setprio(0);
 }
 
 // PV of one half interleaved with QK^T of the next: the two MFMA streams
@@ -434,19 +435,15 @@ __device__ __forceinline__ void pv_qk_half(f32x16 (&o)[kHeadDim / 32], bf16x8 (&
   bf16x8 kf[DEPTH];
 #pragma unroll
   for (int j = 0; j < DEPTH; ++j) kf[j] = k_operand(kn, j);
-  sn[0] = f32x16{};
-  sn[1] = f32x16{};
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     o[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j % DEPTH], pf[j >> 3][(j >> 2) & 1], o[j & 3], 0, 0, 0);
     if (j + DEPTH < NJ) vf[j % DEPTH] = v_operand(vh, j + DEPTH);
-    sn[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j % DEPTH], qf[j >> 1], sn[j & 1], 0, 0, 0);
+    sn[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j % DEPTH], qf[j >> 1], j < 2 ? f32x16{} : sn[j & 1], 0, 0, 0);
     if (j + DEPTH < NJ) kf[j % DEPTH] = k_operand(kn, j + DEPTH);
     __builtin_amdgcn_sched_barrier(0);
   }
-  __builtin_amdgcn_s_setprio(0);
 }
 
 // Online-softmax update of one half of exact scores (in score units): new
@@ -477,11 +474,7 @@ __device__ __forceinline__ void softmax_exact(WaveState<BLK>& ws, const f32x16 (
       float pv[8];
 #pragma unroll
       for (int t = 0; t < 8; ++t) pv[t] = __builtin_amdgcn_exp2f(fmaf(s[t2][8 * s2 + t], sl2, neg_m));
-#pragma unroll
-      for (int t = 0; t < 8; ++t) lsum += pv[t];
-      const bf16x4 lo = __builtin_convertvector(f32x4{pv[0], pv[1], pv[2], pv[3]}, bf16x4);
-      const bf16x4 hi = __builtin_convertvector(f32x4{pv[4], pv[5], pv[6], pv[7]}, bf16x4);
-      pf[t2][s2] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      pf[t2][s2] = pack_probs(pv, lsum);
     }
   }
   ws.l += lsum;
@@ -497,6 +490,99 @@ __device__ __forceinline__ void attend_exact(WaveState<BLK>& ws, const uint8_t* 
   constexpr int kDepth = 4;
   f32x16 sb[2][2];
   qk_half<kDepth>(ws.qf, kb + lk, sb[0]);
+#pragma unroll
+  for (int hh = 0; hh < NH; ++hh) {
+    const uint8_t* vh = vt + lv + (2 * hh) * 8 * kQuad;
+    bf16x8 vf[kDepth];
+#pragma unroll
+    for (int j = 0; j < kDepth; ++j) vf[j] = v_operand(vh, j);
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 pf[2][2];
+    softmax_exact(ws, sb[hh & 1], sl2, pf);
+    __builtin_amdgcn_sched_barrier(0);
+    if (hh + 1 < NH)
+      pv_qk_half<kDepth>(ws.o, vf, pf, vh, ws.qf, kb + lk + (2 * hh + 2) * 8 * kQuad, sb[(hh + 1) & 1]);
+    else
+      pv_jobs<16, kDepth>(ws.o, vf, pf, vh);
+  }
+}
+
+// The next kept block's K / V DMA (BLK rows in 32-row slabs, K and V each),
+// prepared after the item barrier and issued one instruction per MFMA during
+// the first QK^T half, so the eight waves do not all stall together while
+// the vector memory unit accepts them (contiguous K / V only).
+struct ItemDma {
+  const uint8_t* kb;
+  const uint8_t* vb;
+  int lrem;  // rows of the block inside the request
+  int rstride;
+  uint32_t voff;
+  uint8_t* kt;
+  uint8_t* vt;
+  int w;
+  // Instruction I: K (I even) or V (I odd) of slab I / 2.
+  template <int I>
+  __device__ __forceinline__ void fire() const {
+    constexpr int u = I >> 1;
+    const int nrec = uniform(min(max(lrem - kSlab * u, 0), kSlab) * rstride);
+    const int64_t du = (int64_t)(kSlab * u) * rstride;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(((I & 1) ? vb : kb) + du, nrec),
+                                             (lds_ptr)(((I & 1) ? vt : kt) + (kWaves * u + w) * kQuad), 16, voff,
+                                             0, 0, 0);
+  }
+};
+
+template <int BLK>
+__device__ __forceinline__ ItemDma prep_block(const AttnParams& p, const RowCtx& rc, const int32_t* colcache, int e,
+                                              uint8_t* kt, uint8_t* vt, int w, uint32_t voff_kv) {
+  const int J = !rc.cols ? e : uniform(e < kColCache ? lload_i32(colcache + e) : gload_i32(rc.cols + e));
+  const int64_t row0 = ((rc.tok_base + (int64_t)J * BLK) * p.Hkv + rc.h) * (kHeadDim * 2);
+  ItemDma d;
+  d.kb = static_cast<const uint8_t*>(p.kk) + row0;
+  d.vb = static_cast<const uint8_t*>(p.vv) + row0;
+  d.lrem = rc.L - J * BLK;
+  d.rstride = p.Hkv * kHeadDim * 2;
+  d.voff = voff_kv;
+  d.kt = kt;
+  d.vt = vt;
+  d.w = w;
+  return d;
+}
+
+// qk_half with a block's DMA spread over its first MFMAs (two per slab).
+template <int DEPTH, int BLK>
+__device__ __forceinline__ void qk_half_dma(const bf16x8 (&qf)[kHeadDim / 16], const uint8_t* kh, f32x16 (&s)[2],
+                                            const ItemDma& d) {
+  constexpr int NJ = 2 * (kHeadDim / 16);
+  constexpr int NF = 2 * (BLK / kSlab);
+  bf16x8 kf[DEPTH];
+#pragma unroll
+  for (int j = 0; j < DEPTH; ++j) kf[j] = k_operand(kh, j);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    s[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j % DEPTH], qf[j >> 1], j < 2 ? f32x16{} : s[j & 1], 0, 0, 0);
+    if (j + DEPTH < NJ) kf[j % DEPTH] = k_operand(kh, j + DEPTH);
+    if constexpr (NF > 0) if (j == 0) d.template fire<0>();
+    if constexpr (NF > 1) if (j == 1) d.template fire<1>();
+    if constexpr (NF > 2) if (j == 2) d.template fire<2>();
+    if constexpr (NF > 3) if (j == 3) d.template fire<3>();
+    if constexpr (NF > 4) if (j == 4) d.template fire<4>();
+    if constexpr (NF > 5) if (j == 5) d.template fire<5>();
+    if constexpr (NF > 6) if (j == 6) d.template fire<6>();
+    if constexpr (NF > 7) if (j == 7) d.template fire<7>();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// attend_exact whose first QK^T half also issues the next block's DMA.
+template <int BLK>
+__device__ __forceinline__ void attend_exact_dma(WaveState<BLK>& ws, const uint8_t* kb, const uint8_t* vt, float sl2,
+                                                 int lk, int lv, const ItemDma& d) {
+  constexpr int NH = BLK / 64;
+  constexpr int kDepth = 4;
+  f32x16 sb[2][2];
+  qk_half_dma<kDepth, BLK>(ws.qf, kb + lk, sb[0], d);
 #pragma unroll
   for (int hh = 0; hh < NH; ++hh) {
     const uint8_t* vh = vt + lv + (2 * hh) * 8 * kQuad;
@@ -534,6 +620,29 @@ struct ItemLoop {
 
   template <bool EXACT, int SET>
   __device__ __forceinline__ void step(WaveState<BLK>& ws, int e) {
+    if constexpr (EXACT && !PAGED) {
+      // The next item is an off-diagonal or the diagonal block: its DMA runs
+      // inside this item's first QK^T half (waves without rows issue it here).
+      const ItemDma d = prep_block<BLK>(p, rc, colcache, e + 1, SET ? kt0 : kt1, SET ? vt0 : vt1, w, voff_kv);
+      if (wave_active) {
+        attend_exact_dma<BLK>(ws, SET ? kt1 : kt0, SET ? vt1 : vt0, sl2, lk, lv, d);
+      } else {
+        d.template fire<0>();
+        d.template fire<1>();
+        if constexpr (BLK > 32) {
+          d.template fire<2>();
+          d.template fire<3>();
+        }
+        if constexpr (BLK > 64) {
+          d.template fire<4>();
+          d.template fire<5>();
+          d.template fire<6>();
+          d.template fire<7>();
+        }
+      }
+      tiles_ready();
+      return;
+    }
     if (e + 1 < N)
       issue_item<BLK, PAGED>(p, rc, colcache, selbits, e + 1, SET ? kt0 : kt1, SET ? vt0 : vt1, SET ? bias0 : bias1,
                              tid, w, lane, voff_kv, voff_pool);
@@ -559,7 +668,7 @@ struct ItemLoop {
   }
 };
 
-template <int BLK, bool PAGED>
+template <int BLK, bool PAGED, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   // Two tile sets, each its own LDS object, so the compiler can tell the
   // in-flight DMA into one set from the operand reads of the other.
@@ -592,6 +701,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = uniform(tid >> 6);
+  // Waves w and w + 4 share a SIMD. The first of each pair keeps a higher
+  // issue priority for the whole kernel, so after each item barrier it takes
+  // the matrix core first and the pair drifts apart: one wave's softmax then
+  // runs under the other's MFMAs instead of both stalling on the same phase.
+  if (w < 4) __builtin_amdgcn_s_setprio(3);
   const int c = lane & 31, hf = lane >> 5;
   const int prow0 = sub * kRowsPerWG + w * 32;  // first packed row of this wave
   const bool wave_active = prow0 < p.G * BLK;
@@ -662,22 +776,32 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   // code without any score adjustment; the diagonal block and the correction
   // chunks follow through the general one. Item e always lives in tile set
   // e & 1.
-  int e0 = 0, e1 = rc.n_items;
-  if (p.splits > 1) split_range(rc.n_exact, rc.n_items, split, p.splits, e0, e1);
-  if (e0 < e1) {
-    const bool odd = e0 & 1;
-    issue_item<BLK, PAGED>(p, rc, colcache, selbits, e0, odd ? kt1 : kt0, odd ? vt1 : vt0, odd ? bias1 : bias0,
-                           tid, w, lane, voff_kv, voff_pool);
+  if constexpr (SPLIT) {
+    int e0, e1;
+    split_range(rc.n_exact, rc.n_items, split, p.splits, e0, e1);
+    if (e0 < e1) {
+      const bool odd = e0 & 1;
+      issue_item<BLK, PAGED>(p, rc, colcache, selbits, e0, odd ? kt1 : kt0, odd ? vt1 : vt0, odd ? bias1 : bias0,
+                             tid, w, lane, voff_kv, voff_pool);
+      tiles_ready();
+      ItemLoop<BLK, PAGED> L{p, rc, colcache, selbits, kt0, kt1, vt0, vt1, bias0, bias1, e1, tid, w, lane,
+                             voff_kv, voff_pool, wave_active, tq0, tq, sl2, lk, lv, hf};
+      L.template run<true>(ws, e0, min(e1, rc.n_exact - 1));
+      L.template run<false>(ws, max(e0, rc.n_exact - 1), e1);
+    }
+  } else {
+    const int N = rc.n_items;
+    issue_item<BLK, PAGED>(p, rc, colcache, selbits, 0, kt0, vt0, bias0, tid, w, lane, voff_kv, voff_pool);
     tiles_ready();
-    ItemLoop<BLK, PAGED> L{p, rc, colcache, selbits, kt0, kt1, vt0, vt1, bias0, bias1, e1, tid, w, lane,
+    ItemLoop<BLK, PAGED> L{p, rc, colcache, selbits, kt0, kt1, vt0, vt1, bias0, bias1, N, tid, w, lane,
                            voff_kv, voff_pool, wave_active, tq0, tq, sl2, lk, lv, hf};
-    L.template run<true>(ws, e0, min(e1, rc.n_exact - 1));
-    L.template run<false>(ws, max(e0, rc.n_exact - 1), e1);
+    L.template run<true>(ws, 0, rc.n_exact - 1);
+    L.template run<false>(ws, rc.n_exact - 1, N);
   }
 
   if (!wave_active) return;
   const float l_tot = sum_halves(ws.l);
-  if (p.splits > 1) {
+  if constexpr (SPLIT) {
     // Partial result of this split: o / l and log2(l) + m (-inf when the
     // split saw no key), in the workspace for merge_kernel.
     if (q_valid) {
@@ -786,10 +910,10 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnParams p) {
   }
 }
 
-template <int BLK>
+template <int BLK, bool SPLIT>
 void launch_attn_t(const AttnParams& p, dim3 grid, hipStream_t stream) {
-  if (p.kv.paged) hipLaunchKernelGGL((attn_kernel<BLK, true>), grid, dim3(kThreads), 0, stream, p);
-  else hipLaunchKernelGGL((attn_kernel<BLK, false>), grid, dim3(kThreads), 0, stream, p);
+  if (p.kv.paged) hipLaunchKernelGGL((attn_kernel<BLK, true, SPLIT>), grid, dim3(kThreads), 0, stream, p);
+  else hipLaunchKernelGGL((attn_kernel<BLK, false, SPLIT>), grid, dim3(kThreads), 0, stream, p);
 }
 
 }  // namespace
@@ -806,8 +930,13 @@ hipError_t launch_attn(const AttnParams& p, hipStream_t stream) {
   }
   const int64_t wgs = (int64_t)p.Hkv * p.NBq_tot * p.subs * p.splits;
   dim3 grid((unsigned)wgs);
-  if (p.B == 128) launch_attn_t<128>(p, grid, stream);
-  else launch_attn_t<64>(p, grid, stream);
+  if (p.splits > 1) {
+    if (p.B == 128) launch_attn_t<128, true>(p, grid, stream);
+    else launch_attn_t<64, true>(p, grid, stream);
+  } else {
+    if (p.B == 128) launch_attn_t<128, false>(p, grid, stream);
+    else launch_attn_t<64, false>(p, grid, stream);
+  }
   if (p.splits > 1) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
