@@ -284,6 +284,12 @@ __device__ __forceinline__ void decode_work(const AttnParams& p, int& I, int& r,
   const int rem2 = rem / p.Hkv;
   sub = rem2 % p.subs;
   split = rem2 / p.subs;
+  if (rt.R == 1) {
+    // One request: its query blocks qb0 .. NBk - 1, heaviest first.
+    r = 0;
+    I = rt.kblk_off[1] - rt.kblk_off[0] - 1 - pk;
+    return;
+  }
   // C(x) = number of (r, I') with I' > x; non-increasing. Smallest I with C(I) <= pk.
   auto C = [&](int x) {
     int s = 0;
@@ -308,46 +314,54 @@ __device__ __forceinline__ void decode_work(const AttnParams& p, int& I, int& r,
   }
 }
 
+// Starts the DMA of key block J of a row into one K tile and one V tile.
+// Wave w, instruction u writes the 1 KiB group kWaves u + w of the tile:
+// lane l fetches 16-byte chunk l/4 of tile row kSlab u + 4w + l%4.
+template <int BLK, bool PAGED>
+__device__ __forceinline__ void issue_block(const AttnParams& p, const RowCtx& rc, int J, uint8_t* kt, uint8_t* vt,
+                                            int w, int lane, uint32_t voff_kv) {
+  const int rstride = p.Hkv * kHeadDim * 2;  // bytes between consecutive tokens of K or V
+  const int lrem = rc.L - J * BLK;           // rows of block J inside the request (>= 1)
+  if constexpr (!PAGED) {
+    const int64_t row0 = ((rc.tok_base + (int64_t)J * BLK) * p.Hkv + rc.h) * (kHeadDim * 2);
+    const uint8_t* kb = static_cast<const uint8_t*>(p.kk) + row0;
+    const uint8_t* vb = static_cast<const uint8_t*>(p.vv) + row0;
+#pragma unroll
+    for (int u = 0; u < BLK / kSlab; ++u) {
+      const int nrec = uniform(min(max(lrem - kSlab * u, 0), kSlab) * rstride);
+      const int64_t du = (int64_t)(kSlab * u) * rstride;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(kb + du, nrec),
+                                               (lds_ptr)(kt + (kWaves * u + w) * kQuad), 16, voff_kv, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(vb + du, nrec),
+                                               (lds_ptr)(vt + (kWaves * u + w) * kQuad), 16, voff_kv, 0, 0, 0);
+    }
+  } else {
+    // Rows past the request repeat its last token (masked by the causal
+    // mask of the diagonal item); each lane looks up its row's page.
+#pragma unroll
+    for (int u = 0; u < BLK / kSlab; ++u) {
+      const int rr = min(kSlab * u + 4 * w + (lane & 3), lrem - 1);
+      const int t = J * BLK + rr;
+      const int page = p.kv.page_table[(int64_t)rc.r * p.kv.max_pages + t / p.kv.page_size];
+      const int64_t off = (((int64_t)page * p.kv.page_size + t % p.kv.page_size) * p.Hkv + rc.h) * (kHeadDim * 2) +
+                          (lane >> 2) * 16;
+      __builtin_amdgcn_global_load_lds((gbl_ptr)(static_cast<const uint8_t*>(p.kk) + off),
+                                       (lds_ptr)(kt + (kWaves * u + w) * kQuad), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gbl_ptr)(static_cast<const uint8_t*>(p.vv) + off),
+                                       (lds_ptr)(vt + (kWaves * u + w) * kQuad), 16, 0, 0);
+    }
+  }
+}
+
 // Starts the DMA of item e into one K tile, one V tile and (pooled items) one
-// bias row. Wave w, instruction u writes the 1 KiB group kWaves u + w of the
-// tile: lane l fetches 16-byte chunk l/4 of tile row kSlab u + 4w + l%4.
+// bias row.
 template <int BLK, bool PAGED>
 __device__ __forceinline__ void issue_item(const AttnParams& p, const RowCtx& rc, const int32_t* colcache,
                                            const uint32_t* selbits, int e, uint8_t* kt, uint8_t* vt, float* bias,
                                            int tid, int w, int lane, uint32_t voff_kv, uint32_t voff_pool) {
-  const int rstride = p.Hkv * kHeadDim * 2;  // bytes between consecutive tokens of K or V
   if (e < rc.n_exact) {
     const int J = !rc.cols ? e : uniform(e < kColCache ? lload_i32(colcache + e) : gload_i32(rc.cols + e));
-    const int lrem = rc.L - J * BLK;  // rows of block J inside the request (>= 1)
-    if constexpr (!PAGED) {
-      const int64_t row0 = ((rc.tok_base + (int64_t)J * BLK) * p.Hkv + rc.h) * (kHeadDim * 2);
-      const uint8_t* kb = static_cast<const uint8_t*>(p.kk) + row0;
-      const uint8_t* vb = static_cast<const uint8_t*>(p.vv) + row0;
-#pragma unroll
-      for (int u = 0; u < BLK / kSlab; ++u) {
-        const int nrec = uniform(min(max(lrem - kSlab * u, 0), kSlab) * rstride);
-        const int64_t du = (int64_t)(kSlab * u) * rstride;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(kb + du, nrec),
-                                                 (lds_ptr)(kt + (kWaves * u + w) * kQuad), 16, voff_kv, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(vb + du, nrec),
-                                                 (lds_ptr)(vt + (kWaves * u + w) * kQuad), 16, voff_kv, 0, 0, 0);
-      }
-    } else {
-      // Rows past the request repeat its last token (masked by the causal
-      // mask of the diagonal item); each lane looks up its row's page.
-#pragma unroll
-      for (int u = 0; u < BLK / kSlab; ++u) {
-        const int rr = min(kSlab * u + 4 * w + (lane & 3), lrem - 1);
-        const int t = J * BLK + rr;
-        const int page = p.kv.page_table[(int64_t)rc.r * p.kv.max_pages + t / p.kv.page_size];
-        const int64_t off = (((int64_t)page * p.kv.page_size + t % p.kv.page_size) * p.Hkv + rc.h) * (kHeadDim * 2) +
-                            (lane >> 2) * 16;
-        __builtin_amdgcn_global_load_lds((gbl_ptr)(static_cast<const uint8_t*>(p.kk) + off),
-                                         (lds_ptr)(kt + (kWaves * u + w) * kQuad), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((gbl_ptr)(static_cast<const uint8_t*>(p.vv) + off),
-                                         (lds_ptr)(vt + (kWaves * u + w) * kQuad), 16, 0, 0);
-      }
-    }
+    issue_block<BLK, PAGED>(p, rc, J, kt, vt, w, lane, voff_kv);
   } else {
     // Correction chunk: pooled columns c0 .. c0+63 (bf16 rows of 256 bytes);
     // columns at or past I read zeros and get bias -inf.
@@ -734,33 +748,75 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
     oscale = *p.descale_v;
   }
 
+  // Q rows of a bf16 unsplit launch with 128-key blocks are staged through
+  // the idle tile set 1 by DMA, 16 lanes per 256-byte row, so each load
+  // instruction reads four whole rows; loading the operands directly would
+  // touch 32 rows (lines) per instruction, each four times. Wave w stages
+  // its 32 rows in groups of four, kQGroup bytes apart (the padding spreads
+  // the operand reads over the banks).
+  constexpr int kQGroup = 4 * kHeadDim * 2 + 16;
+  constexpr bool kQStage = BLK == 128 && !SPLIT;
+  static_assert(!kQStage || 4 * 8 * kQGroup <= (int)(Tile<BLK>::kWords * 16), "Q staging space");
+  const bool q_lds = kQStage && !p.fp8;
+  uint8_t* const qs = ((w >> 2) ? vt1 : kt1) + (w & 3) * 8 * kQGroup;
+  if (q_lds && wave_active) {
+    const int nvalid = max(0, min(32, nI - tq0));  // rows of the wave's 32 that exist
+    const int rstride = p.Hq * kHeadDim * 2;
+    const uint8_t* qb = static_cast<const uint8_t*>(p.q) + ((tok - c) * p.Hq + g) * (kHeadDim * 2);
+    const uint32_t qoff = (uint32_t)((lane >> 4) * rstride + (lane & 15) * 16);
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      // Buffer range: rows 4 it .. nvalid - 1 (bytes past the base of row 4 it).
+      const int nrec = uniform(nvalid > 4 * it ? (nvalid - 1 - 4 * it) * rstride + kHeadDim * 2 : 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(qb + (int64_t)(4 * it) * rstride, nrec),
+                                               (lds_ptr)(qs + it * kQGroup), 16, qoff, 0, 0, 0);
+    }
+  }
+
+  // Without split-KV the row starts at item 0, its first kept block: that
+  // block streams in while Q and the row's tables load.
+  if constexpr (!SPLIT)
+    issue_block<BLK, PAGED>(p, rc, p.dense ? 0 : sload_i32(rc.cols), kt0, vt0, w, lane, voff_kv);
+
   WaveState<BLK> ws;
   ws.m = kNegBig;
   ws.l = 0.f;
 #pragma unroll
   for (int dt = 0; dt < kHeadDim / 32; ++dt) ws.o[dt] = f32x16{};
+  if (!q_lds) {
 #pragma unroll
-  for (int ks = 0; ks < kHeadDim / 16; ++ks) {
-    uint4 qv = make_uint4(0, 0, 0, 0);
-    if (q_valid) {
-      const int64_t el = (tok * p.Hq + g) * kHeadDim + ks * 16 + hf * 8;
-      if (p.fp8) {
-        const uint2 w8 = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(p.q) + el);
-        qv.x = pack_bf16x2(e4m3_to_float(w8.x & 0xFF), e4m3_to_float((w8.x >> 8) & 0xFF));
-        qv.y = pack_bf16x2(e4m3_to_float((w8.x >> 16) & 0xFF), e4m3_to_float(w8.x >> 24));
-        qv.z = pack_bf16x2(e4m3_to_float(w8.y & 0xFF), e4m3_to_float((w8.y >> 8) & 0xFF));
-        qv.w = pack_bf16x2(e4m3_to_float((w8.y >> 16) & 0xFF), e4m3_to_float(w8.y >> 24));
-      } else {
-        qv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + el);
+    for (int ks = 0; ks < kHeadDim / 16; ++ks) {
+      uint4 qv = make_uint4(0, 0, 0, 0);
+      if (q_valid) {
+        const int64_t el = (tok * p.Hq + g) * kHeadDim + ks * 16 + hf * 8;
+        if (p.fp8) {
+          const uint2 w8 = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(p.q) + el);
+          qv.x = pack_bf16x2(e4m3_to_float(w8.x & 0xFF), e4m3_to_float((w8.x >> 8) & 0xFF));
+          qv.y = pack_bf16x2(e4m3_to_float((w8.x >> 16) & 0xFF), e4m3_to_float(w8.x >> 24));
+          qv.z = pack_bf16x2(e4m3_to_float(w8.y & 0xFF), e4m3_to_float((w8.y >> 8) & 0xFF));
+          qv.w = pack_bf16x2(e4m3_to_float((w8.y >> 16) & 0xFF), e4m3_to_float(w8.y >> 24));
+        } else {
+          qv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + el);
+        }
       }
+      ws.qf[ks] = __builtin_bit_cast(bf16x8, qv);
     }
-    ws.qf[ks] = __builtin_bit_cast(bf16x8, qv);
   }
 
   if (!p.dense) {
     if (do_corr)
       for (int wd = tid; wd <= (I >> 5); wd += kThreads) selbits[wd] = 0u;
     for (int e = tid; e < min(rc.n_exact, kColCache); e += kThreads) colcache[e] = rc.cols[e];
+  }
+  if (q_lds) {
+    // This wave's staged rows have landed (with the block and the columns):
+    // lane (c, hf) takes 16-byte chunk 2 ks + hf of row c.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    const uint8_t* qr = qs + (c >> 2) * kQGroup + (c & 3) * (kHeadDim * 2) + hf * 16;
+#pragma unroll
+    for (int ks = 0; ks < kHeadDim / 16; ++ks) ws.qf[ks] = *reinterpret_cast<const bf16x8*>(qr + ks * 32);
+  }
+  if (!p.dense) {
     __syncthreads();
     if (do_corr) {
       for (int e = tid; e < rc.n_exact; e += kThreads) {
@@ -791,7 +847,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
     }
   } else {
     const int N = rc.n_items;
-    issue_item<BLK, PAGED>(p, rc, colcache, selbits, 0, kt0, vt0, bias0, tid, w, lane, voff_kv, voff_pool);
     tiles_ready();
     ItemLoop<BLK, PAGED> L{p, rc, colcache, selbits, kt0, kt1, vt0, vt1, bias0, bias1, N, tid, w, lane,
                            voff_kv, voff_pool, wave_active, tq0, tq, sl2, lk, lv, hf};
@@ -821,9 +876,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
     }
     return;
   }
-  if (q_valid) {
-    const float inv = oscale / l_tot;
-    uint16_t* orow = p.out + (tok * p.Hq + g) * kHeadDim;
+  // Output rows through LDS: a lane holds 8-byte pieces of its query's row,
+  // and rows of one head lie Hq * 256 bytes apart, so direct stores would
+  // write 64 partial lines per instruction. The wave stages its 32 rows in
+  // its own part of the (now idle) tile buffers, 272 bytes apart, and stores
+  // them back 16 lanes per row: whole 256-byte rows.
+  {
+    const float inv = q_valid ? oscale / l_tot : 0.f;
+    constexpr int kOStride = kHeadDim * 2 + 16;
+    constexpr int kOStage = 32 * kOStride;
+    constexpr int kPer = (int)(Tile<BLK>::kWords * 16) / kOStage;  // waves per tile object
+    static_assert(kPer * 4 >= kWaves, "staging space");
+    const int oi = w / kPer;
+    uint8_t* const st = (oi == 0 ? kt0 : oi == 1 ? kt1 : oi == 2 ? vt0 : vt1) + (w % kPer) * kOStage;
 #pragma unroll
     for (int dt = 0; dt < kHeadDim / 32; ++dt) {
 #pragma unroll
@@ -831,11 +896,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
         uint2 pk;
         pk.x = pack_bf16x2(ws.o[dt][4 * i + 0] * inv, ws.o[dt][4 * i + 1] * inv);
         pk.y = pack_bf16x2(ws.o[dt][4 * i + 2] * inv, ws.o[dt][4 * i + 3] * inv);
-        *reinterpret_cast<uint2*>(orow + dt * 32 + i * 8 + hf * 4) = pk;
+        *reinterpret_cast<uint2*>(st + c * kOStride + (dt * 32 + i * 8 + hf * 4) * 2) = pk;
       }
     }
-    if (p.lse != nullptr && hf == 0) p.lse[(int64_t)g * p.T + tok] = (ws.m + __log2f(l_tot)) * kLn2;
+    const int64_t tok0 = tok - c;  // token of the wave's first row
+    const int chunk = lane & 15;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int rr = 4 * it + (lane >> 4);
+      const uint4 v = *reinterpret_cast<const uint4*>(st + rr * kOStride + chunk * 16);
+      if (tq0 + rr < nI) *reinterpret_cast<uint4*>(p.out + ((tok0 + rr) * p.Hq + g) * kHeadDim + chunk * 8) = v;
+    }
   }
+  if (q_valid && p.lse != nullptr && hf == 0) p.lse[(int64_t)g * p.T + tok] = (ws.m + __log2f(l_tot)) * kLn2;
 }
 
 // Conversion pass before the attention kernel (one launch, grid-stride):

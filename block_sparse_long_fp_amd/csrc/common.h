@@ -90,6 +90,10 @@ typedef const __attribute__((address_space(1))) int32_t g_int32;
 typedef const __attribute__((address_space(1))) uint8_t g_uint8;
 typedef const __attribute__((address_space(1))) float g_float;
 typedef const __attribute__((address_space(3))) int32_t l_int32;
+// Constant address space: memory no thread writes while the kernel runs.
+// Wave-uniform loads through it become scalar loads (s_load).
+typedef const __attribute__((address_space(4))) int32_t c_int32;
+__device__ __forceinline__ int32_t sload_i32(const int32_t* p) { return *(c_int32*)(p); }
 __device__ __forceinline__ uint4 gload16(g_u32x4* p) { return __builtin_bit_cast(uint4, *p); }
 __device__ __forceinline__ int32_t gload_i32(const int32_t* p) { return *(g_int32*)(p); }
 __device__ __forceinline__ int32_t lload_i32(const int32_t* p) { return *(l_int32*)(p); }
