@@ -353,6 +353,15 @@ __device__ __forceinline__ void issue_block(const AttnParams& p, const RowCtx& r
   }
 }
 
+// Key block of item e < n_exact of a row: item 0 is the diagonal block I,
+// items 1 .. n_exact - 1 the CSR's other kept blocks in column order (the
+// CSR row ends with the diagonal block, which is always kept).
+__device__ __forceinline__ int item_block(const RowCtx& rc, const int32_t* colcache, int e) {
+  if (e == 0) return rc.I;
+  if (!rc.cols) return e - 1;
+  return uniform(e - 1 < kColCache ? lload_i32(colcache + e - 1) : gload_i32(rc.cols + e - 1));
+}
+
 // Starts the DMA of item e into one K tile, one V tile and (pooled items) one
 // bias row.
 template <int BLK, bool PAGED>
@@ -360,8 +369,7 @@ __device__ __forceinline__ void issue_item(const AttnParams& p, const RowCtx& rc
                                            const uint32_t* selbits, int e, uint8_t* kt, uint8_t* vt, float* bias,
                                            int tid, int w, int lane, uint32_t voff_kv, uint32_t voff_pool) {
   if (e < rc.n_exact) {
-    const int J = !rc.cols ? e : uniform(e < kColCache ? lload_i32(colcache + e) : gload_i32(rc.cols + e));
-    issue_block<BLK, PAGED>(p, rc, J, kt, vt, w, lane, voff_kv);
+    issue_block<BLK, PAGED>(p, rc, item_block(rc, colcache, e), kt, vt, w, lane, voff_kv);
   } else {
     // Correction chunk: pooled columns c0 .. c0+63 (bf16 rows of 256 bytes);
     // columns at or past I read zeros and get bias -inf.
@@ -413,7 +421,7 @@ template <int BLK, bool EXACT>
 __device__ __forceinline__ void compute_item(WaveState<BLK>& ws, const RowCtx& rc, int e, const uint8_t* kt,
                                              const uint8_t* vt, const float* bias, int tq0, int tq, float sl2,
                                              int lk, int lv, int hf) {
-  const int kind = EXACT ? kExact : (e == rc.n_exact - 1 ? kDiag : kPooled);
+  const int kind = EXACT ? kExact : (e == 0 ? kDiag : (e < rc.n_exact ? kExact : kPooled));
   attend_item<BLK, EXACT>(ws, kt, vt, bias, kind, tq0 >> 5, tq, sl2, lk, lv, hf);
 }
 
@@ -549,7 +557,7 @@ struct ItemDma {
 template <int BLK>
 __device__ __forceinline__ ItemDma prep_block(const AttnParams& p, const RowCtx& rc, const int32_t* colcache, int e,
                                               uint8_t* kt, uint8_t* vt, int w, uint32_t voff_kv) {
-  const int J = !rc.cols ? e : uniform(e < kColCache ? lload_i32(colcache + e) : gload_i32(rc.cols + e));
+  const int J = item_block(rc, colcache, e);
   const int64_t row0 = ((rc.tok_base + (int64_t)J * BLK) * p.Hkv + rc.h) * (kHeadDim * 2);
   ItemDma d;
   d.kb = static_cast<const uint8_t*>(p.kk) + row0;
@@ -706,11 +714,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   const int qi = I - rt.qb0[rc.r];  // query block of the call
   const int nI = min(BLK, rc.L - I * BLK);
   const int64_t row = (int64_t)rc.h * p.NBq_tot + rt.blk_off[rc.r] + qi;
-  rc.n_exact = p.dense ? I + 1 : p.row_ptr[row + 1] - p.row_ptr[row];
-  rc.cols = p.dense ? nullptr : p.col_idx + p.row_ptr[row];
-  const bool do_corr = p.mean_correction && !p.dense && I > 0;
-  rc.n_items = rc.n_exact + (do_corr ? (I + kPC - 1) / kPC : 0);
-  rc.pooled_row0 = (int64_t)rc.h * p.kpitch + rt.kblk_off[rc.r];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -754,6 +757,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   // touch 32 rows (lines) per instruction, each four times. Wave w stages
   // its 32 rows in groups of four, kQGroup bytes apart (the padding spreads
   // the operand reads over the banks).
+  // Without split-KV the row starts at item 0, the diagonal block: it needs
+  // no CSR entry, so its DMA starts first, while Q and the row's tables load.
+  if constexpr (!SPLIT) issue_block<BLK, PAGED>(p, rc, I, kt0, vt0, w, lane, voff_kv);
+
   constexpr int kQGroup = 4 * kHeadDim * 2 + 16;
   constexpr bool kQStage = BLK == 128 && !SPLIT;
   static_assert(!kQStage || 4 * 8 * kQGroup <= (int)(Tile<BLK>::kWords * 16), "Q staging space");
@@ -773,10 +780,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
     }
   }
 
-  // Without split-KV the row starts at item 0, its first kept block: that
-  // block streams in while Q and the row's tables load.
-  if constexpr (!SPLIT)
-    issue_block<BLK, PAGED>(p, rc, p.dense ? 0 : sload_i32(rc.cols), kt0, vt0, w, lane, voff_kv);
+  // The row's CSR extent (scalar loads, after the DMA above so they do not
+  // delay it).
+  const int rp0 = p.dense ? 0 : sload_i32(p.row_ptr + row);
+  rc.n_exact = p.dense ? I + 1 : sload_i32(p.row_ptr + row + 1) - rp0;
+  rc.cols = p.dense ? nullptr : p.col_idx + rp0;
+  const bool do_corr = p.mean_correction && !p.dense && I > 0;
+  rc.n_items = rc.n_exact + (do_corr ? (I + kPC - 1) / kPC : 0);
+  rc.pooled_row0 = (int64_t)rc.h * p.kpitch + rt.kblk_off[rc.r];
 
   WaveState<BLK> ws;
   ws.m = kNegBig;
@@ -827,11 +838,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
     __syncthreads();
   }
 
-  // Items [e0, e1) of this split (all items without split-KV). The row's
-  // off-diagonal kept blocks run first through an instantiation of the item
-  // code without any score adjustment; the diagonal block and the correction
-  // chunks follow through the general one. Item e always lives in tile set
-  // e & 1.
+  // Items [e0, e1) of this split (all items without split-KV): the diagonal
+  // block, the other kept blocks, the correction chunks. The kept blocks
+  // between the first and the last run through an instantiation of the item
+  // code without any score adjustment (its DMA step can only stream a block
+  // next); the others through the general one. Item e always lives in tile
+  // set e & 1.
   if constexpr (SPLIT) {
     int e0, e1;
     split_range(rc.n_exact, rc.n_items, split, p.splits, e0, e1);
@@ -842,16 +854,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
       tiles_ready();
       ItemLoop<BLK, PAGED> L{p, rc, colcache, selbits, kt0, kt1, vt0, vt1, bias0, bias1, e1, tid, w, lane,
                              voff_kv, voff_pool, wave_active, tq0, tq, sl2, lk, lv, hf};
-      L.template run<true>(ws, e0, min(e1, rc.n_exact - 1));
-      L.template run<false>(ws, max(e0, rc.n_exact - 1), e1);
+      L.template run<false>(ws, e0, min(e1, 1));
+      L.template run<true>(ws, max(e0, 1), min(e1, rc.n_exact - 1));
+      L.template run<false>(ws, max(e0, max(1, rc.n_exact - 1)), e1);
     }
   } else {
     const int N = rc.n_items;
     tiles_ready();
     ItemLoop<BLK, PAGED> L{p, rc, colcache, selbits, kt0, kt1, vt0, vt1, bias0, bias1, N, tid, w, lane,
                            voff_kv, voff_pool, wave_active, tq0, tq, sl2, lk, lv, hf};
-    L.template run<true>(ws, 0, rc.n_exact - 1);
-    L.template run<false>(ws, rc.n_exact - 1, N);
+    L.template run<false>(ws, 0, 1);
+    L.template run<true>(ws, 1, rc.n_exact - 1);
+    L.template run<false>(ws, max(1, rc.n_exact - 1), N);
   }
 
   if (!wave_active) return;
