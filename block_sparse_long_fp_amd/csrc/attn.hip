@@ -40,11 +40,13 @@
 //     FP8) that a small conversion kernel writes into the workspace; FP8 K/V
 //     codes are converted the same way (exactly, code -> bf16), so the
 //     attention kernel itself runs one bf16 path.
-//   * Online softmax in base 2, updated per 64-key half of an item: max on
-//     raw scores, one fma + exp2 per score, fp32 row sums. The running max
-//     only moves when a half's max exceeds it by more than 8 (probabilities
-//     stay below 256, exact after the final division), so output rescales are
-//     rare.
+//   * Online softmax in base 2, updated per 64-key half of an item: one fma +
+//     exp2 per score against the running max as it stands, fp32 row sums. A
+//     half takes its own max only when a probability exceeds 2^64 (the row's
+//     first keys, or scores that grew by more than 64 in log2 units); the
+//     running max then moves if the half's max exceeds it by more than 8, and
+//     the output is rescaled. Probabilities stay below 2^64 and row sums far
+//     inside fp32; the result is exact after the final division.
 //   * Workgroups run heaviest first (query block index descending over the
 //     ragged batch), and consecutive ids cycle over KV heads so the
 //     round-robin XCD dispatch spreads each head's K/V over the L2s.
@@ -135,6 +137,55 @@ struct WaveState {
   float m;                   // running max (log2 units)
   float l;                   // this lane's partial row sum
 };
+
+// Probabilities 2^(s sc - m) of one 64-key half as bf16 P operands; returns
+// this lane's fp32 sum of them.
+__device__ __forceinline__ float half_probs(const f32x16 (&s)[2], float sc, float neg_m, bf16x8 (&pf)[2][2]) {
+  float lsum = 0.f;
+#pragma unroll
+  for (int t2 = 0; t2 < 2; ++t2) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      float pv[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) pv[t] = __builtin_amdgcn_exp2f(fmaf(s[t2][8 * s2 + t], sc, neg_m));
+      pf[t2][s2] = pack_probs(pv, lsum);
+    }
+  }
+  return lsum;
+}
+
+// Online-softmax update of one half of scores s (s sc in log2 units). The
+// probabilities are taken against the running max m as it stands; only when
+// one of them exceeds 2^64 (always on the row's first keys, where m is unset)
+// does the half take its max, move m if that max exceeds it by more than
+// kSlack, rescale O and l, and take them again. So m may trail the true
+// maximum by up to 64: every probability stays below 2^64 and every row sum
+// below 2^86, far inside fp32, and the result is the same softmax after the
+// final division. The common path spends no instruction on the maximum.
+template <int BLK>
+__device__ __forceinline__ void softmax_half(WaveState<BLK>& ws, const f32x16 (&s)[2], float sc, bf16x8 (&pf)[2][2]) {
+  constexpr float kPMax = 18446744073709551616.0f;  // 2^64
+  float lsum = half_probs(s, sc, -ws.m, pf);
+  if (__ballot(!(lsum <= kPMax)) != 0) {
+    float mx = kNegBig;
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[t2][e]);
+    mx = max_halves(mx * sc);
+    const float m_new = mx > ws.m + kSlack ? mx : ws.m;
+    if (__ballot(m_new != ws.m) != 0) {
+      const float corr = __builtin_amdgcn_exp2f(ws.m - m_new);
+      ws.l *= corr;
+#pragma unroll
+      for (int dt = 0; dt < kHeadDim / 32; ++dt) ws.o[dt] *= corr;
+    }
+    ws.m = m_new;
+    lsum = half_probs(s, sc, -m_new, pf);
+  }
+  ws.l += lsum;
+}
 
 // Item kinds: a selected key block off the diagonal (all keys visible), the
 // diagonal block (causal mask from tile kt_lim on), or a chunk of pooled
@@ -238,35 +289,8 @@ __device__ __forceinline__ void attend_item(WaveState<BLK>& ws, const uint8_t* k
           for (int jj = 0; jj < 4; ++jj)
             if ((2 * hh + t2) * 32 + i * 8 + hf * 4 + jj > tq) s[t2][4 * i + jj] = -INFINITY;
     }
-    float mx = kNegBig;
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[t2][e]);
-    mx = max_halves(mx * sc);
-    // Lazy running max (see the file header).
-    const float m_new = mx > ws.m + kSlack ? mx : ws.m;
-    if (__ballot(m_new != ws.m) != 0) {
-      const float corr = __builtin_amdgcn_exp2f(ws.m - m_new);
-      ws.l *= corr;
-#pragma unroll
-      for (int dt = 0; dt < kHeadDim / 32; ++dt) ws.o[dt] *= corr;
-    }
-    ws.m = m_new;
-    const float neg_m = -m_new;
-    float lsum = 0.f;
     bf16x8 pf[2][2];
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        float pv[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) pv[t] = __builtin_amdgcn_exp2f(fmaf(s[t2][8 * s2 + t], sc, neg_m));
-        pf[t2][s2] = pack_probs(pv, lsum);
-      }
-    }
-    ws.l += lsum;
+    softmax_half(ws, s, sc, pf);
     __builtin_amdgcn_sched_barrier(0);
     pv_jobs<16, kDepth>(ws.o, vf, pf, vh);
   }
@@ -468,40 +492,6 @@ __device__ __forceinline__ void pv_qk_half(f32x16 (&o)[kHeadDim / 32], bf16x8 (&
   }
 }
 
-// Online-softmax update of one half of exact scores (in score units): new
-// running max (lazy), output rescale if it moved, probabilities as bf16 P
-// operands and their fp32 sum.
-template <int BLK>
-__device__ __forceinline__ void softmax_exact(WaveState<BLK>& ws, const f32x16 (&s)[2], float sl2, bf16x8 (&pf)[2][2]) {
-  float mx = kNegBig;
-#pragma unroll
-  for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[t2][e]);
-  mx = max_halves(mx * sl2);
-  const float m_new = mx > ws.m + kSlack ? mx : ws.m;
-  if (__ballot(m_new != ws.m) != 0) {
-    const float corr = __builtin_amdgcn_exp2f(ws.m - m_new);
-    ws.l *= corr;
-#pragma unroll
-    for (int dt = 0; dt < kHeadDim / 32; ++dt) ws.o[dt] *= corr;
-  }
-  ws.m = m_new;
-  const float neg_m = -m_new;
-  float lsum = 0.f;
-#pragma unroll
-  for (int t2 = 0; t2 < 2; ++t2) {
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      float pv[8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) pv[t] = __builtin_amdgcn_exp2f(fmaf(s[t2][8 * s2 + t], sl2, neg_m));
-      pf[t2][s2] = pack_probs(pv, lsum);
-    }
-  }
-  ws.l += lsum;
-}
-
 // An off-diagonal kept block: all keys visible, no score adjustment. Its
 // halves are software-pipelined: QK^T(0); softmax(0); PV(0) with QK^T(1);
 // softmax(1); PV(1).
@@ -520,7 +510,7 @@ __device__ __forceinline__ void attend_exact(WaveState<BLK>& ws, const uint8_t* 
     for (int j = 0; j < kDepth; ++j) vf[j] = v_operand(vh, j);
     __builtin_amdgcn_sched_barrier(0);
     bf16x8 pf[2][2];
-    softmax_exact(ws, sb[hh & 1], sl2, pf);
+    softmax_half(ws, sb[hh & 1], sl2, pf);
     __builtin_amdgcn_sched_barrier(0);
     if (hh + 1 < NH)
       pv_qk_half<kDepth>(ws.o, vf, pf, vh, ws.qf, kb + lk + (2 * hh + 2) * 8 * kQuad, sb[(hh + 1) & 1]);
@@ -613,7 +603,7 @@ __device__ __forceinline__ void attend_exact_dma(WaveState<BLK>& ws, const uint8
     for (int j = 0; j < kDepth; ++j) vf[j] = v_operand(vh, j);
     __builtin_amdgcn_sched_barrier(0);
     bf16x8 pf[2][2];
-    softmax_exact(ws, sb[hh & 1], sl2, pf);
+    softmax_half(ws, sb[hh & 1], sl2, pf);
     __builtin_amdgcn_sched_barrier(0);
     if (hh + 1 < NH)
       pv_qk_half<kDepth>(ws.o, vf, pf, vh, ws.qf, kb + lk + (2 * hh + 2) * 8 * kQuad, sb[(hh + 1) & 1]);
