@@ -29,21 +29,49 @@ namespace {
 constexpr int kPoolThreads = 256;
 constexpr int kChunks = kHeadDim / 8;  // 8 elements per chunk
 
+constexpr int kBatch = 8;  // loads in flight per thread
+
+// The 8 elements at `elem` as raw words (16 bytes of bf16, or 8 bytes of
+// FP8 codes in .x/.y).
 template <bool FP8>
-__device__ __forceinline__ void load_chunk(const void* base, int64_t elem, float (&x)[8]) {
+__device__ __forceinline__ uint4 load_raw(const void* base, int64_t elem) {
   if constexpr (FP8) {
     const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(base) + elem);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = e4m3_to_float((w.x >> (8 * i)) & 0xFFu);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[4 + i] = e4m3_to_float((w.y >> (8 * i)) & 0xFFu);
+    return make_uint4(w.x, w.y, 0, 0);
   } else {
-    const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + elem);
-    x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x);
-    x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
-    x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z);
-    x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+    return *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + elem);
   }
+}
+
+template <bool FP8>
+__device__ __forceinline__ void add_raw(const uint4 w, float (&acc)[8]) {
+  if constexpr (FP8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += e4m3_to_float((w.x >> (8 * i)) & 0xFFu);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[4 + i] += e4m3_to_float((w.y >> (8 * i)) & 0xFFu);
+  } else {
+    acc[0] += bf16_lo(w.x); acc[1] += bf16_hi(w.x);
+    acc[2] += bf16_lo(w.y); acc[3] += bf16_hi(w.y);
+    acc[4] += bf16_lo(w.z); acc[5] += bf16_hi(w.z);
+    acc[6] += bf16_lo(w.w); acc[7] += bf16_hi(w.w);
+  }
+}
+
+// acc += the chunks at elem0 + k * estride for k = 0 .. cnt-1, in that order,
+// with kBatch loads in flight.
+template <bool FP8>
+__device__ __forceinline__ void sum_strided(const void* base, int64_t elem0, int64_t estride, int cnt,
+                                            float (&acc)[8]) {
+  int k = 0;
+  for (; k + kBatch <= cnt; k += kBatch) {
+    uint4 w[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) w[u] = load_raw<FP8>(base, elem0 + (int64_t)(k + u) * estride);
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) add_raw<FP8>(w[u], acc);
+  }
+  for (; k < cnt; ++k) add_raw<FP8>(load_raw<FP8>(base, elem0 + (int64_t)k * estride), acc);
 }
 
 template <bool FP8>
@@ -84,23 +112,21 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolParams p) {
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    // This thread's tokens: grp, grp + groups, ... below n.
+    const int cnt = grp < n ? (n - grp + groups - 1) / groups : 0;
     if (slot < G) {
       const int g = h * G + slot;
-      for (int t = grp; has_q && t < n; t += groups) {
-        const int64_t e = ((qtok0 + t) * p.Hq + g) * kHeadDim + chunk * 8;
-        float x[8];
-        load_chunk<FP8>(p.q, e, x);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += x[i];
-      }
+      if (has_q)
+        sum_strided<FP8>(p.q, ((qtok0 + grp) * p.Hq + g) * kHeadDim + chunk * 8, (int64_t)groups * p.Hq * kHeadDim,
+                         cnt, acc);
     } else {
       const void* src = (slot == G) ? p.k : p.v;
-      for (int t = grp; t < n; t += groups) {
-        const int64_t e = kv_elem_offset(p.kv, rt, r, t0 + t, h, p.Hkv) + chunk * 8;
-        float x[8];
-        load_chunk<FP8>(src, e, x);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += x[i];
+      if (!p.kv.paged) {
+        sum_strided<FP8>(src, kv_elem_offset(p.kv, rt, r, t0 + grp, h, p.Hkv) + chunk * 8,
+                         (int64_t)groups * p.Hkv * kHeadDim, cnt, acc);
+      } else {
+        for (int t = grp; t < n; t += groups)
+          add_raw<FP8>(load_raw<FP8>(src, kv_elem_offset(p.kv, rt, r, t0 + t, h, p.Hkv) + chunk * 8), acc);
       }
     }
     float* dst = part + ((int64_t)grp * tasks + task) * 8;
