@@ -303,6 +303,66 @@ __device__ __forceinline__ void attend_item(WaveState<BLK>& ws, const uint8_t* k
   }
 }
 
+// Several requests: (query block I, request r) of unit row pk. With C(x) the
+// number of (request q, query block I' of q) with I' > x, non-increasing in
+// x, I is the smallest x with C(x) <= pk, and r the (pk - C(I))-th request
+// (in order) that has query block I. Lane q (and q + 64) holds request q's
+// key-block count and first query block; each round of the search lets the 64
+// lanes evaluate C at 64 evenly spaced candidates (the request values
+// broadcast by readlane), so three rounds cover 2^18 blocks, with no chain of
+// dependent memory loads.
+__device__ __forceinline__ void decode_multi(const ReqTable& rt, int pk, int& I, int& r) {
+  const int lane = threadIdx.x & 63;
+  const int R = rt.R;
+  int nbA = 0, q0A = 0, nbB = 0, q0B = 0;
+  if (lane < R) {
+    nbA = rt.kblk_off[lane + 1] - rt.kblk_off[lane];
+    q0A = rt.qb0[lane];
+  }
+  if (lane + 64 < R) {
+    nbB = rt.kblk_off[lane + 65] - rt.kblk_off[lane + 64];
+    q0B = rt.qb0[lane + 64];
+  }
+  auto req = [&](int q, int& nb, int& q0) {
+    nb = __builtin_amdgcn_readlane(q < 64 ? nbA : nbB, q & 63);
+    q0 = __builtin_amdgcn_readlane(q < 64 ? q0A : q0B, q & 63);
+  };
+  int lo = 0, hi = rt.nb_max - 1;  // I lies in [lo, hi]; C(hi) = 0 <= pk
+  while (lo < hi) {
+    const int step = (hi - lo + 64) / 64;
+    const int x = min(lo + (lane + 1) * step - 1, hi);  // lane 63 takes hi
+    int cnt = 0;
+    for (int q = 0; q < R; ++q) {
+      int nb, q0;
+      req(q, nb, q0);
+      cnt += max(0, nb - max(x + 1, q0));
+    }
+    const uint64_t ok = __ballot(cnt <= pk);
+    const int f = __builtin_ctzll(ok);
+    hi = min(lo + (f + 1) * step - 1, hi);
+    lo = lo + f * step;
+  }
+  I = lo;
+  int j = pk;
+  for (int q = 0; q < R; ++q) {
+    int nb, q0;
+    req(q, nb, q0);
+    j -= max(0, nb - max(I + 1, q0));
+  }
+  r = 0;
+  for (int q = 0; q < R; ++q) {
+    int nb, q0;
+    req(q, nb, q0);
+    if (q0 <= I && nb > I) {
+      if (j == 0) {
+        r = q;
+        break;
+      }
+      --j;
+    }
+  }
+}
+
 // blockIdx -> (key block I of a query block, request r) in descending-I order
 // over the ragged batch, plus (kv head, sub-tile, split). Request r's query
 // blocks are its key blocks qb0 .. NBk - 1 (all of them in a whole prefill).
@@ -326,28 +386,7 @@ __device__ __forceinline__ void decode_work(const AttnParams& p, int& I, int& r,
     I = rt.kblk_off[1] - rt.kblk_off[0] - 1 - pk;
     return;
   }
-  // C(x) = number of (r, I') with I' > x; non-increasing. Smallest I with C(I) <= pk.
-  auto C = [&](int x) {
-    int s = 0;
-    for (int q = 0; q < rt.R; ++q)
-      s += max(0, rt.kblk_off[q + 1] - rt.kblk_off[q] - 1 - max(x, rt.qb0[q] - 1));
-    return s;
-  };
-  int lo = 0, hi = rt.nb_max - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (C(mid) <= pk) hi = mid;
-    else lo = mid + 1;
-  }
-  I = lo;
-  int j = pk - C(I);
-  r = 0;
-  for (int q = 0; q < rt.R; ++q) {
-    if (rt.qb0[q] <= I && rt.kblk_off[q + 1] - rt.kblk_off[q] > I) {
-      if (j == 0) { r = q; break; }
-      --j;
-    }
-  }
+  decode_multi(rt, pk, I, r);
 }
 
 // Starts the DMA of key block J of a row into one K tile and one V tile.

@@ -125,8 +125,22 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolParams p) {
         sum_strided<FP8>(src, kv_elem_offset(p.kv, rt, r, t0 + grp, h, p.Hkv) + chunk * 8,
                          (int64_t)groups * p.Hkv * kHeadDim, cnt, acc);
       } else {
-        for (int t = grp; t < n; t += groups)
-          add_raw<FP8>(load_raw<FP8>(src, kv_elem_offset(p.kv, rt, r, t0 + t, h, p.Hkv) + chunk * 8), acc);
+        // Paged: a batch's page-table lookups go out together, then its loads.
+        int k = 0;
+        for (; k + kBatch <= cnt; k += kBatch) {
+          int64_t off[kBatch];
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u)
+            off[u] = kv_elem_offset(p.kv, rt, r, t0 + grp + (k + u) * groups, h, p.Hkv) + chunk * 8;
+          uint4 w[kBatch];
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u) w[u] = load_raw<FP8>(src, off[u]);
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u) add_raw<FP8>(w[u], acc);
+        }
+        for (; k < cnt; ++k)
+          add_raw<FP8>(load_raw<FP8>(src, kv_elem_offset(p.kv, rt, r, t0 + grp + k * groups, h, p.Hkv) + chunk * 8),
+                       acc);
       }
     }
     float* dst = part + ((int64_t)grp * tasks + task) * 8;
