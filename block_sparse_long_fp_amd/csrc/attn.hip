@@ -73,6 +73,11 @@ constexpr int kRowsPerWG = kWaves * 32;
 constexpr int kSlab = 4 * kWaves;       // tile rows one DMA instruction of every wave fills
 constexpr int kPC = 64;                 // pooled columns per correction item
 constexpr int kQuad = 4 * 256 + 64;     // LDS bytes of a group of four 256-byte rows
+// K / V layouts (the PAGED template argument): contiguous, paged with any
+// page size (a page-table lookup per row), paged with a page size that is a
+// multiple of 4 (one lookup per four rows, which lets the DMA be spread).
+constexpr int kContig = 0, kPagedAny = 1, kPaged4 = 2;
+
 // Query blocks after which the KV head of a work-unit slot moves on (see
 // decode_work).
 constexpr int kHeadRotate = 16;
@@ -392,7 +397,7 @@ __device__ __forceinline__ void decode_work(const AttnParams& p, int& I, int& r,
 // Starts the DMA of key block J of a row into one K tile and one V tile.
 // Wave w, instruction u writes the 1 KiB group kWaves u + w of the tile:
 // lane l fetches 16-byte chunk l/4 of tile row kSlab u + 4w + l%4.
-template <int BLK, bool PAGED>
+template <int BLK, int PAGED>
 __device__ __forceinline__ void issue_block(const AttnParams& p, const RowCtx& rc, int J, uint8_t* kt, uint8_t* vt,
                                             int w, int lane, uint32_t voff_kv) {
   const int rstride = p.Hkv * kHeadDim * 2;  // bytes between consecutive tokens of K or V
@@ -439,7 +444,7 @@ __device__ __forceinline__ int item_block(const RowCtx& rc, const int32_t* colca
 
 // Starts the DMA of item e into one K tile, one V tile and (pooled items) one
 // bias row.
-template <int BLK, bool PAGED>
+template <int BLK, int PAGED>
 __device__ __forceinline__ void issue_item(const AttnParams& p, const RowCtx& rc, const int32_t* colcache,
                                            const uint32_t* selbits, int e, uint8_t* kt, uint8_t* vt, float* bias,
                                            int tid, int w, int lane, uint32_t voff_kv, uint32_t voff_pool) {
@@ -575,6 +580,7 @@ __device__ __forceinline__ void attend_exact(WaveState<BLK>& ws, const uint8_t* 
 // the first QK^T half, so the eight waves do not all stall together while
 // the vector memory unit accepts them (contiguous K / V only).
 struct ItemDma {
+  static constexpr int kFirst = 0;  // MFMA after which instruction 0 goes out
   const uint8_t* kb;
   const uint8_t* vb;
   int lrem;  // rows of the block inside the request
@@ -612,10 +618,62 @@ __device__ __forceinline__ ItemDma prep_block(const AttnParams& p, const RowCtx&
   return d;
 }
 
+// The next kept block's DMA in paged K / V, for page sizes that are a
+// multiple of 4: the four rows one wave's instruction fills (4w .. 4w+3 of a
+// 32-row slab, 4-aligned) then lie in one page, so each slab needs one page
+// id per wave, read by a scalar load when the DMA is prepared, and the
+// instruction reads the rows through a buffer range from that page's row
+// (rows past the request read zeros, masked as keys past every query). Its
+// instructions go out from the fifth MFMA on, leaving the page loads time.
+struct PagedDma {
+  static constexpr int kFirst = 4;
+  const uint8_t* kk;
+  const uint8_t* vv;
+  int64_t off[4];  // byte offset of the wave's first row of slab u (K and V alike)
+  int nrec[4];     // bytes of that 4-row group inside the request
+  uint32_t voff;   // lane: row lane % 4 of the group, chunk lane / 4
+  uint8_t* kt;
+  uint8_t* vt;
+  int w;
+  template <int I>
+  __device__ __forceinline__ void fire() const {
+    constexpr int u = I >> 1;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(((I & 1) ? vv : kk) + off[u], nrec[u]),
+                                             (lds_ptr)(((I & 1) ? vt : kt) + (kWaves * u + w) * kQuad), 16, voff,
+                                             0, 0, 0);
+  }
+};
+
+template <int BLK>
+__device__ __forceinline__ PagedDma prep_paged(const AttnParams& p, const RowCtx& rc, const int32_t* colcache, int e,
+                                               uint8_t* kt, uint8_t* vt, int w, int lane) {
+  static_assert(BLK / kSlab <= 4, "slabs per block");
+  const int J = item_block(rc, colcache, e);
+  const int lrem = rc.L - J * BLK;
+  const int rstride = p.Hkv * kHeadDim * 2;
+  PagedDma d;
+  d.kk = static_cast<const uint8_t*>(p.kk);
+  d.vv = static_cast<const uint8_t*>(p.vv);
+  d.voff = (uint32_t)((lane & 3) * rstride + (lane >> 2) * 16);
+  d.kt = kt;
+  d.vt = vt;
+  d.w = w;
+  const int32_t* ptab = p.kv.page_table + (int64_t)rc.r * p.kv.max_pages;
+#pragma unroll
+  for (int u = 0; u < BLK / kSlab; ++u) {
+    const int r0 = kSlab * u + 4 * w;  // the wave's first row of the slab
+    const int t = J * BLK + min(r0, lrem - 1);
+    const int page = sload_i32(ptab + t / p.kv.page_size);
+    d.off[u] = (((int64_t)page * p.kv.page_size + t % p.kv.page_size) * p.Hkv + rc.h) * (kHeadDim * 2);
+    d.nrec[u] = uniform(min(max(lrem - r0, 0), 4) * rstride);
+  }
+  return d;
+}
+
 // qk_half with a block's DMA spread over its first MFMAs (two per slab).
-template <int DEPTH, int BLK>
+template <int DEPTH, int BLK, typename D>
 __device__ __forceinline__ void qk_half_dma(const bf16x8 (&qf)[kHeadDim / 16], const uint8_t* kh, f32x16 (&s)[2],
-                                            const ItemDma& d) {
+                                            const D& d) {
   constexpr int NJ = 2 * (kHeadDim / 16);
   constexpr int NF = 2 * (BLK / kSlab);
   bf16x8 kf[DEPTH];
@@ -626,26 +684,26 @@ __device__ __forceinline__ void qk_half_dma(const bf16x8 (&qf)[kHeadDim / 16], c
   for (int j = 0; j < NJ; ++j) {
     s[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j % DEPTH], qf[j >> 1], j < 2 ? f32x16{} : s[j & 1], 0, 0, 0);
     if (j + DEPTH < NJ) kf[j % DEPTH] = k_operand(kh, j + DEPTH);
-    if constexpr (NF > 0) if (j == 0) d.template fire<0>();
-    if constexpr (NF > 1) if (j == 1) d.template fire<1>();
-    if constexpr (NF > 2) if (j == 2) d.template fire<2>();
-    if constexpr (NF > 3) if (j == 3) d.template fire<3>();
-    if constexpr (NF > 4) if (j == 4) d.template fire<4>();
-    if constexpr (NF > 5) if (j == 5) d.template fire<5>();
-    if constexpr (NF > 6) if (j == 6) d.template fire<6>();
-    if constexpr (NF > 7) if (j == 7) d.template fire<7>();
+    if constexpr (NF > 0) if (j == D::kFirst + 0) d.template fire<0>();
+    if constexpr (NF > 1) if (j == D::kFirst + 1) d.template fire<1>();
+    if constexpr (NF > 2) if (j == D::kFirst + 2) d.template fire<2>();
+    if constexpr (NF > 3) if (j == D::kFirst + 3) d.template fire<3>();
+    if constexpr (NF > 4) if (j == D::kFirst + 4) d.template fire<4>();
+    if constexpr (NF > 5) if (j == D::kFirst + 5) d.template fire<5>();
+    if constexpr (NF > 6) if (j == D::kFirst + 6) d.template fire<6>();
+    if constexpr (NF > 7) if (j == D::kFirst + 7) d.template fire<7>();
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 // attend_exact whose first QK^T half also issues the next block's DMA.
-template <int BLK>
+template <int BLK, typename D>
 __device__ __forceinline__ void attend_exact_dma(WaveState<BLK>& ws, const uint8_t* kb, const uint8_t* vt, float sl2,
-                                                 int lk, int lv, const ItemDma& d) {
+                                                 int lk, int lv, const D& d) {
   constexpr int NH = BLK / 64;
   constexpr int kDepth = 4;
   f32x16 sb[2][2];
-  qk_half_dma<kDepth, BLK>(ws.qf, kb + lk, sb[0], d);
+  qk_half_dma<kDepth, BLK, D>(ws.qf, kb + lk, sb[0], d);
 #pragma unroll
   for (int hh = 0; hh < NH; ++hh) {
     const uint8_t* vh = vt + lv + (2 * hh) * 8 * kQuad;
@@ -666,7 +724,7 @@ __device__ __forceinline__ void attend_exact_dma(WaveState<BLK>& ws, const uint8
 // The item loop of one workgroup. step<EXACT, SET>: stream item e+1 into the
 // other tile set while item e is computed from set SET, then wait for the
 // stream and for every wave.
-template <int BLK, bool PAGED>
+template <int BLK, int PAGED>
 struct ItemLoop {
   const AttnParams& p;
   const RowCtx& rc;
@@ -681,30 +739,46 @@ struct ItemLoop {
   float sl2;
   int lk, lv, hf;
 
+  // A kept block from tile set `set`, with the next block's DMA D spread
+  // over its first QK^T half.
+  template <typename D>
+  __device__ __forceinline__ void spread_step(WaveState<BLK>& ws, const D& d, int set) {
+    if (wave_active) {
+      attend_exact_dma<BLK, D>(ws, set ? kt1 : kt0, set ? vt1 : vt0, sl2, lk, lv, d);
+    } else {
+      d.template fire<0>();
+      d.template fire<1>();
+      if constexpr (BLK > 32) {
+        d.template fire<2>();
+        d.template fire<3>();
+      }
+      if constexpr (BLK > 64) {
+        d.template fire<4>();
+        d.template fire<5>();
+        d.template fire<6>();
+        d.template fire<7>();
+      }
+    }
+  }
+
   template <bool EXACT, int SET>
   __device__ __forceinline__ void step(WaveState<BLK>& ws, int e) {
-    if constexpr (EXACT && !PAGED) {
+    if constexpr (EXACT) {
       // The next item is an off-diagonal or the diagonal block: its DMA runs
       // inside this item's first QK^T half (waves without rows issue it here).
-      const ItemDma d = prep_block<BLK>(p, rc, colcache, e + 1, SET ? kt0 : kt1, SET ? vt0 : vt1, w, voff_kv);
-      if (wave_active) {
-        attend_exact_dma<BLK>(ws, SET ? kt1 : kt0, SET ? vt1 : vt0, sl2, lk, lv, d);
-      } else {
-        d.template fire<0>();
-        d.template fire<1>();
-        if constexpr (BLK > 32) {
-          d.template fire<2>();
-          d.template fire<3>();
+      // Paged K / V with a page size that is not a multiple of 4 keeps the
+      // burst below.
+      if constexpr (PAGED != kPagedAny) {
+        if constexpr (PAGED) {
+          const PagedDma d = prep_paged<BLK>(p, rc, colcache, e + 1, SET ? kt0 : kt1, SET ? vt0 : vt1, w, lane);
+          spread_step(ws, d, SET);
+        } else {
+          const ItemDma d = prep_block<BLK>(p, rc, colcache, e + 1, SET ? kt0 : kt1, SET ? vt0 : vt1, w, voff_kv);
+          spread_step(ws, d, SET);
         }
-        if constexpr (BLK > 64) {
-          d.template fire<4>();
-          d.template fire<5>();
-          d.template fire<6>();
-          d.template fire<7>();
-        }
+        tiles_ready();
+        return;
       }
-      tiles_ready();
-      return;
     }
     if (e + 1 < N)
       issue_item<BLK, PAGED>(p, rc, colcache, selbits, e + 1, SET ? kt0 : kt1, SET ? vt0 : vt1, SET ? bias0 : bias1,
@@ -731,7 +805,7 @@ struct ItemLoop {
   }
 };
 
-template <int BLK, bool PAGED, bool SPLIT>
+template <int BLK, int PAGED, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   // Two tile sets, each its own LDS object, so the compiler can tell the
   // in-flight DMA into one set from the operand reads of the other.
@@ -1040,8 +1114,10 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnParams p) {
 
 template <int BLK, bool SPLIT>
 void launch_attn_t(const AttnParams& p, dim3 grid, hipStream_t stream) {
-  if (p.kv.paged) hipLaunchKernelGGL((attn_kernel<BLK, true, SPLIT>), grid, dim3(kThreads), 0, stream, p);
-  else hipLaunchKernelGGL((attn_kernel<BLK, false, SPLIT>), grid, dim3(kThreads), 0, stream, p);
+  if (!p.kv.paged) hipLaunchKernelGGL((attn_kernel<BLK, kContig, SPLIT>), grid, dim3(kThreads), 0, stream, p);
+  else if (p.kv.page_size % 4 == 0)
+    hipLaunchKernelGGL((attn_kernel<BLK, kPaged4, SPLIT>), grid, dim3(kThreads), 0, stream, p);
+  else hipLaunchKernelGGL((attn_kernel<BLK, kPagedAny, SPLIT>), grid, dim3(kThreads), 0, stream, p);
 }
 
 }  // namespace

@@ -99,6 +99,20 @@ def test_paged_equals_contiguous_bitwise():
         assert np.array_equal(a[key], b[key]), key
 
 
+@pytest.mark.parametrize("page_size", [17, 6])
+def test_paged_page_size_not_multiple_of_4(page_size):
+    # Page sizes that are not a multiple of 4 take the per-row page lookup
+    # (the four rows one DMA instruction of a wave fills may straddle pages);
+    # the result must equal the contiguous layout's bit for bit.
+    wl = synth.make_workload("qwen4b_varlen_paged", lengths=[700, 1333], Hq=4, Hkv=1, min_sparse_len=0,
+                             page_size=page_size, n_planted=3)
+    _check_full(wl)
+    a = run_gpu(wl, paged=True)
+    b = run_gpu(wl, paged=False)
+    for key in ("row_ptr", "col_idx", "out", "lse"):
+        assert np.array_equal(a[key], b[key]), key
+
+
 def test_alpha_zero_sparse_equals_dense_kernel_and_oracle():
     # unsplit, so both calls process each row's key blocks in one sequence
     wl = synth.make_workload("llama_32k", L=1800, Hq=8, Hkv=2, n_planted=4)
