@@ -211,11 +211,11 @@ WsLayout ws_layout(const fp_problem* p, const Shape& s) {
   return w;
 }
 
-// Attention workspace: bf16 k_bar, v_bar (sparse calls), for FP8 bf16 copies
-// of the K and V codes in the caller's layout, and with split-KV the parts'
+// Attention workspace: bf16 k_bar, v_bar (sparse calls), for FP8 a bf16 copy
+// of the V codes in the caller's layout (K is read as FP8), and with split-KV the parts'
 // fp32 outputs [splits, Tq, Hq, d] and log2-sum-exps [splits, Tq, Hq].
 struct AttnWs {
-  size_t kbar16, vbar16, kk, vv, opart, lsepart, total;
+  size_t kbar16, vbar16, vv, opart, lsepart, total;
   int64_t kv_elems;
   int splits;
 };
@@ -232,9 +232,8 @@ AttnWs attn_ws_layout(const fp_problem* p, const Shape& s, bool sparse, int spli
   const size_t lp = splits > 1 ? align256((size_t)splits * rows * 4) : 0;
   w.kbar16 = 0;
   w.vbar16 = pool;
-  w.kk = 2 * pool;
-  w.vv = 2 * pool + kv;
-  w.opart = 2 * pool + 2 * kv;
+  w.vv = 2 * pool;
+  w.opart = 2 * pool + kv;
   w.lsepart = w.opart + op;
   w.total = w.lsepart + lp;
   return w;
@@ -388,7 +387,7 @@ static fp_status run_attention(const fp_problem* p, const fp_attn_args* attn, co
   AttnParams ap{};
   ap.q = q; ap.k = k; ap.v = v;
   const bool fp8 = p->dtype == FP_FP8_E4M3;
-  ap.kk = fp8 ? static_cast<const void*>(ws + aw.kk) : k;
+  ap.kk = k;
   ap.vv = fp8 ? static_cast<const void*>(ws + aw.vv) : v;
   ap.kv_elems = aw.kv_elems;
   const bool pooled = !dense && attn->mean_correction;

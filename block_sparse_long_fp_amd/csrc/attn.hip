@@ -37,9 +37,16 @@
 //     the hardware hands lane i dim i of 4 consecutive keys), also at
 //     immediate offsets; both are bank-conflict free.
 //   * Pooled items read bf16 copies of k_bar, v_bar (scaled to code units for
-//     FP8) that a small conversion kernel writes into the workspace; FP8 K/V
-//     codes are converted the same way (exactly, code -> bf16), so the
-//     attention kernel itself runs one bf16 path.
+//     FP8) that a small conversion kernel writes into the workspace.
+//   * FP8 (E4M3) inputs: QK^T of the kept blocks runs on the codes with
+//     v_mfma_f32_32x32x64_f8f6f4 (products of two codes are exact in fp32, so
+//     the scores are those of the widened codes, at twice the bf16 rate); K
+//     tiles hold the FP8 rows (half the DMA and LDS bytes). P V stays bf16:
+//     P rounded to E4M3 (3 mantissa bits) moves the output about 20 times
+//     as far as bf16 P does (max-abs 0.027 against 0.0015 on unit-variance
+//     V, 4K keys). V is widened once by the conversion kernel (exactly),
+//     and correction chunks multiply the bf16 pooled rows by Q widened in
+//     registers.
 //   * Online softmax in base 2, updated per 64-key half of an item: one fma +
 //     exp2 per score against the running max as it stands, fp32 row sums. A
 //     half takes its own max only when a probability exceeds 2^64 (the row's
@@ -77,6 +84,13 @@ constexpr int kQuad = 4 * 256 + 64;     // LDS bytes of a group of four 256-byte
 // page size (a page-table lookup per row), paged with a page size that is a
 // multiple of 4 (one lookup per four rows, which lets the DMA be spread).
 constexpr int kContig = 0, kPagedAny = 1, kPaged4 = 2;
+// FP8 K tiles hold the codes themselves (128-byte rows) in groups of eight
+// rows: 1024 bytes chunk-major (16-byte chunk c of row 8g + i at 128c + 16i),
+// the order one wave's 1 KiB DMA writes when lane l fetches chunk l/8 of row
+// 8g + l%8, plus 128 bytes of padding, so the sixteen lanes of one operand
+// read (rows c .. c+15, one chunk) hit distinct banks.
+constexpr int kOct = 8 * 128 + 128;
+constexpr int kSlab8 = 8 * kWaves;      // FP8 K rows one DMA instruction of every wave fills
 
 // Query blocks after which the KV head of a work-unit slot moves on (see
 // decode_work).
@@ -109,7 +123,10 @@ template <int BLK>
 struct Tile {
   static constexpr int kBytes = BLK / 4 * kQuad;
   static constexpr int kWords = kBytes / 16;
+  static_assert(BLK / 8 * kOct <= kBytes, "FP8 K tile");
 };
+
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
@@ -144,7 +161,8 @@ __device__ __forceinline__ float sum_halves(float x) {
 // Per-wave online-softmax state for 32 query rows.
 template <int BLK>
 struct WaveState {
-  bf16x8 qf[kHeadDim / 16];  // B operand of S^T = K Q^T, one per 16-dim step
+  bf16x8 qf[kHeadDim / 16];  // B operand of S^T = K Q^T, one per 16-dim step (bf16)
+  i32x8 q8[kHeadDim / 64];   // FP8: the codes as B operand, one per 64-dim step
   f32x16 o[kHeadDim / 32];   // O^T accumulators, one per 32-dim tile
   float m;                   // running max (log2 units)
   float l;                   // this lane's partial row sum
@@ -229,6 +247,78 @@ __device__ __forceinline__ void pv_jobs(f32x16 (&o)[kHeadDim / 32], bf16x8 (&vf)
   }
 }
 
+// bf16 K operand of QK job j of a half (tile 2hh + (j & 1), 16-dim step
+// ks = j >> 1): 16 bytes of row c. The lane's dims of step ks are those its
+// Q operand holds: 16 ks + 8 hf .. (chunk 2 ks + hf) for bf16 Q; for FP8 Q,
+// whose codes are held per 64-dim step, 64 (ks / 4) + 32 hf + 8 (ks % 4) ..
+// (chunk 8 (ks / 4) + 4 hf + ks % 4); the lane's hf part is in its base.
+template <bool F8>
+__device__ __forceinline__ bf16x8 k_operand(const uint8_t* kh, int j) {
+  const int ks = j >> 1;
+  const int off = F8 ? 512 * (ks >> 2) + 64 * (ks & 3) : 128 * ks;
+  return *reinterpret_cast<const bf16x8*>(kh + (j & 1) * 8 * kQuad + off);
+}
+
+// QK^T of one half: two accumulation chains, K operands read kDepth ahead.
+template <int DEPTH, bool F8>
+__device__ __forceinline__ void qk_half(const bf16x8 (&qf)[kHeadDim / 16], const uint8_t* kh, f32x16 (&s)[2]) {
+  constexpr int NJ = 2 * (kHeadDim / 16);
+  bf16x8 kf[DEPTH];
+#pragma unroll
+  for (int j = 0; j < DEPTH; ++j) kf[j] = k_operand<F8>(kh, j);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    s[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j % DEPTH], qf[j >> 1], j < 2 ? f32x16{} : s[j & 1], 0, 0, 0);
+    if (j + DEPTH < NJ) kf[j % DEPTH] = k_operand<F8>(kh, j + DEPTH);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// FP8 K operand of QK job j of a half (tile 2hh + (j & 1), dims 64 (j >> 1)
+// + 32 hf .. + 31): 32 bytes of row c, chunks 4 (j >> 1) + 2 hf and the next.
+__device__ __forceinline__ i32x8 k8_operand(const uint8_t* kh, int j) {
+  const uint8_t* a = kh + (j & 1) * 4 * kOct + (j >> 1) * 512;
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(a);
+  const u32x4 hi = *reinterpret_cast<const u32x4*>(a + 128);
+  return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// S^T += K Q^T over 64 dims on E4M3 codes (v_mfma_f32_32x32x64_f8f6f4, both
+// operands FP8, no block scales): the products of two codes are exact in
+// fp32, so the scores equal those of the codes widened to bf16.
+__device__ __forceinline__ f32x16 mfma_f8(const i32x8& a, const i32x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// The FP8 Q codes widened to bf16 (exactly: every E4M3 value is a bf16
+// value) as B operands of bf16 products, 8 codes per 16-dim step in the
+// order k_operand<true> reads the K side.
+__device__ __forceinline__ void widen_q(const i32x8 (&q8)[kHeadDim / 64], bf16x8 (&qf)[kHeadDim / 16]) {
+#pragma unroll
+  for (int ks = 0; ks < kHeadDim / 16; ++ks) {
+    const uint32_t lo = (uint32_t)q8[ks >> 2][2 * (ks & 3)], hi = (uint32_t)q8[ks >> 2][2 * (ks & 3) + 1];
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+    qf[ks] = bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  }
+}
+
+// FP8 QK^T of one half: tiles 2hh, 2hh+1 in two 64-dim steps each (four
+// MFMAs, two chains); the second step's operands load under the first.
+__device__ __forceinline__ void qk_half8(const i32x8 (&q8)[kHeadDim / 64], const uint8_t* kh, f32x16 (&s)[2]) {
+  i32x8 kf[2] = {k8_operand(kh, 0), k8_operand(kh, 1)};
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    s[j & 1] = mfma_f8(kf[j & 1], q8[j >> 1], j < 2 ? f32x16{} : s[j & 1]);
+    if (j < 2) kf[j & 1] = k8_operand(kh, j + 2);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // One item for one wave, processed in 64-key halves (each: QK^T of two
 // 32-key tiles, online-softmax update, PV), which keeps 32 score registers
 // live instead of 64. Every half computes both of its tiles: on the diagonal
@@ -241,10 +331,12 @@ __device__ __forceinline__ void pv_jobs(f32x16 (&o)[kHeadDim / 32], bf16x8 (&vf)
 // Operand reads run a few MFMAs ahead of their use; the schedule is pinned
 // with scheduling fences because the compiler otherwise places every LDS read
 // right before its MFMA and exposes the LDS latency each time.
-template <int BLK, bool EXACT>
+// F8: kept blocks are FP8 K tiles (operand base lk8), correction chunks bf16
+// tiles of the pooled rows (base lk).
+template <int BLK, bool EXACT, bool F8>
 __device__ __forceinline__ void attend_item(WaveState<BLK>& ws, const uint8_t* kb, const uint8_t* vt,
                                             const float* bias, int kind, int kt_lim, int tq, float sl2, int lk,
-                                            int lv, int hf) {
+                                            int lk8, int lv, int hf) {
   constexpr int kDepth = 4;  // operand reads in flight
   if (EXACT) kind = kExact;
   const int nh = kind == kPooled ? 1 : BLK / 64;
@@ -254,24 +346,20 @@ __device__ __forceinline__ void attend_item(WaveState<BLK>& ws, const uint8_t* k
 #pragma unroll
   for (int hh = 0; hh < BLK / 64; ++hh) {
     if (hh >= nh || (kind == kDiag && 2 * hh > kt_lim)) break;
-    // QK^T of tiles 2hh, 2hh+1: jobs alternate between the two accumulation
-    // chains; rows 32kt + c of a tile, the 16 dims of step ks 128 ks bytes
-    // after the lane's first chunk (four-row groups, see the file header).
-    constexpr int NJ = 2 * (kHeadDim / 16);
-    const uint8_t* kh = kb + lk + (2 * hh) * 8 * kQuad;
-    bf16x8 kf[kDepth];
-#pragma unroll
-    for (int j = 0; j < kDepth; ++j)
-      kf[j] = *reinterpret_cast<const bf16x8*>(kh + (j & 1) * 8 * kQuad + (j >> 1) * 128);
-    __builtin_amdgcn_sched_barrier(0);
+    // QK^T of tiles 2hh, 2hh+1 (rows 32kt + c of a tile).
     f32x16 s[2];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      s[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j % kDepth], ws.qf[j >> 1], j < 2 ? f32x16{} : s[j & 1], 0, 0, 0);
-      if (j + kDepth < NJ)
-        kf[j % kDepth] =
-            *reinterpret_cast<const bf16x8*>(kh + ((j + kDepth) & 1) * 8 * kQuad + ((j + kDepth) >> 1) * 128);
-      __builtin_amdgcn_sched_barrier(0);
+    if constexpr (F8) {
+      if (kind != kPooled) {
+        qk_half8(ws.q8, kb + lk8 + (2 * hh) * 4 * kOct, s);
+      } else {
+        // The pooled rows are bf16: Q widened for this chunk (not kept, to
+        // leave the registers to the kept blocks' pipeline).
+        bf16x8 qw[kHeadDim / 16];
+        widen_q(ws.q8, qw);
+        qk_half<kDepth, true>(qw, kb + lk + (2 * hh) * 8 * kQuad, s);
+      }
+    } else {
+      qk_half<kDepth, false>(ws.qf, kb + lk + (2 * hh) * 8 * kQuad, s);
     }
     // The first V operands load while the softmax runs.
     const uint8_t* vh = vt + lv + (2 * hh) * 8 * kQuad;
@@ -396,37 +484,59 @@ __device__ __forceinline__ void decode_work(const AttnParams& p, int& I, int& r,
 
 // Starts the DMA of key block J of a row into one K tile and one V tile.
 // Wave w, instruction u writes the 1 KiB group kWaves u + w of the tile:
-// lane l fetches 16-byte chunk l/4 of tile row kSlab u + 4w + l%4.
-template <int BLK, int PAGED>
+// lane l fetches 16-byte chunk l/4 of tile row kSlab u + 4w + l%4 (FP8 K:
+// chunk l/8 of row kSlab8 u + 8w + l%8).
+template <int BLK, int PAGED, bool F8>
 __device__ __forceinline__ void issue_block(const AttnParams& p, const RowCtx& rc, int J, uint8_t* kt, uint8_t* vt,
                                             int w, int lane, uint32_t voff_kv) {
-  const int rstride = p.Hkv * kHeadDim * 2;  // bytes between consecutive tokens of K or V
+  const int rstride = p.Hkv * kHeadDim * 2;  // bytes between consecutive tokens of bf16 K or V
+  const int rs8 = p.Hkv * kHeadDim;          // the same for FP8 K
   const int lrem = rc.L - J * BLK;           // rows of block J inside the request (>= 1)
   if constexpr (!PAGED) {
-    const int64_t row0 = ((rc.tok_base + (int64_t)J * BLK) * p.Hkv + rc.h) * (kHeadDim * 2);
-    const uint8_t* kb = static_cast<const uint8_t*>(p.kk) + row0;
-    const uint8_t* vb = static_cast<const uint8_t*>(p.vv) + row0;
+    const int64_t tok0 = (rc.tok_base + (int64_t)J * BLK) * p.Hkv + rc.h;
+    const uint8_t* kb = static_cast<const uint8_t*>(p.kk) + tok0 * (F8 ? kHeadDim : kHeadDim * 2);
+    const uint8_t* vb = static_cast<const uint8_t*>(p.vv) + tok0 * (kHeadDim * 2);
+    if constexpr (F8) {
+      const uint32_t voff8 = (uint32_t)((8 * w + (lane & 7)) * rs8 + (lane >> 3) * 16);
+#pragma unroll
+      for (int u = 0; u < BLK / kSlab8; ++u) {
+        const int nrec = uniform(min(max(lrem - kSlab8 * u, 0), kSlab8) * rs8);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(kb + (int64_t)(kSlab8 * u) * rs8, nrec),
+                                                 (lds_ptr)(kt + (kWaves * u + w) * kOct), 16, voff8, 0, 0, 0);
+      }
+    }
 #pragma unroll
     for (int u = 0; u < BLK / kSlab; ++u) {
       const int nrec = uniform(min(max(lrem - kSlab * u, 0), kSlab) * rstride);
       const int64_t du = (int64_t)(kSlab * u) * rstride;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(kb + du, nrec),
-                                               (lds_ptr)(kt + (kWaves * u + w) * kQuad), 16, voff_kv, 0, 0, 0);
+      if constexpr (!F8)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(kb + du, nrec),
+                                                 (lds_ptr)(kt + (kWaves * u + w) * kQuad), 16, voff_kv, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(vb + du, nrec),
                                                (lds_ptr)(vt + (kWaves * u + w) * kQuad), 16, voff_kv, 0, 0, 0);
     }
   } else {
     // Rows past the request repeat its last token (masked by the causal
     // mask of the diagonal item); each lane looks up its row's page.
+    const int32_t* ptab = p.kv.page_table + (int64_t)rc.r * p.kv.max_pages;
+    const int ps = p.kv.page_size;
+    if constexpr (F8) {
+#pragma unroll
+      for (int u = 0; u < BLK / kSlab8; ++u) {
+        const int t = J * BLK + min(kSlab8 * u + 8 * w + (lane & 7), lrem - 1);
+        const int64_t off = (((int64_t)ptab[t / ps] * ps + t % ps) * p.Hkv + rc.h) * kHeadDim + (lane >> 3) * 16;
+        __builtin_amdgcn_global_load_lds((gbl_ptr)(static_cast<const uint8_t*>(p.kk) + off),
+                                         (lds_ptr)(kt + (kWaves * u + w) * kOct), 16, 0, 0);
+      }
+    }
 #pragma unroll
     for (int u = 0; u < BLK / kSlab; ++u) {
-      const int rr = min(kSlab * u + 4 * w + (lane & 3), lrem - 1);
-      const int t = J * BLK + rr;
-      const int page = p.kv.page_table[(int64_t)rc.r * p.kv.max_pages + t / p.kv.page_size];
-      const int64_t off = (((int64_t)page * p.kv.page_size + t % p.kv.page_size) * p.Hkv + rc.h) * (kHeadDim * 2) +
-                          (lane >> 2) * 16;
-      __builtin_amdgcn_global_load_lds((gbl_ptr)(static_cast<const uint8_t*>(p.kk) + off),
-                                       (lds_ptr)(kt + (kWaves * u + w) * kQuad), 16, 0, 0);
+      const int t = J * BLK + min(kSlab * u + 4 * w + (lane & 3), lrem - 1);
+      const int64_t slot = ((int64_t)ptab[t / ps] * ps + t % ps) * p.Hkv + rc.h;
+      const int64_t off = slot * (kHeadDim * 2) + (lane >> 2) * 16;
+      if constexpr (!F8)
+        __builtin_amdgcn_global_load_lds((gbl_ptr)(static_cast<const uint8_t*>(p.kk) + off),
+                                         (lds_ptr)(kt + (kWaves * u + w) * kQuad), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((gbl_ptr)(static_cast<const uint8_t*>(p.vv) + off),
                                        (lds_ptr)(vt + (kWaves * u + w) * kQuad), 16, 0, 0);
     }
@@ -444,12 +554,12 @@ __device__ __forceinline__ int item_block(const RowCtx& rc, const int32_t* colca
 
 // Starts the DMA of item e into one K tile, one V tile and (pooled items) one
 // bias row.
-template <int BLK, int PAGED>
+template <int BLK, int PAGED, bool F8>
 __device__ __forceinline__ void issue_item(const AttnParams& p, const RowCtx& rc, const int32_t* colcache,
                                            const uint32_t* selbits, int e, uint8_t* kt, uint8_t* vt, float* bias,
                                            int tid, int w, int lane, uint32_t voff_kv, uint32_t voff_pool) {
   if (e < rc.n_exact) {
-    issue_block<BLK, PAGED>(p, rc, item_block(rc, colcache, e), kt, vt, w, lane, voff_kv);
+    issue_block<BLK, PAGED, F8>(p, rc, item_block(rc, colcache, e), kt, vt, w, lane, voff_kv);
   } else {
     // Correction chunk: pooled columns c0 .. c0+63 (bf16 rows of 256 bytes);
     // columns at or past I read zeros and get bias -inf.
@@ -497,33 +607,12 @@ __device__ __forceinline__ void tiles_ready() {
 }
 
 // One item of the row from tile set (kt, vt, bias).
-template <int BLK, bool EXACT>
+template <int BLK, bool EXACT, bool F8>
 __device__ __forceinline__ void compute_item(WaveState<BLK>& ws, const RowCtx& rc, int e, const uint8_t* kt,
                                              const uint8_t* vt, const float* bias, int tq0, int tq, float sl2,
-                                             int lk, int lv, int hf) {
+                                             int lk, int lk8, int lv, int hf) {
   const int kind = EXACT ? kExact : (e == 0 ? kDiag : (e < rc.n_exact ? kExact : kPooled));
-  attend_item<BLK, EXACT>(ws, kt, vt, bias, kind, tq0 >> 5, tq, sl2, lk, lv, hf);
-}
-
-// K operand of QK job j of a half (tile 2hh + (j & 1), dims 16 (j >> 1) ..).
-__device__ __forceinline__ bf16x8 k_operand(const uint8_t* kh, int j) {
-  return *reinterpret_cast<const bf16x8*>(kh + (j & 1) * 8 * kQuad + (j >> 1) * 128);
-}
-
-// QK^T of one half: two accumulation chains, K operands read kDepth ahead.
-template <int DEPTH>
-__device__ __forceinline__ void qk_half(const bf16x8 (&qf)[kHeadDim / 16], const uint8_t* kh, f32x16 (&s)[2]) {
-  constexpr int NJ = 2 * (kHeadDim / 16);
-  bf16x8 kf[DEPTH];
-#pragma unroll
-  for (int j = 0; j < DEPTH; ++j) kf[j] = k_operand(kh, j);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    s[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j % DEPTH], qf[j >> 1], j < 2 ? f32x16{} : s[j & 1], 0, 0, 0);
-    if (j + DEPTH < NJ) kf[j % DEPTH] = k_operand(kh, j + DEPTH);
-    __builtin_amdgcn_sched_barrier(0);
-  }
+  attend_item<BLK, EXACT, F8>(ws, kt, vt, bias, kind, tq0 >> 5, tq, sl2, lk, lk8, lv, hf);
 }
 
 // PV of one half interleaved with QK^T of the next: the two MFMA streams
@@ -536,28 +625,51 @@ __device__ __forceinline__ void pv_qk_half(f32x16 (&o)[kHeadDim / 32], bf16x8 (&
   constexpr int NJ = 16;
   bf16x8 kf[DEPTH];
 #pragma unroll
-  for (int j = 0; j < DEPTH; ++j) kf[j] = k_operand(kn, j);
+  for (int j = 0; j < DEPTH; ++j) kf[j] = k_operand<false>(kn, j);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     o[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j % DEPTH], pf[j >> 3][(j >> 2) & 1], o[j & 3], 0, 0, 0);
     if (j + DEPTH < NJ) vf[j % DEPTH] = v_operand(vh, j + DEPTH);
     sn[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j % DEPTH], qf[j >> 1], j < 2 ? f32x16{} : sn[j & 1], 0, 0, 0);
-    if (j + DEPTH < NJ) kf[j % DEPTH] = k_operand(kn, j + DEPTH);
+    if (j + DEPTH < NJ) kf[j % DEPTH] = k_operand<false>(kn, j + DEPTH);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// An off-diagonal kept block: all keys visible, no score adjustment. Its
-// halves are software-pipelined: QK^T(0); softmax(0); PV(0) with QK^T(1);
-// softmax(1); PV(1).
-template <int BLK>
-__device__ __forceinline__ void attend_exact(WaveState<BLK>& ws, const uint8_t* kb, const uint8_t* vt, float sl2,
-                                             int lk, int lv) {
+// pv_qk_half with the next half's QK^T in FP8: one FP8 MFMA (twice the
+// cycles of a bf16 one) after every fourth PV MFMA.
+template <int DEPTH>
+__device__ __forceinline__ void pv_qk_half8(f32x16 (&o)[kHeadDim / 32], bf16x8 (&vf)[DEPTH], const bf16x8 (&pf)[2][2],
+                                            const uint8_t* vh, const i32x8 (&q8)[kHeadDim / 64], const uint8_t* kn,
+                                            f32x16 (&sn)[2]) {
+  constexpr int NJ = 16;
+  i32x8 kf[2] = {k8_operand(kn, 0), k8_operand(kn, 1)};
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    o[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j % DEPTH], pf[j >> 3][(j >> 2) & 1], o[j & 3], 0, 0, 0);
+    if (j + DEPTH < NJ) vf[j % DEPTH] = v_operand(vh, j + DEPTH);
+    if ((j & 3) == 3) {
+      const int q = j >> 2;
+      sn[q & 1] = mfma_f8(kf[q & 1], q8[q >> 1], q < 2 ? f32x16{} : sn[q & 1]);
+      if (q < 2) kf[q & 1] = k8_operand(kn, q + 2);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Bytes between the K operands of consecutive halves (two 32-row tiles).
+template <bool F8>
+constexpr int kHalfK = F8 ? 8 * kOct : 16 * kQuad;
+
+// Softmax and PV of half hh of a kept block whose scores are in sb[hh & 1],
+// with the next half's QK^T interleaved into the PV.
+template <int BLK, bool F8>
+__device__ __forceinline__ void exact_halves(WaveState<BLK>& ws, const uint8_t* kh, const uint8_t* vt, float sl2,
+                                             int lv, f32x16 (&sb)[2][2]) {
   constexpr int NH = BLK / 64;
   constexpr int kDepth = 4;
-  f32x16 sb[2][2];
-  qk_half<kDepth>(ws.qf, kb + lk, sb[0]);
 #pragma unroll
   for (int hh = 0; hh < NH; ++hh) {
     const uint8_t* vh = vt + lv + (2 * hh) * 8 * kQuad;
@@ -568,11 +680,29 @@ __device__ __forceinline__ void attend_exact(WaveState<BLK>& ws, const uint8_t* 
     bf16x8 pf[2][2];
     softmax_half(ws, sb[hh & 1], sl2, pf);
     __builtin_amdgcn_sched_barrier(0);
-    if (hh + 1 < NH)
-      pv_qk_half<kDepth>(ws.o, vf, pf, vh, ws.qf, kb + lk + (2 * hh + 2) * 8 * kQuad, sb[(hh + 1) & 1]);
-    else
+    if (hh + 1 < NH) {
+      if constexpr (F8)
+        pv_qk_half8<kDepth>(ws.o, vf, pf, vh, ws.q8, kh + (hh + 1) * kHalfK<F8>, sb[(hh + 1) & 1]);
+      else
+        pv_qk_half<kDepth>(ws.o, vf, pf, vh, ws.qf, kh + (hh + 1) * kHalfK<F8>, sb[(hh + 1) & 1]);
+    } else {
       pv_jobs<16, kDepth>(ws.o, vf, pf, vh);
+    }
   }
+}
+
+// An off-diagonal kept block: all keys visible, no score adjustment. Its
+// halves are software-pipelined: QK^T(0); softmax(0); PV(0) with QK^T(1);
+// softmax(1); PV(1). kh: the lane's K operand base in the tile.
+template <int BLK, bool F8>
+__device__ __forceinline__ void attend_exact(WaveState<BLK>& ws, const uint8_t* kh, const uint8_t* vt, float sl2,
+                                             int lv) {
+  f32x16 sb[2][2];
+  if constexpr (F8)
+    qk_half8(ws.q8, kh, sb[0]);
+  else
+    qk_half<4, false>(ws.qf, kh, sb[0]);
+  exact_halves<BLK, F8>(ws, kh, vt, sl2, lv, sb);
 }
 
 // The next kept block's K / V DMA (BLK rows in 32-row slabs, K and V each),
@@ -678,12 +808,12 @@ __device__ __forceinline__ void qk_half_dma(const bf16x8 (&qf)[kHeadDim / 16], c
   constexpr int NF = 2 * (BLK / kSlab);
   bf16x8 kf[DEPTH];
 #pragma unroll
-  for (int j = 0; j < DEPTH; ++j) kf[j] = k_operand(kh, j);
+  for (int j = 0; j < DEPTH; ++j) kf[j] = k_operand<false>(kh, j);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     s[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j % DEPTH], qf[j >> 1], j < 2 ? f32x16{} : s[j & 1], 0, 0, 0);
-    if (j + DEPTH < NJ) kf[j % DEPTH] = k_operand(kh, j + DEPTH);
+    if (j + DEPTH < NJ) kf[j % DEPTH] = k_operand<false>(kh, j + DEPTH);
     if constexpr (NF > 0) if (j == D::kFirst + 0) d.template fire<0>();
     if constexpr (NF > 1) if (j == D::kFirst + 1) d.template fire<1>();
     if constexpr (NF > 2) if (j == D::kFirst + 2) d.template fire<2>();
@@ -696,35 +826,109 @@ __device__ __forceinline__ void qk_half_dma(const bf16x8 (&qf)[kHeadDim / 16], c
   }
 }
 
-// attend_exact whose first QK^T half also issues the next block's DMA.
-template <int BLK, typename D>
-__device__ __forceinline__ void attend_exact_dma(WaveState<BLK>& ws, const uint8_t* kb, const uint8_t* vt, float sl2,
-                                                 int lk, int lv, const D& d) {
-  constexpr int NH = BLK / 64;
-  constexpr int kDepth = 4;
-  f32x16 sb[2][2];
-  qk_half_dma<kDepth, BLK, D>(ws.qf, kb + lk, sb[0], d);
-#pragma unroll
-  for (int hh = 0; hh < NH; ++hh) {
-    const uint8_t* vh = vt + lv + (2 * hh) * 8 * kQuad;
-    bf16x8 vf[kDepth];
-#pragma unroll
-    for (int j = 0; j < kDepth; ++j) vf[j] = v_operand(vh, j);
-    __builtin_amdgcn_sched_barrier(0);
-    bf16x8 pf[2][2];
-    softmax_half(ws, sb[hh & 1], sl2, pf);
-    __builtin_amdgcn_sched_barrier(0);
-    if (hh + 1 < NH)
-      pv_qk_half<kDepth>(ws.o, vf, pf, vh, ws.qf, kb + lk + (2 * hh + 2) * 8 * kQuad, sb[(hh + 1) & 1]);
-    else
-      pv_jobs<16, kDepth>(ws.o, vf, pf, vh);
+// The next kept block's DMA for FP8 K (contiguous K / V): the BLK / 64 FP8
+// K instructions, then the bf16 V slabs.
+template <int BLK>
+struct ItemDma8 {
+  static constexpr int kNK = BLK / kSlab8;
+  static constexpr int kCount = kNK + BLK / kSlab;
+  const uint8_t* kb;  // FP8 K rows of the block (row stride rstride / 2)
+  const uint8_t* vb;  // bf16 V rows
+  int lrem;
+  int rstride;
+  uint32_t voff, voff8;
+  uint8_t* kt;
+  uint8_t* vt;
+  int w;
+  template <int I>
+  __device__ __forceinline__ void fire() const {
+    if constexpr (I < kNK) {
+      const int rs8 = rstride >> 1;
+      const int nrec = uniform(min(max(lrem - kSlab8 * I, 0), kSlab8) * rs8);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(kb + (int64_t)(kSlab8 * I) * rs8, nrec),
+                                               (lds_ptr)(kt + (kWaves * I + w) * kOct), 16, voff8, 0, 0, 0);
+    } else {
+      constexpr int u = I - kNK;
+      const int nrec = uniform(min(max(lrem - kSlab * u, 0), kSlab) * rstride);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(vb + (int64_t)(kSlab * u) * rstride, nrec),
+                                               (lds_ptr)(vt + (kWaves * u + w) * kQuad), 16, voff, 0, 0, 0);
+    }
   }
+};
+
+template <int BLK>
+__device__ __forceinline__ ItemDma8<BLK> prep_block8(const AttnParams& p, const RowCtx& rc, const int32_t* colcache,
+                                                     int e, uint8_t* kt, uint8_t* vt, int w, int lane,
+                                                     uint32_t voff_kv) {
+  const int J = item_block(rc, colcache, e);
+  const int64_t tok0 = (rc.tok_base + (int64_t)J * BLK) * p.Hkv + rc.h;
+  ItemDma8<BLK> d;
+  d.kb = static_cast<const uint8_t*>(p.kk) + tok0 * kHeadDim;
+  d.vb = static_cast<const uint8_t*>(p.vv) + tok0 * (kHeadDim * 2);
+  d.lrem = rc.L - J * BLK;
+  d.rstride = p.Hkv * kHeadDim * 2;
+  d.voff = voff_kv;
+  d.voff8 = (uint32_t)((8 * w + (lane & 7)) * (p.Hkv * kHeadDim) + (lane >> 3) * 16);
+  d.kt = kt;
+  d.vt = vt;
+  d.w = w;
+  return d;
+}
+
+// Issues DMA instructions [0, NF) of d.
+template <int NF, typename D>
+__device__ __forceinline__ void fire_all(const D& d) {
+  if constexpr (NF > 0) d.template fire<0>();
+  if constexpr (NF > 1) d.template fire<1>();
+  if constexpr (NF > 2) d.template fire<2>();
+  if constexpr (NF > 3) d.template fire<3>();
+  if constexpr (NF > 4) d.template fire<4>();
+  if constexpr (NF > 5) d.template fire<5>();
+  if constexpr (NF > 6) d.template fire<6>();
+  if constexpr (NF > 7) d.template fire<7>();
+}
+
+// qk_half8 with a block's DMA spread over its MFMAs, two instructions after
+// each (an FP8 MFMA takes as long as two bf16 ones).
+template <int BLK>
+__device__ __forceinline__ void qk_half8_dma(const i32x8 (&q8)[kHeadDim / 64], const uint8_t* kh, f32x16 (&s)[2],
+                                             const ItemDma8<BLK>& d) {
+  constexpr int NF = ItemDma8<BLK>::kCount;
+  static_assert(NF <= 8, "two DMA instructions per FP8 MFMA");
+  i32x8 kf[2] = {k8_operand(kh, 0), k8_operand(kh, 1)};
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    s[j & 1] = mfma_f8(kf[j & 1], q8[j >> 1], j < 2 ? f32x16{} : s[j & 1]);
+    if (j < 2) kf[j & 1] = k8_operand(kh, j + 2);
+    if constexpr (NF > 0) if (j == 0) d.template fire<0>();
+    if constexpr (NF > 1) if (j == 0) d.template fire<1>();
+    if constexpr (NF > 2) if (j == 1) d.template fire<2>();
+    if constexpr (NF > 3) if (j == 1) d.template fire<3>();
+    if constexpr (NF > 4) if (j == 2) d.template fire<4>();
+    if constexpr (NF > 5) if (j == 2) d.template fire<5>();
+    if constexpr (NF > 6) if (j == 3) d.template fire<6>();
+    if constexpr (NF > 7) if (j == 3) d.template fire<7>();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// attend_exact whose first QK^T half also issues the next block's DMA.
+template <int BLK, bool F8, typename D>
+__device__ __forceinline__ void attend_exact_dma(WaveState<BLK>& ws, const uint8_t* kh, const uint8_t* vt, float sl2,
+                                                 int lv, const D& d) {
+  f32x16 sb[2][2];
+  if constexpr (F8)
+    qk_half8_dma<BLK>(ws.q8, kh, sb[0], d);
+  else
+    qk_half_dma<4, BLK, D>(ws.qf, kh, sb[0], d);
+  exact_halves<BLK, F8>(ws, kh, vt, sl2, lv, sb);
 }
 
 // The item loop of one workgroup. step<EXACT, SET>: stream item e+1 into the
 // other tile set while item e is computed from set SET, then wait for the
 // stream and for every wave.
-template <int BLK, int PAGED>
+template <int BLK, int PAGED, bool F8>
 struct ItemLoop {
   const AttnParams& p;
   const RowCtx& rc;
@@ -737,28 +941,18 @@ struct ItemLoop {
   bool wave_active;
   int tq0, tq;
   float sl2;
-  int lk, lv, hf;
+  int lk, lk8, lv, hf;
+  // The lane's K operand base for kept blocks.
+  __device__ __forceinline__ int lkx() const { return F8 ? lk8 : lk; }
 
-  // A kept block from tile set `set`, with the next block's DMA D spread
-  // over its first QK^T half.
-  template <typename D>
+  // A kept block from tile set `set`, with the next block's DMA D (NF
+  // instructions) spread over its first QK^T half.
+  template <int NF, typename D>
   __device__ __forceinline__ void spread_step(WaveState<BLK>& ws, const D& d, int set) {
-    if (wave_active) {
-      attend_exact_dma<BLK, D>(ws, set ? kt1 : kt0, set ? vt1 : vt0, sl2, lk, lv, d);
-    } else {
-      d.template fire<0>();
-      d.template fire<1>();
-      if constexpr (BLK > 32) {
-        d.template fire<2>();
-        d.template fire<3>();
-      }
-      if constexpr (BLK > 64) {
-        d.template fire<4>();
-        d.template fire<5>();
-        d.template fire<6>();
-        d.template fire<7>();
-      }
-    }
+    if (wave_active)
+      attend_exact_dma<BLK, F8, D>(ws, (set ? kt1 : kt0) + lkx(), set ? vt1 : vt0, sl2, lv, d);
+    else
+      fire_all<NF>(d);
   }
 
   template <bool EXACT, int SET>
@@ -766,29 +960,36 @@ struct ItemLoop {
     if constexpr (EXACT) {
       // The next item is an off-diagonal or the diagonal block: its DMA runs
       // inside this item's first QK^T half (waves without rows issue it here).
-      // Paged K / V with a page size that is not a multiple of 4 keeps the
-      // burst below.
-      if constexpr (PAGED != kPagedAny) {
+      // Paged K / V with a page size that is not a multiple of 4 (and
+      // paged FP8 K, whose 8-row groups may straddle pages) keeps the burst
+      // below.
+      if constexpr (F8 && PAGED == kContig) {
+        const ItemDma8<BLK> d =
+            prep_block8<BLK>(p, rc, colcache, e + 1, SET ? kt0 : kt1, SET ? vt0 : vt1, w, lane, voff_kv);
+        spread_step<ItemDma8<BLK>::kCount>(ws, d, SET);
+        tiles_ready();
+        return;
+      } else if constexpr (!F8 && PAGED != kPagedAny) {
         if constexpr (PAGED) {
           const PagedDma d = prep_paged<BLK>(p, rc, colcache, e + 1, SET ? kt0 : kt1, SET ? vt0 : vt1, w, lane);
-          spread_step(ws, d, SET);
+          spread_step<2 * (BLK / kSlab)>(ws, d, SET);
         } else {
           const ItemDma d = prep_block<BLK>(p, rc, colcache, e + 1, SET ? kt0 : kt1, SET ? vt0 : vt1, w, voff_kv);
-          spread_step(ws, d, SET);
+          spread_step<2 * (BLK / kSlab)>(ws, d, SET);
         }
         tiles_ready();
         return;
       }
     }
     if (e + 1 < N)
-      issue_item<BLK, PAGED>(p, rc, colcache, selbits, e + 1, SET ? kt0 : kt1, SET ? vt0 : vt1, SET ? bias0 : bias1,
-                             tid, w, lane, voff_kv, voff_pool);
+      issue_item<BLK, PAGED, F8>(p, rc, colcache, selbits, e + 1, SET ? kt0 : kt1, SET ? vt0 : vt1,
+                                 SET ? bias0 : bias1, tid, w, lane, voff_kv, voff_pool);
     if (wave_active) {
       if (EXACT)
-        attend_exact<BLK>(ws, SET ? kt1 : kt0, SET ? vt1 : vt0, sl2, lk, lv);
+        attend_exact<BLK, F8>(ws, (SET ? kt1 : kt0) + lkx(), SET ? vt1 : vt0, sl2, lv);
       else
-        compute_item<BLK, false>(ws, rc, e, SET ? kt1 : kt0, SET ? vt1 : vt0, SET ? bias1 : bias0, tq0, tq, sl2,
-                                 lk, lv, hf);
+        compute_item<BLK, false, F8>(ws, rc, e, SET ? kt1 : kt0, SET ? vt1 : vt0, SET ? bias1 : bias0, tq0, tq,
+                                     sl2, lk, lk8, lv, hf);
     }
     tiles_ready();
   }
@@ -805,7 +1006,9 @@ struct ItemLoop {
   }
 };
 
-template <int BLK, int PAGED, bool SPLIT>
+// F8: Q and K are E4M3 codes (QK^T on the FP8 matrix cores), V a bf16 copy
+// of its codes.
+template <int BLK, int PAGED, bool SPLIT, bool F8>
 __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   // Two tile sets, each its own LDS object, so the compiler can tell the
   // in-flight DMA into one set from the operand reads of the other.
@@ -846,8 +1049,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   const int tq = tq0 + c;
   const bool q_valid = wave_active && tq < nI;
   const int64_t tok = rt.tok_off[rc.r] + (int64_t)qi * BLK + tq;  // query token
-  // K operand: row c of a 32-row tile, chunk hf (then + 128 bytes per 16 dims).
-  const int lk = (c >> 2) * kQuad + (c & 3) * 16 + hf * 64;
+  // K operand: row c of a 32-row tile, chunk hf (then + 128 bytes per 16
+  // dims); with FP8 Q (correction chunks) chunk 4 hf, see k_operand. FP8 K:
+  // row c, chunk 2 hf (then + 512 bytes per 64 dims).
+  const int lk = (c >> 2) * kQuad + (c & 3) * 16 + hf * (F8 ? 256 : 64);
+  const int lk8 = (c >> 3) * kOct + (c & 7) * 16 + hf * 256;
   // V^T operand: lane j of 16-lane group gq reads dims 16(gq&1) + 4(j&3)..+3 of
   // key 4(gq>>1) + j/4 (tile_off layout).
   const int j16 = lane & 15, gq = lane >> 4;
@@ -861,7 +1067,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   // by the V descale.
   float sl2 = p.sm_scale * kLog2e;
   float oscale = 1.f;
-  if (p.fp8) {
+  if constexpr (F8) {
     sl2 *= *p.descale_q * *p.descale_k;
     oscale = *p.descale_v;
   }
@@ -874,12 +1080,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   // the operand reads over the banks).
   // Without split-KV the row starts at item 0, the diagonal block: it needs
   // no CSR entry, so its DMA starts first, while Q and the row's tables load.
-  if constexpr (!SPLIT) issue_block<BLK, PAGED>(p, rc, I, kt0, vt0, w, lane, voff_kv);
+  if constexpr (!SPLIT) issue_block<BLK, PAGED, F8>(p, rc, I, kt0, vt0, w, lane, voff_kv);
 
   constexpr int kQGroup = 4 * kHeadDim * 2 + 16;
   constexpr bool kQStage = BLK == 128 && !SPLIT;
   static_assert(!kQStage || 4 * 8 * kQGroup <= (int)(Tile<BLK>::kWords * 16), "Q staging space");
-  const bool q_lds = kQStage && !p.fp8;
+  constexpr bool q_lds = kQStage && !F8;
   uint8_t* const qs = ((w >> 2) ? vt1 : kt1) + (w & 3) * 8 * kQGroup;
   if (q_lds && wave_active) {
     const int nvalid = max(0, min(32, nI - tq0));  // rows of the wave's 32 that exist
@@ -909,22 +1115,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   ws.l = 0.f;
 #pragma unroll
   for (int dt = 0; dt < kHeadDim / 32; ++dt) ws.o[dt] = f32x16{};
-  if (!q_lds) {
+  if constexpr (F8) {
+    // Lane (c, hf): codes 64 ks2 + 32 hf .. + 31 of its query.
+#pragma unroll
+    for (int ks2 = 0; ks2 < kHeadDim / 64; ++ks2) {
+      uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
+      if (q_valid) {
+        const uint8_t* qp = static_cast<const uint8_t*>(p.q) + (tok * p.Hq + g) * kHeadDim + ks2 * 64 + hf * 32;
+        a = *reinterpret_cast<const uint4*>(qp);
+        b = *reinterpret_cast<const uint4*>(qp + 16);
+      }
+      ws.q8[ks2] = i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+    }
+  } else if (!q_lds) {
 #pragma unroll
     for (int ks = 0; ks < kHeadDim / 16; ++ks) {
       uint4 qv = make_uint4(0, 0, 0, 0);
-      if (q_valid) {
-        const int64_t el = (tok * p.Hq + g) * kHeadDim + ks * 16 + hf * 8;
-        if (p.fp8) {
-          const uint2 w8 = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(p.q) + el);
-          qv.x = pack_bf16x2(e4m3_to_float(w8.x & 0xFF), e4m3_to_float((w8.x >> 8) & 0xFF));
-          qv.y = pack_bf16x2(e4m3_to_float((w8.x >> 16) & 0xFF), e4m3_to_float(w8.x >> 24));
-          qv.z = pack_bf16x2(e4m3_to_float(w8.y & 0xFF), e4m3_to_float((w8.y >> 8) & 0xFF));
-          qv.w = pack_bf16x2(e4m3_to_float((w8.y >> 16) & 0xFF), e4m3_to_float(w8.y >> 24));
-        } else {
-          qv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + el);
-        }
-      }
+      if (q_valid)
+        qv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + (tok * p.Hq + g) * kHeadDim +
+                                             ks * 16 + hf * 8);
       ws.qf[ks] = __builtin_bit_cast(bf16x8, qv);
     }
   }
@@ -934,7 +1143,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
       for (int wd = tid; wd <= (I >> 5); wd += kThreads) selbits[wd] = 0u;
     for (int e = tid; e < min(rc.n_exact, kColCache); e += kThreads) colcache[e] = rc.cols[e];
   }
-  if (q_lds) {
+  if constexpr (q_lds) {
     // This wave's staged rows have landed (with the block and the columns):
     // lane (c, hf) takes 16-byte chunk 2 ks + hf of row c.
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
@@ -964,11 +1173,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
     split_range(rc.n_exact, rc.n_items, split, p.splits, e0, e1);
     if (e0 < e1) {
       const bool odd = e0 & 1;
-      issue_item<BLK, PAGED>(p, rc, colcache, selbits, e0, odd ? kt1 : kt0, odd ? vt1 : vt0, odd ? bias1 : bias0,
-                             tid, w, lane, voff_kv, voff_pool);
+      issue_item<BLK, PAGED, F8>(p, rc, colcache, selbits, e0, odd ? kt1 : kt0, odd ? vt1 : vt0,
+                                 odd ? bias1 : bias0, tid, w, lane, voff_kv, voff_pool);
       tiles_ready();
-      ItemLoop<BLK, PAGED> L{p, rc, colcache, selbits, kt0, kt1, vt0, vt1, bias0, bias1, e1, tid, w, lane,
-                             voff_kv, voff_pool, wave_active, tq0, tq, sl2, lk, lv, hf};
+      ItemLoop<BLK, PAGED, F8> L{p, rc, colcache, selbits, kt0, kt1, vt0, vt1, bias0, bias1, e1, tid, w, lane,
+                                 voff_kv, voff_pool, wave_active, tq0, tq, sl2, lk, lk8, lv, hf};
       L.template run<false>(ws, e0, min(e1, 1));
       L.template run<true>(ws, max(e0, 1), min(e1, rc.n_exact - 1));
       L.template run<false>(ws, max(e0, max(1, rc.n_exact - 1)), e1);
@@ -976,8 +1185,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   } else {
     const int N = rc.n_items;
     tiles_ready();
-    ItemLoop<BLK, PAGED> L{p, rc, colcache, selbits, kt0, kt1, vt0, vt1, bias0, bias1, N, tid, w, lane,
-                           voff_kv, voff_pool, wave_active, tq0, tq, sl2, lk, lv, hf};
+    ItemLoop<BLK, PAGED, F8> L{p, rc, colcache, selbits, kt0, kt1, vt0, vt1, bias0, bias1, N, tid, w, lane,
+                               voff_kv, voff_pool, wave_active, tq0, tq, sl2, lk, lk8, lv, hf};
     L.template run<false>(ws, 0, 1);
     L.template run<true>(ws, 1, rc.n_exact - 1);
     L.template run<false>(ws, max(1, rc.n_exact - 1), N);
@@ -1042,12 +1251,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
 
 // Conversion pass before the attention kernel (one launch, grid-stride):
 // bf16 copies of k_bar, v_bar in code units (divided by the K / V descales
-// for FP8), and for FP8 the K and V codes as bf16 (exact).
+// for FP8), and for FP8 the V codes as bf16 (exact; K stays FP8).
 __global__ __launch_bounds__(256) void prep_kernel(AttnParams p, int64_t n_pool8, int64_t n_kv8) {
   const float ks = p.fp8 ? 1.f / *p.descale_k : 1.f;
   const float vs = p.fp8 ? 1.f / *p.descale_v : 1.f;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < 2 * n_pool8 + 2 * n_kv8; i += stride) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < 2 * n_pool8 + n_kv8; i += stride) {
     if (i < 2 * n_pool8) {
       const bool isv = i >= n_pool8;
       const int64_t k8 = isv ? i - n_pool8 : i;
@@ -1062,16 +1271,14 @@ __global__ __launch_bounds__(256) void prep_kernel(AttnParams p, int64_t n_pool8
       o.w = pack_bf16x2(b.z * s, b.w * s);
       reinterpret_cast<uint4*>(isv ? p.vbar16 : p.kbar16)[k8] = o;
     } else {
-      const int64_t j = i - 2 * n_pool8;
-      const bool isv = j >= n_kv8;
-      const int64_t k8 = isv ? j - n_kv8 : j;
-      const uint2 c = reinterpret_cast<const uint2*>(isv ? p.v : p.k)[k8];
+      const int64_t k8 = i - 2 * n_pool8;
+      const uint2 c = reinterpret_cast<const uint2*>(p.v)[k8];
       uint4 o;
       o.x = pack_bf16x2(e4m3_to_float(c.x & 0xFF), e4m3_to_float((c.x >> 8) & 0xFF));
       o.y = pack_bf16x2(e4m3_to_float((c.x >> 16) & 0xFF), e4m3_to_float(c.x >> 24));
       o.z = pack_bf16x2(e4m3_to_float(c.y & 0xFF), e4m3_to_float((c.y >> 8) & 0xFF));
       o.w = pack_bf16x2(e4m3_to_float((c.y >> 16) & 0xFF), e4m3_to_float(c.y >> 24));
-      reinterpret_cast<uint4*>(const_cast<void*>(isv ? p.vv : p.kk))[k8] = o;
+      reinterpret_cast<uint4*>(const_cast<void*>(p.vv))[k8] = o;
     }
   }
 }
@@ -1114,10 +1321,16 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnParams p) {
 
 template <int BLK, bool SPLIT>
 void launch_attn_t(const AttnParams& p, dim3 grid, hipStream_t stream) {
-  if (!p.kv.paged) hipLaunchKernelGGL((attn_kernel<BLK, kContig, SPLIT>), grid, dim3(kThreads), 0, stream, p);
-  else if (p.kv.page_size % 4 == 0)
-    hipLaunchKernelGGL((attn_kernel<BLK, kPaged4, SPLIT>), grid, dim3(kThreads), 0, stream, p);
-  else hipLaunchKernelGGL((attn_kernel<BLK, kPagedAny, SPLIT>), grid, dim3(kThreads), 0, stream, p);
+  if (p.fp8) {
+    if (!p.kv.paged) hipLaunchKernelGGL((attn_kernel<BLK, kContig, SPLIT, true>), grid, dim3(kThreads), 0, stream, p);
+    else hipLaunchKernelGGL((attn_kernel<BLK, kPagedAny, SPLIT, true>), grid, dim3(kThreads), 0, stream, p);
+  } else if (!p.kv.paged) {
+    hipLaunchKernelGGL((attn_kernel<BLK, kContig, SPLIT, false>), grid, dim3(kThreads), 0, stream, p);
+  } else if (p.kv.page_size % 4 == 0) {
+    hipLaunchKernelGGL((attn_kernel<BLK, kPaged4, SPLIT, false>), grid, dim3(kThreads), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((attn_kernel<BLK, kPagedAny, SPLIT, false>), grid, dim3(kThreads), 0, stream, p);
+  }
 }
 
 }  // namespace
@@ -1128,7 +1341,7 @@ hipError_t launch_attn(const AttnParams& p, hipStream_t stream) {
   const int64_t n_pool8 = p.kbar16 ? (int64_t)p.Hkv * p.kpitch * kHeadDim / 8 : 0;
   const int64_t n_kv8 = p.fp8 ? p.kv_elems / 8 : 0;
   if (n_pool8 + n_kv8 > 0) {
-    const int64_t work = 2 * n_pool8 + 2 * n_kv8;
+    const int64_t work = 2 * n_pool8 + n_kv8;
     const int blocks = (int)(work < 8192 * 256 ? (work + 255) / 256 : 8192);
     hipLaunchKernelGGL(prep_kernel, dim3(blocks), dim3(256), 0, stream, p, n_pool8, n_kv8);
   }

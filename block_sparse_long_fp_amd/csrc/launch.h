@@ -49,8 +49,8 @@ struct AttnParams {
   const void* q;
   const void* k;        // caller's K / V (bf16 or FP8 codes)
   const void* v;
-  const void* kk;       // K / V as bf16 the attention kernel reads: k / v for
-  const void* vv;       // bf16 inputs, the workspace copies for FP8
+  const void* kk;       // K the attention kernel reads: k (bf16 or FP8 codes)
+  const void* vv;       // V as bf16: v, or for FP8 the workspace copy of its codes
   const float* k_bar;
   const float* v_bar;
   uint16_t* kbar16;     // workspace: bf16 k_bar / v_bar in code units (or NULL)

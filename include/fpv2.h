@@ -181,7 +181,7 @@ fp_status fp_select_workspace_bytes(const fp_problem* p, size_t* bytes);
 /* Bytes of DEVICE workspace fp_sparse_prefill (sparse = 1) or fp_dense_prefill
  * (sparse = 0) needs with these attention args (NULL: defaults, automatic
  * split): bf16 copies of k_bar and v_bar for the correction (sparse only), for
- * FP8 bf16 copies of the K and V codes (exact), and with split-KV the parts'
+ * FP8 a bf16 copy of the V codes (exact; K is read as FP8), and with split-KV the parts'
  * fp32 outputs and log-sum-exps. 0 for an unsplit dense bf16 problem. */
 fp_status fp_attn_workspace_bytes(const fp_problem* p, const fp_attn_args* attn, int32_t sparse,
                                   size_t* bytes);

@@ -52,8 +52,9 @@ def test_attention_workspace_sizes():
     assert fp.attn_workspace_bytes(p, False, ONE) == 0
     ds = [torch.ones(1) for _ in range(3)]
     p8 = _prob(dtype=fp.FP_FP8_E4M3, descales=ds)
-    assert fp.attn_workspace_bytes(p8, True, ONE) == 2 * a256(Hkv * nb * d * 2) + 2 * a256(T * Hkv * d * 2)
-    assert fp.attn_workspace_bytes(p8, False, ONE) == 2 * a256(T * Hkv * d * 2)
+    # FP8: plus one bf16 copy of the V codes (K is read as FP8).
+    assert fp.attn_workspace_bytes(p8, True, ONE) == 2 * a256(Hkv * nb * d * 2) + a256(T * Hkv * d * 2)
+    assert fp.attn_workspace_bytes(p8, False, ONE) == a256(T * Hkv * d * 2)
 
 
 def test_index_shape_and_workspace():
@@ -78,8 +79,8 @@ def test_chunked_index_shape():
     assert fp.attn_workspace_bytes(p, True, ONE) == 2 * a256(8 * nbk * 128 * 2)
     ds = [torch.ones(1) for _ in range(3)]
     p8 = _prob(cu_seqlens=[0, 1000, 1640], cu_seqlens_k=[0, 3048, 3688], dtype=fp.FP_FP8_E4M3, descales=ds)
-    # FP8 copies cover every key token (Tk = 3688), not only the chunk
-    assert fp.attn_workspace_bytes(p8, False, ONE) == 2 * a256(3688 * 8 * 128 * 2)
+    # the FP8 V copy covers every key token (Tk = 3688), not only the chunk
+    assert fp.attn_workspace_bytes(p8, False, ONE) == a256(3688 * 8 * 128 * 2)
 
 
 def test_split_kv_choice_and_workspace():
