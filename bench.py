@@ -24,13 +24,24 @@ import numpy as np
 
 METRIC = "ms/layer & dense-equiv TFLOP/s at 128K causal prefill; % MFMA peak on computed FLOPs"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # MI355X dense MFMA peaks
+
+
+def mixed_peak(flops, exact_flops, dtype):
+    """Matrix-core peak of the FP8 kernel's actual mix: the kept blocks' QK^T
+    (half of their FLOPs) at the FP8 rate, their PV and the correction columns
+    at the bf16 rate. For bf16 inputs, the bf16 peak."""
+    if dtype != "fp8" or flops <= 0:
+        return PEAK_TFLOPS[dtype]
+    f8 = exact_flops / 2
+    return flops / (f8 / PEAK_TFLOPS["fp8"] + (flops - f8) / PEAK_TFLOPS["bf16"])
 HBM_PEAK_GBS = 8000.0
 
 
-# rocprofv3 HBM counters of the attention kernel are recorded in this file
+# rocprofv3 HBM counters of the attention kernel are recorded in these files
 # together with a hash of the kernel's sources; the benchmark reports them as
 # roofline.traffic only while the sources still hash the same.
-TRAFFIC_RECORD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "attn_kernel_llama128k_bf16.md")
+TRAFFIC_RECORDS = [os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", f)
+                   for f in ("attn_kernel_llama128k_bf16.md", "attn_kernel_qwen30b128k_fp8.md")]
 ATTN_SOURCES = ["attn.hip", "common.h"]
 
 
@@ -48,11 +59,13 @@ def recorded_traffic(workload, alpha):
     """HBM bytes per attention launch from the recorded FETCH_SIZE / WRITE_SIZE
     counters (KiB per dispatch, scaled by the copy-calibration factors), or None
     when no record matches this workload and the current kernel sources."""
-    try:
-        with open(TRAFFIC_RECORD) as f:
-            lines = [ln.strip() for ln in f if ln.strip().startswith("traffic-record:")]
-    except OSError:
-        return None
+    lines = []
+    for path in TRAFFIC_RECORDS:
+        try:
+            with open(path) as f:
+                lines += [ln.strip() for ln in f if ln.strip().startswith("traffic-record:")]
+        except OSError:
+            continue
     src = attn_source_hash()
     for ln in lines:
         kv = dict(tok.split("=", 1) for tok in ln.split()[1:] if "=" in tok)
@@ -116,7 +129,8 @@ def csr_work(row_ptr, col_idx, wl, blk_off, mean_correction=True):
     Per selected (h, I, J): 4 * d * (G * n_I) * n_J FLOPs (QK^T and PV over the
     packed rows; full tile on the diagonal). Per pruned causal (h, I, J < I):
     4 * d * (G * n_I) FLOPs (one pooled column). Also returns the strict
-    causal count (diagonal tile halved) and the kept fraction over causal pairs.
+    causal count (diagonal tile halved), the kept fraction over causal pairs
+    and the FLOPs of the selected blocks alone.
     Query block i of a request sits at key block I = qb0 + i (qb0 > 0 for a
     chunk of a chunked prefill).
     """
@@ -126,6 +140,7 @@ def csr_work(row_ptr, col_idx, wl, blk_off, mean_correction=True):
     counts = np.diff(row_ptr)
     flops = 0.0
     strict = 0.0
+    exact_flops = 0.0
     pairs = 0
     for r, (Lq, Lk) in enumerate(zip(wl.seqlens, wl.key_seqlens)):
         nb = blk_off[r + 1] - blk_off[r]
@@ -138,6 +153,7 @@ def csr_work(row_ptr, col_idx, wl, blk_off, mean_correction=True):
             # every selected J < I is a full block; the diagonal is n_I x n_I
             exact = (c - 1) * nI * B + nI * nI
             flops += 4 * d * G * float(exact.sum())
+            exact_flops += 4 * d * G * float(exact.sum())
             strict += 4 * d * G * float(((c - 1) * nI * B + nI * (nI + 1) / 2).sum())
             if mean_correction and not dense_req:
                 pruned = I - (c - 1)
@@ -145,7 +161,7 @@ def csr_work(row_ptr, col_idx, wl, blk_off, mean_correction=True):
                 strict += 4 * d * G * float((pruned * nI).sum())
             pairs += int((I + 1).sum())
     kept = float(row_ptr[-1]) / float(pairs)
-    return flops, strict, kept
+    return flops, strict, kept, exact_flops
 
 
 def stage1_bytes(wl):
@@ -274,7 +290,7 @@ def run_chunked(args, wl, fp, torch, q, k, v, descales):
         cw = synth.chunk_of(wl, s0, c)
         rp = b.row_ptr.cpu().numpy().astype(np.int64)
         nbq = -(-c // wl.block_size)
-        f, st, _ = csr_work(rp, None, cw, np.array([0, nbq]), not args.no_mean_correction)
+        f, st, _, _ = csr_work(rp, None, cw, np.array([0, nbq]), not args.no_mean_correction)
         flops, strict = flops + f, strict + st
         nnz += int(rp[-1])
         qb0 = s0 // wl.block_size
@@ -390,7 +406,7 @@ def main():
     col_idx = bufs.col_idx[: int(row_ptr[-1])].cpu().numpy()
     nbs = [-(-L // wl.block_size) for L in wl.seqlens]
     blk_off = np.concatenate([[0], np.cumsum(nbs)]).astype(np.int64)
-    flops, strict, kept = csr_work(row_ptr, col_idx, wl, blk_off, not args.no_mean_correction)
+    flops, strict, kept, exact_flops = csr_work(row_ptr, col_idx, wl, blk_off, not args.no_mean_correction)
     att_avg = float(np.mean(att_ms))
     dense_eq = wl.dense_equiv_flops()
     peak = PEAK_TFLOPS[wl.dtype]
@@ -444,6 +460,8 @@ def main():
         "ms_per_layer": ms,
         "stages_ms": {"pool": float(np.mean(pool_ms)), "select": float(np.mean(sel_ms)), "attention": att_avg},
         "attn_mfma_frac_computed": achieved / peak,
+        # FP8: against the peak of its FP8 / bf16 product mix (= frac for bf16)
+        "attn_mfma_frac_mixed_peak": achieved / mixed_peak(flops, exact_flops, wl.dtype),
         "attn_flops_computed": flops,
         "attn_flops_causal_strict": strict,
         "dense_kernel_ms": dense_ms,
