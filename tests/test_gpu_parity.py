@@ -78,6 +78,24 @@ def test_fp8_gqa8():
     _check_full(wl)
 
 
+@pytest.mark.parametrize("page_size", [0, 64, 6])
+def test_fp8_block64_varlen(page_size):
+    # FP8 products with 64-key blocks (one FP8 K DMA instruction per wave) on
+    # ragged requests, unsplit and split; paged K / V (page sizes with and
+    # without whole 8-row groups per page) must equal the contiguous layout
+    # bit for bit.
+    wl = synth.make_workload("qwen4b_varlen_paged", lengths=[700, 1333], Hq=8, Hkv=2, min_sparse_len=0,
+                             n_planted=3, B=64, fp8=True, page_size=page_size)
+    assert wl.dtype == "fp8" and wl.paged == (page_size > 0)
+    _check_full(wl, num_splits=1)
+    _check_full(wl, num_splits=3)
+    if page_size:
+        a = run_gpu(wl, paged=True, num_splits=1)
+        b = run_gpu(wl, paged=False, num_splits=1)
+        for key in ("row_ptr", "col_idx", "out", "lse"):
+            assert np.array_equal(a[key], b[key]), key
+
+
 def test_varlen_paged_min_sparse_len():
     wl = synth.make_workload("qwen4b_varlen_paged", lengths=[300, 1000, 2100, 129], Hq=8, Hkv=2,
                              min_sparse_len=1000, page_size=64)
