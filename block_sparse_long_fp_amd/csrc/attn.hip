@@ -16,15 +16,18 @@
 //     (KV head h, query block I): wave w owns 32 consecutive tokens of one
 //     query head. G*B rows per (h, I) are split over ceil(G*B/256) workgroups.
 //   * Transposed products keep every lane on one query: S^T = K Q^T and
-//     O^T = V^T P^T with v_mfma_f32_32x32x16_bf16. A lane (column c, half hf)
+//     O^T = V^T P^T with v_mfma_f32_32x32x16_bf16 (QK^T of FP8 inputs with
+//     v_mfma_f32_32x32x64_f8f6f4, below). A lane (column c, half hf)
 //     holds the scores and output dims of query c, so row max and row sum are
 //     in-lane plus one v_permlane32_swap, and the probabilities feed the PV
 //     product straight from registers (the PV contraction index is relabelled
 //     to match the score accumulator layout).
 //   * Work items: the CSR row's key blocks, then correction chunks of 64
 //     pooled columns whose per-column bias log2(n_J) or -inf masks selected
-//     and non-causal blocks (from an LDS bitmap of the row). Exact, diagonal
-//     and pooled items are separate instantiations of the item code.
+//     and non-causal blocks (from an LDS bitmap of the row). The kept blocks
+//     between the row's first and last item run through a pipelined
+//     instantiation without score adjustments; the diagonal block, the last
+//     kept block and the correction chunks through a general one.
 //   * Staging is direct HBM -> LDS (buffer_load ... lds / global_load_lds,
 //     16 bytes per lane) into double-buffered tiles, so no registers carry
 //     K or V. A tile stores rows in groups of four: group g (rows 4g..4g+3)
