@@ -163,10 +163,12 @@ def test_alpha_above_one_keeps_only_diagonal():
     assert np.array_equal(gpu["col_idx"], np.arange(nb))
 
 
-def test_single_token_and_one_block_requests():
+@pytest.mark.parametrize("fp8", [False, True])
+def test_single_token_and_one_block_requests(fp8):
     wl = synth.make_workload("qwen4b_varlen_paged", lengths=[1, 2, 127, 128, 129], Hq=4, Hkv=2, page_size=16,
-                             min_sparse_len=0, n_planted=0)
+                             min_sparse_len=0, n_planted=0, fp8=fp8)
     _check_full(wl)
+    _check_full(wl, paged=False, num_splits=1)
 
 
 @pytest.mark.parametrize("forced", [dict(sink=2, window=4, last_n=8), dict(sink=1, window=0, last_n=0),
