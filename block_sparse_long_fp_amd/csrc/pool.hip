@@ -5,7 +5,8 @@
 // queries and pools block-mean statistics) and Figure 4 (a pruned block is
 // represented by its mean key and mean value).
 //
-// Work split: one workgroup per (key block b of the ragged batch, KV head h). Its
+// Work split: one workgroup per (key block b of the ragged batch, KV head h),
+// the heads of one block consecutive. Its
 // threads own "slots" (the G query heads of the group, then K, then V) times
 // 16-byte column chunks of the 128-wide head dim, and split the block's tokens
 // into interleaved groups; every load is a 16-byte (bf16) or 8-byte (fp8)
@@ -43,13 +44,20 @@ __device__ __forceinline__ uint4 load_raw(const void* base, int64_t elem) {
   }
 }
 
+// FP8 codes are widened with the gfx950 conversion v_cvt_scalef32_pk_f32_fp8
+// (two codes per instruction, scale 1: exact, every E4M3 value is an fp32
+// value), which keeps the FP8 pass bound by memory rather than by decoding.
 template <bool FP8>
 __device__ __forceinline__ void add_raw(const uint4 w, float (&acc)[8]) {
   if constexpr (FP8) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] += e4m3_to_float((w.x >> (8 * i)) & 0xFFu);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[4 + i] += e4m3_to_float((w.y >> (8 * i)) & 0xFFu);
+    const f32x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w.x, 1.0f, false);
+    const f32x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w.x, 1.0f, true);
+    const f32x2 f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w.y, 1.0f, false);
+    const f32x2 f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w.y, 1.0f, true);
+    acc[0] += f0[0]; acc[1] += f0[1];
+    acc[2] += f1[0]; acc[3] += f1[1];
+    acc[4] += f2[0]; acc[5] += f2[1];
+    acc[6] += f3[0]; acc[7] += f3[1];
   } else {
     acc[0] += bf16_lo(w.x); acc[1] += bf16_hi(w.x);
     acc[2] += bf16_lo(w.y); acc[3] += bf16_hi(w.y);
@@ -77,18 +85,21 @@ __device__ __forceinline__ void sum_strided(const void* base, int64_t elem0, int
 template <bool FP8>
 __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolParams p) {
   extern __shared__ float part[];  // [groups][slots*kChunks][8]
-  const int h = blockIdx.y;
+  // Consecutive workgroups are the KV heads of one block, so the workgroups
+  // running together read whole token rows of Q, K and V.
+  const int h = (int)(blockIdx.x % (unsigned)p.Hkv);
+  const int bid = (int)(blockIdx.x / (unsigned)p.Hkv);
   const ReqTable& rt = p.rt;
-  // blockIdx.x: a global key block id in [0, NBk_tot), or with chunk_only a
-  // global query block id in [0, NBq_tot) whose key block is pooled.
+  // bid: a global key block id in [0, NBk_tot), or with chunk_only a global
+  // query block id in [0, NBq_tot) whose key block is pooled.
   int r = 0;
   int J;
   if (p.chunk_only) {
-    while (r + 1 < rt.R && rt.blk_off[r + 1] <= (int)blockIdx.x) ++r;
-    J = rt.qb0[r] + (int)blockIdx.x - rt.blk_off[r];
+    while (r + 1 < rt.R && rt.blk_off[r + 1] <= bid) ++r;
+    J = rt.qb0[r] + bid - rt.blk_off[r];
   } else {
-    while (r + 1 < rt.R && rt.kblk_off[r + 1] <= (int)blockIdx.x) ++r;
-    J = (int)blockIdx.x - rt.kblk_off[r];
+    while (r + 1 < rt.R && rt.kblk_off[r + 1] <= bid) ++r;
+    J = bid - rt.kblk_off[r];
   }
   const int b = rt.kblk_off[r] + J;  // global key block id
   const int L = rt.ktok_off[r + 1] - rt.ktok_off[r];
@@ -190,7 +201,7 @@ size_t pool_lds_bytes(int G) {
 }
 
 hipError_t launch_pool(const PoolParams& p, hipStream_t stream) {
-  dim3 grid(p.chunk_only ? p.NBq_tot : p.NBk_tot, p.Hkv);
+  dim3 grid((unsigned)p.Hkv * (unsigned)(p.chunk_only ? p.NBq_tot : p.NBk_tot));
   const size_t lds = pool_lds_bytes(p.G);
   if (p.fp8)
     hipLaunchKernelGGL(pool_kernel<true>, grid, dim3(kPoolThreads), lds, stream, p);
