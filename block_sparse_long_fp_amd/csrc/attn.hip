@@ -1254,7 +1254,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
 
 // Conversion pass before the attention kernel (one launch, grid-stride):
 // bf16 copies of k_bar, v_bar in code units (divided by the K / V descales
-// for FP8), and for FP8 the V codes as bf16 (exact; K stays FP8).
+// for FP8), and for FP8 the V codes as bf16 (exact, two codes per
+// v_cvt_scalef32_pk_bf16_fp8; K stays FP8).
 __global__ __launch_bounds__(256) void prep_kernel(AttnParams p, int64_t n_pool8, int64_t n_kv8) {
   const float ks = p.fp8 ? 1.f / *p.descale_k : 1.f;
   const float vs = p.fp8 ? 1.f / *p.descale_v : 1.f;
@@ -1276,12 +1277,11 @@ __global__ __launch_bounds__(256) void prep_kernel(AttnParams p, int64_t n_pool8
     } else {
       const int64_t k8 = i - 2 * n_pool8;
       const uint2 c = reinterpret_cast<const uint2*>(p.v)[k8];
-      uint4 o;
-      o.x = pack_bf16x2(e4m3_to_float(c.x & 0xFF), e4m3_to_float((c.x >> 8) & 0xFF));
-      o.y = pack_bf16x2(e4m3_to_float((c.x >> 16) & 0xFF), e4m3_to_float(c.x >> 24));
-      o.z = pack_bf16x2(e4m3_to_float(c.y & 0xFF), e4m3_to_float((c.y >> 8) & 0xFF));
-      o.w = pack_bf16x2(e4m3_to_float((c.y >> 16) & 0xFF), e4m3_to_float(c.y >> 24));
-      reinterpret_cast<uint4*>(const_cast<void*>(p.vv))[k8] = o;
+      const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, false);
+      const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, true);
+      const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, false);
+      const bf16x2 e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, true);
+      reinterpret_cast<bf16x8*>(const_cast<void*>(p.vv))[k8] = bf16x8{a[0], a[1], b[0], b[1], d[0], d[1], e[0], e[1]};
     }
   }
 }

@@ -57,19 +57,9 @@ __device__ __forceinline__ int64_t kv_elem_offset(const KVAddr& a, const ReqTabl
   return (row * Hkv + h) * kHeadDim;
 }
 
-// OCP E4M3 (FN) byte -> float, exact. gfx950 uses the OCP encoding.
-__device__ __forceinline__ float e4m3_to_float(uint32_t c) {
-  const uint32_t s = (c & 0x80u) << 24;
-  const uint32_t e = (c >> 3) & 0xFu;
-  const uint32_t m = c & 0x7u;
-  float v;
-  if (e == 0) {
-    v = (float)m * 0.001953125f;  // m/8 * 2^-6
-  } else {
-    v = __uint_as_float(((e + 120u) << 23) | (m << 20));  // (1+m/8) * 2^(e-7)
-  }
-  return __uint_as_float(__float_as_uint(v) | s);
-}
+// FP8 inputs are OCP E4M3 (FN) codes, the encoding the gfx950 conversion
+// and matrix instructions take (v_cvt_scalef32_pk_*_fp8 with scale 1 widen
+// them exactly).
 
 // bf16 <-> float helpers on raw bits.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
