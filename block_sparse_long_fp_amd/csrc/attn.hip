@@ -59,11 +59,13 @@
 //     inside fp32; the result is exact after the final division.
 //   * Workgroups run heaviest first (query block index descending over the
 //     ragged batch). Consecutive ids cycle over KV heads, and the head of each
-//     id slot rotates every kHeadRotate query blocks: the round-robin XCD
+//     id slot rotates every kRotateSpan / Hkv query blocks: the round-robin XCD
 //     dispatch then keeps a head's K/V in one L2 across neighbouring rows
 //     while every XCD sees every head (the heads' kept counts differ by up
 //     to 14 % at 128K, and a fixed head per XCD let the busiest one set the
-//     kernel time: 9.62 -> 8.61 ms).
+//     kernel time: 9.62 -> 8.61 ms). The period measured best at 16 query
+//     blocks with 8 KV heads (9.0 ms against 9.0-9.4 for 1 .. 128) and at 32
+//     with 4 (6.84 against 6.96 ms for 16).
 //   * Split-KV ([digest] Table 7: count-balanced CSR splits): when a launch
 //     has too few rows to fill the chip, each row's item list is cut into
 //     `splits` consecutive parts of equal cost (an exact block counts 2, a
@@ -95,9 +97,9 @@ constexpr int kContig = 0, kPagedAny = 1, kPaged4 = 2;
 constexpr int kOct = 8 * 128 + 128;
 constexpr int kSlab8 = 8 * kWaves;      // FP8 K rows one DMA instruction of every wave fills
 
-// Query blocks after which the KV head of a work-unit slot moves on (see
+// A work-unit slot keeps its KV head for kRotateSpan / Hkv query blocks (see
 // decode_work).
-constexpr int kHeadRotate = 16;
+constexpr int kRotateSpan = 128;
 constexpr int kColCache = 1024;         // CSR columns cached in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -469,10 +471,10 @@ __device__ __forceinline__ void decode_work(const AttnParams& p, int& I, int& r,
   const int rem = blockIdx.x - pk * U;
   // Slot rem of the units of one query block runs on XCD rem % 8 (workgroups
   // go round-robin over the eight XCDs). Giving a slot the same KV head for
-  // kHeadRotate query blocks keeps that head's K / V tiles in one XCD's L2
+  // kRotateSpan / Hkv query blocks keeps that head's K / V tiles in one XCD's L2
   // across neighbouring rows; moving on afterwards spreads every head over
   // every XCD, so one head with more kept blocks does not hold back its XCD.
-  h = (rem + pk / kHeadRotate) % p.Hkv;
+  h = (rem + pk / max(1, kRotateSpan / p.Hkv)) % p.Hkv;
   const int rem2 = rem / p.Hkv;
   sub = rem2 % p.subs;
   split = rem2 / p.subs;
