@@ -60,6 +60,7 @@ class _Problem(ctypes.Structure):
         ("num_pages", ctypes.c_int32),
         ("cu_seqlens_k", ctypes.POINTER(ctypes.c_int32)),
         ("pooled_pitch", ctypes.c_int32),
+        ("pooled_row_off", ctypes.POINTER(ctypes.c_int32)),
     ]
 
 
@@ -122,6 +123,117 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+# --------------------------------------------------------------------------
+# Argument checks of the binding. The C ABI takes raw pointers, so it cannot
+# see a tensor's dtype, device, strides or size; these checks run before any
+# library call and raise FpError with the status code the C side uses for
+# the same class of mistake. Every operand is checked for dtype, shape and
+# contiguity first, then all of them for being on one GPU.
+# --------------------------------------------------------------------------
+
+FP_ERR_NULL, FP_ERR_SHAPE, FP_ERR_DTYPE, FP_ERR_LAYOUT, FP_ERR_WORKSPACE = 1, 2, 5, 6, 8
+_ELEM = {FP_BF16: torch.bfloat16, FP_FP8_E4M3: torch.float8_e4m3fn}
+
+
+def _tensor(t, name: str, dtype, shape=None, min_rows=None, flat_min: Optional[int] = None,
+            shape_code: int = FP_ERR_SHAPE):
+    """Raise FpError unless ``t`` is a contiguous tensor of ``dtype`` and of
+    ``shape`` (a tuple; with ``min_rows`` the first dim may be larger), or
+    with ``flat_min`` 1-D with at least that many elements."""
+    if t is None:
+        raise FpError(FP_ERR_NULL, f"{name} is None")
+    if not isinstance(t, torch.Tensor):
+        raise FpError(FP_ERR_LAYOUT, f"{name} is a {type(t).__name__}, not a torch.Tensor")
+    if t.dtype != dtype:
+        raise FpError(FP_ERR_DTYPE, f"{name} has dtype {t.dtype}, expected {dtype}")
+    got = tuple(t.shape)
+    if flat_min is not None:
+        if t.dim() != 1 or t.numel() < flat_min:
+            raise FpError(shape_code, f"{name} has shape {got}, expected 1-D with >= {flat_min} elements")
+    elif shape is not None:
+        if min_rows is not None:
+            ok = len(got) == len(shape) and got[0] >= min_rows and got[1:] == tuple(shape[1:])
+        else:
+            ok = got == tuple(shape)
+        if not ok:
+            want = ("(>= %d, %s)" % (min_rows, ", ".join(map(str, shape[1:])))) if min_rows is not None else shape
+            raise FpError(shape_code, f"{name} has shape {got}, expected {want}")
+    if not t.is_contiguous():
+        raise FpError(FP_ERR_LAYOUT, f"{name} is not contiguous (strides {tuple(t.stride())})")
+    return t
+
+
+def _one_gpu(named):
+    """All tensors of ``named`` (name -> tensor or None) on one GPU; returns it."""
+    dev = None
+    for name, t in named:
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise FpError(FP_ERR_LAYOUT, f"{name} is on {t.device}, not on a GPU")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise FpError(FP_ERR_LAYOUT, f"{name} is on {t.device}, the other operands on {dev}")
+    return dev
+
+
+def _qkv_checks(prob: "Problem", q, k, v):
+    """Q [Tq, Hq, d]; K, V [Tk, Hkv, d] or page pools [pages, page_size, Hkv, d];
+    all of the problem's element type; FP8 descales and the page table.
+    Returns the (name, tensor) pairs checked."""
+    s = prob.s
+    d = s.head_dim
+    el = _ELEM.get(s.dtype)
+    if el is None:
+        raise FpError(FP_ERR_DTYPE, f"unknown dtype code {s.dtype}")
+    # Inputs may hold more leading rows than the call reads (a buffer sized for
+    # a whole prompt, a page pool with spare pages); the kernels read rows
+    # below Tq / Tk / num_pages only.
+    if s.kv_layout == FP_KV_PAGED:
+        kv_shape = (s.num_pages, s.page_size, s.num_kv_heads, d)
+    else:
+        kv_shape = (prob.Tk, s.num_kv_heads, d)
+    named = [("q", _tensor(q, "q", el, (prob.Tq, s.num_q_heads, d), min_rows=prob.Tq)),
+             ("k", _tensor(k, "k", el, kv_shape, min_rows=kv_shape[0])),
+             ("v", _tensor(v, "v", el, kv_shape, min_rows=kv_shape[0]))]
+    if s.dtype == FP_FP8_E4M3:
+        if prob.descales is None:
+            raise FpError(FP_ERR_DTYPE, "FP8 inputs need descale_q, descale_k and descale_v")
+        for name, t in zip(("descale_q", "descale_k", "descale_v"), prob.descales):
+            named.append((name, _tensor(t, name, torch.float32, (1,))))
+    if s.kv_layout == FP_KV_PAGED:
+        named.append(("page_table", _tensor(prob.page_table, "page_table", torch.int32,
+                                            (prob.num_seqs, s.max_pages_per_seq), min_rows=prob.num_seqs)))
+    return named
+
+
+def _pooled_checks(prob: "Problem", q_bar=None, k_bar=None, v_bar=None):
+    """Returns (CSR rows, checked pairs)."""
+    rows, nnz, nbq, nbk = index_shape(prob)
+    pitch = prob.s.pooled_pitch or nbk
+    Hkv, d = prob.s.num_kv_heads, prob.s.head_dim
+    named = []
+    if q_bar is not None:
+        named.append(("q_bar", _tensor(q_bar, "q_bar", torch.float32, (Hkv, nbq, d))))
+    for name, t in (("k_bar", k_bar), ("v_bar", v_bar)):
+        if t is not None:
+            named.append((name, _tensor(t, name, torch.float32, (Hkv, pitch, d))))
+    return rows, named
+
+
+def _out_checks(prob: "Problem", out, lse):
+    s = prob.s
+    named = [("out", _tensor(out, "out", torch.bfloat16, (prob.Tq, s.num_q_heads, s.head_dim)))]
+    if lse is not None:
+        named.append(("lse", _tensor(lse, "lse", torch.float32, (s.num_q_heads, prob.Tq))))
+    return named
+
+
+def _workspace_check(ws, name="workspace"):
+    return [(name, _tensor(ws, name, torch.uint8, flat_min=1, shape_code=FP_ERR_WORKSPACE))]
+
+
 def _stream(stream=None):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -139,7 +251,8 @@ class Problem:
     def __init__(self, cu_seqlens: Sequence[int], num_q_heads: int, num_kv_heads: int, block_size: int,
                  head_dim: int = 128, dtype: int = FP_BF16, descales: Optional[Sequence[torch.Tensor]] = None,
                  page_table: Optional[torch.Tensor] = None, page_size: int = 0, num_pages: int = 0,
-                 cu_seqlens_k: Optional[Sequence[int]] = None, pooled_pitch: int = 0):
+                 cu_seqlens_k: Optional[Sequence[int]] = None, pooled_pitch: int = 0,
+                 pooled_row_off: Optional[Sequence[int]] = None):
         cu = [int(x) for x in cu_seqlens]
         self.cu_seqlens = cu
         self.cu_seqlens_k = cu if cu_seqlens_k is None else [int(x) for x in cu_seqlens_k]
@@ -152,6 +265,11 @@ class Problem:
             self._cuk = (ctypes.c_int32 * len(self.cu_seqlens_k))(*self.cu_seqlens_k)
             s.cu_seqlens_k = ctypes.cast(self._cuk, ctypes.POINTER(ctypes.c_int32))
         s.pooled_pitch = pooled_pitch
+        if pooled_row_off is not None:
+            self._prow = (ctypes.c_int32 * len(pooled_row_off))(*[int(x) for x in pooled_row_off])
+            s.pooled_row_off = ctypes.cast(self._prow, ctypes.POINTER(ctypes.c_int32))
+        self.descales = list(descales) if descales is not None else None
+        self.page_table = page_table
         s.num_q_heads, s.num_kv_heads, s.head_dim, s.block_size = num_q_heads, num_kv_heads, head_dim, block_size
         s.dtype = dtype
         if descales is not None:
@@ -171,6 +289,18 @@ class Problem:
     @property
     def ref(self):
         return ctypes.byref(self.s)
+
+    @property
+    def num_seqs(self) -> int:
+        return len(self.cu_seqlens) - 1
+
+    @property
+    def Tq(self) -> int:
+        return self.cu_seqlens[-1]
+
+    @property
+    def Tk(self) -> int:
+        return self.cu_seqlens_k[-1]
 
 
 def index_shape(prob: Problem):
@@ -228,6 +358,7 @@ def validate(prob: Problem, sel: Optional[_SelectArgs] = None, attn: Optional[_A
 
 
 def pool_blocks(prob: Problem, q, k, v, q_bar, k_bar, v_bar, stream=None):
+    _one_gpu(_qkv_checks(prob, q, k, v) + _pooled_checks(prob, q_bar, k_bar, v_bar)[1])
     _check(lib().fp_pool_blocks(prob.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(q_bar), _ptr(k_bar), _ptr(v_bar),
                                 _stream(stream)))
 
@@ -235,11 +366,18 @@ def pool_blocks(prob: Problem, q, k, v, q_bar, k_bar, v_bar, stream=None):
 def pool_chunk_blocks(prob: Problem, q, k, v, q_bar, k_bar, v_bar, stream=None):
     """fp_pool_chunk_blocks: pools q_bar and only the key blocks the chunk
     adds; k_bar / v_bar rows of earlier blocks must hold earlier calls' values."""
+    _one_gpu(_qkv_checks(prob, q, k, v) + _pooled_checks(prob, q_bar, k_bar, v_bar)[1])
     _check(lib().fp_pool_chunk_blocks(prob.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(q_bar), _ptr(k_bar),
                                       _ptr(v_bar), _stream(stream)))
 
 
 def select_blocks(prob: Problem, sel: _SelectArgs, q_bar, k_bar, row_ptr, col_idx, workspace, stream=None):
+    rows, named = _pooled_checks(prob, q_bar, k_bar)
+    if q_bar is None or k_bar is None:
+        raise FpError(FP_ERR_NULL, "q_bar and k_bar are required")
+    named += [("row_ptr", _tensor(row_ptr, "row_ptr", torch.int32, (rows + 1,))),
+              ("col_idx", _tensor(col_idx, "col_idx", torch.int32, flat_min=1))]
+    _one_gpu(named + _workspace_check(workspace))
     _check(lib().fp_select_blocks(prob.ref, ctypes.byref(sel), _ptr(q_bar), _ptr(k_bar), _ptr(row_ptr),
                                   _ptr(col_idx), col_idx.numel(), _ptr(workspace), workspace.numel(),
                                   _stream(stream)))
@@ -249,6 +387,16 @@ def sparse_prefill(prob: Problem, attn: _AttnArgs, q, k, v, k_bar, v_bar, row_pt
                    workspace=None, stream=None):
     """fp_sparse_prefill; ``workspace`` (uint8 device tensor of at least
     attn_workspace_bytes(prob, True) bytes) is allocated here when None."""
+    named = _qkv_checks(prob, q, k, v)
+    rows, pooled = _pooled_checks(prob, None, k_bar, v_bar)
+    if attn.mean_correction and (k_bar is None or v_bar is None):
+        raise FpError(FP_ERR_NULL, "mean correction needs k_bar and v_bar")
+    named += pooled + [("row_ptr", _tensor(row_ptr, "row_ptr", torch.int32, (rows + 1,))),
+                       ("col_idx", _tensor(col_idx, "col_idx", torch.int32, flat_min=1))]
+    named += _out_checks(prob, out, lse)
+    if workspace is not None:
+        named += _workspace_check(workspace)
+    _one_gpu(named)
     workspace = _attn_workspace(prob, True, workspace, out.device, attn)
     nbytes = 0 if workspace is None else workspace.numel()
     _check(lib().fp_sparse_prefill(prob.ref, ctypes.byref(attn), _ptr(q), _ptr(k), _ptr(v), _ptr(k_bar),
@@ -258,6 +406,10 @@ def sparse_prefill(prob: Problem, attn: _AttnArgs, q, k, v, k_bar, v_bar, row_pt
 
 def dense_prefill(prob: Problem, attn: _AttnArgs, q, k, v, out, lse=None, workspace=None, stream=None):
     """fp_dense_prefill; ``workspace`` as in sparse_prefill (only FP8 needs one)."""
+    named = _qkv_checks(prob, q, k, v) + _out_checks(prob, out, lse)
+    if workspace is not None:
+        named += _workspace_check(workspace)
+    _one_gpu(named)
     workspace = _attn_workspace(prob, False, workspace, out.device, attn)
     nbytes = 0 if workspace is None else workspace.numel()
     _check(lib().fp_dense_prefill(prob.ref, ctypes.byref(attn), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
@@ -316,7 +468,12 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: Seque
     """
     Hq = q.shape[1]
     Hkv = k.shape[-2]
-    dtype = FP_FP8_E4M3 if q.dtype == torch.float8_e4m3fn else FP_BF16
+    if q.dtype == torch.bfloat16:
+        dtype = FP_BF16
+    elif q.dtype == torch.float8_e4m3fn:
+        dtype = FP_FP8_E4M3
+    else:
+        raise FpError(FP_ERR_DTYPE, f"q has dtype {q.dtype}; the kernels take bfloat16 or float8_e4m3fn")
     prob = Problem(cu_seqlens, Hq, Hkv, block_size, q.shape[-1], dtype, descales, page_table, page_size,
                    k.shape[0] if page_table is not None else 0, cu_seqlens_k)
     bufs = Buffers(prob, q.device, q.shape[-1])

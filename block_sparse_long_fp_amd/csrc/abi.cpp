@@ -112,6 +112,32 @@ fp_status check_problem(const fp_problem* p, Shape* sh) {
   }
   if (p->pooled_pitch != 0 && p->pooled_pitch < nbk_tot)
     return fail(FP_ERR_SHAPE, "pooled_pitch=%d < %lld key blocks", p->pooled_pitch, (long long)nbk_tot);
+  if (p->pooled_row_off) {
+    // Each request's rows [base, base + NBk_r) lie below the pitch, and no
+    // two requests' rows overlap (checked on the intervals sorted by base).
+    const int64_t pitch = p->pooled_pitch ? p->pooled_pitch : nbk_tot;
+    int order[FP_MAX_SEQS];
+    int64_t nbk_of[FP_MAX_SEQS];
+    for (int r = 0; r < p->num_seqs; ++r) {
+      order[r] = r;
+      nbk_of[r] = ((int64_t)cuk[r + 1] - cuk[r] + B - 1) / B;
+      const int64_t base = p->pooled_row_off[r];
+      if (base < 0 || base + nbk_of[r] > pitch)
+        return fail(FP_ERR_SHAPE, "pooled_row_off[%d]=%lld: rows up to %lld exceed the pitch %lld", r,
+                    (long long)base, (long long)(base + nbk_of[r]), (long long)pitch);
+    }
+    for (int i = 1; i < p->num_seqs; ++i)  // insertion sort by base (R <= 128)
+      for (int j = i; j > 0 && p->pooled_row_off[order[j]] < p->pooled_row_off[order[j - 1]]; --j) {
+        const int t = order[j];
+        order[j] = order[j - 1];
+        order[j - 1] = t;
+      }
+    for (int i = 1; i < p->num_seqs; ++i) {
+      const int a = order[i - 1], b = order[i];
+      if ((int64_t)p->pooled_row_off[a] + nbk_of[a] > p->pooled_row_off[b])
+        return fail(FP_ERR_SHAPE, "pooled rows of requests %d and %d overlap", a, b);
+    }
+  }
   s.NBq_tot = nbq_tot;
   s.NBk_tot = nbk_tot;
   s.kpitch = p->pooled_pitch ? p->pooled_pitch : nbk_tot;
@@ -124,7 +150,8 @@ fp_status check_problem(const fp_problem* p, Shape* sh) {
 fp_status check_select(const fp_select_args* a) {
   if (!a) return fail(FP_ERR_NULL, "select args are NULL");
   if (std::isnan(a->alpha)) return fail(FP_ERR_ARG, "alpha is NaN");
-  if (!std::isfinite(a->sel_scale)) return fail(FP_ERR_ARG, "sel_scale must be finite");
+  if (!std::isfinite(a->sel_scale) || !(a->sel_scale > 0.f))
+    return fail(FP_ERR_ARG, "sel_scale=%g must be finite and > 0", (double)a->sel_scale);
   if (a->min_sparse_len < 0) return fail(FP_ERR_ARG, "min_sparse_len=%d must be >= 0", a->min_sparse_len);
   if (a->sink_blocks < 0 || a->window_blocks < 0 || a->last_n_blocks < 0)
     return fail(FP_ERR_ARG, "sink_blocks=%d window_blocks=%d last_n_blocks=%d must be >= 0", a->sink_blocks,
@@ -183,6 +210,7 @@ ReqTable make_table(const fp_problem* p, const Shape& s) {
     t.kblk_off[r + 1] = t.kblk_off[r] + (Lk + B - 1) / B;
     t.qb0[r] = (Lk - Lq) / B;
   }
+  for (int r = 0; r < s.R; ++r) t.prow_off[r] = p->pooled_row_off ? p->pooled_row_off[r] : t.kblk_off[r];
   return t;
 }
 

@@ -147,7 +147,7 @@ struct RowCtx {
   int n_exact;          // CSR entries (key blocks) of the row
   int n_items;          // plus the correction chunks
   const int32_t* cols;  // CSR row (nullptr in dense mode)
-  int64_t pooled_row0;  // row h * kpitch + kblk_off[r] of k_bar / v_bar
+  int64_t pooled_row0;  // row h * kpitch + prow_off[r] of k_bar / v_bar
   int64_t tok_base;     // first key token of the request (contiguous K / V)
 };
 
@@ -1113,7 +1113,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   rc.cols = p.dense ? nullptr : p.col_idx + rp0;
   const bool do_corr = p.mean_correction && !p.dense && I > 0;
   rc.n_items = rc.n_exact + (do_corr ? (I + kPC - 1) / kPC : 0);
-  rc.pooled_row0 = (int64_t)rc.h * p.kpitch + rt.kblk_off[rc.r];
+  rc.pooled_row0 = (int64_t)rc.h * p.kpitch + rt.prow_off[rc.r];
 
   WaveState<BLK> ws;
   ws.m = kNegBig;

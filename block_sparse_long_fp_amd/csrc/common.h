@@ -34,6 +34,7 @@ struct ReqTable {
   int32_t blk_off[kMaxSeqs + 1];     // prefix sums of NBq_r (q_bar and CSR rows)
   int32_t kblk_off[kMaxSeqs + 1];    // prefix sums of NBk_r (k_bar and v_bar rows)
   int32_t qb0[kMaxSeqs];             // first query block's key-block id
+  int32_t prow_off[kMaxSeqs];        // first k_bar / v_bar row (per KV head) of each request
 };
 
 // K/V addressing: contiguous [T, Hkv, d] or paged [pages, page_size, Hkv, d].

@@ -101,7 +101,7 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolParams p) {
     while (r + 1 < rt.R && rt.kblk_off[r + 1] <= bid) ++r;
     J = bid - rt.kblk_off[r];
   }
-  const int b = rt.kblk_off[r] + J;  // global key block id
+  const int b = rt.prow_off[r] + J;  // k_bar / v_bar row of key block J (per KV head)
   const int L = rt.ktok_off[r + 1] - rt.ktok_off[r];
   const int t0 = J * p.B;
   const int n = min(p.B, L - t0);

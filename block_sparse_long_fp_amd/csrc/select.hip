@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(SelectParams p) {
   const int tid = threadIdx.x;
 
   const float* qsrc = p.q_bar + ((int64_t)h * p.NBq_tot + rt.blk_off[r]) * kHeadDim;
-  const float* ksrc = p.k_bar + ((int64_t)h * p.kpitch + rt.kblk_off[r]) * kHeadDim;
+  const float* ksrc = p.k_bar + ((int64_t)h * p.kpitch + rt.prow_off[r]) * kHeadDim;
   for (int e = tid; e < kTileI * (kHeadDim / 4); e += kScoreThreads) {
     const int rr = e / (kHeadDim / 4), c4 = e % (kHeadDim / 4);
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);

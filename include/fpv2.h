@@ -58,8 +58,9 @@
  *                           ([digest] "What they did", Fix 3; Table 7: paged KV,
  *                           arbitrary page size).
  *            pooled q_bar:  fp32 [Hkv, NBq_tot, d], row h * NBq_tot + blk_off[r] + i.
- *            pooled k_bar, v_bar: fp32 [Hkv, P, d], row h * P + kblk_off[r] + J,
- *                           P = pooled_pitch (NBk_tot when 0).
+ *            pooled k_bar, v_bar: fp32 [Hkv, P, d], row h * P + base_r + J,
+ *                           P = pooled_pitch (NBk_tot when 0), base_r =
+ *                           pooled_row_off[r] (kblk_off[r] when NULL).
  *            CSR:           one row per (h, r, i), row id h * NBq_tot + blk_off[r] + i;
  *                           row_ptr int32 [Hkv * NBq_tot + 1]; col_idx int32
  *                           request-local key-block ids J <= I, strictly
@@ -78,7 +79,7 @@
 extern "C" {
 #endif
 
-#define FPV2_ABI_VERSION 6
+#define FPV2_ABI_VERSION 7
 
 /* Status codes. */
 typedef int32_t fp_status;
@@ -132,6 +133,13 @@ typedef struct fp_problem {
   int32_t pooled_pitch;          /* rows per KV head of k_bar / v_bar: 0 means      */
                                  /* NBk_tot, else >= NBk_tot (a buffer sized for a  */
                                  /* whole prompt, reused across its chunks)         */
+  const int32_t* pooled_row_off; /* HOST [R] first k_bar / v_bar row (per KV head)  */
+                                 /* of each request, or NULL (= kblk_off[r]). Rows  */
+                                 /* base_r .. base_r + NBk_r - 1 must lie below the */
+                                 /* pitch and not overlap another request's. With a */
+                                 /* region per request sized for its whole prompt,  */
+                                 /* a batch of chunked requests keeps each request's */
+                                 /* pooled rows in place from chunk to chunk        */
 } fp_problem;
 
 /* Block selection ([digest] abstract: max-based dynamic thresholding;
@@ -145,7 +153,7 @@ typedef struct fp_problem {
  * last_n_blocks; in chunked prefill, the chunk's last blocks). */
 typedef struct fp_select_args {
   float alpha;                   /* threshold; alpha <= 0 keeps every causal block */
-  float sel_scale;               /* score temperature tau, finite                  */
+  float sel_scale;               /* score temperature tau, finite and > 0          */
   int32_t min_sparse_len;        /* requests with Lq_r < this keep every causal block */
   int32_t sink_blocks;           /* >= 0 */
   int32_t window_blocks;         /* >= 0 */
@@ -211,7 +219,10 @@ fp_status fp_pool_blocks(const fp_problem* p, const void* q, const void* k, cons
  * chunk are complete and their means do not change, so their k_bar / v_bar
  * rows are neither read nor written here: they must already hold the values
  * an earlier call wrote (typically the previous chunk's call on the same
- * buffers, with a pooled_pitch that fits the whole prompt). The pages note
+ * buffers, with a pooled_pitch that fits the whole prompt). In a batch of
+ * several requests their rows only stay in place from call to call when
+ * pooled_row_off fixes each request's region (kblk_off[r] moves as earlier
+ * requests gain blocks). The pages note
  * that per-chunk selection repeats Stage 1 for every chunk ([podcast]);
  * this call keeps that repeated work proportional to the chunk. With
  * off_r = 0 it equals fp_pool_blocks. */

@@ -190,9 +190,10 @@ def test_argument_validation():
     with pytest.raises(fp.FpError) as e:
         fp.validate(p, fp.select_args(float("nan")))
     assert e.value.code == 9
-    with pytest.raises(fp.FpError) as e:
-        fp.validate(p, fp.select_args(0.3, float("inf")))
-    assert e.value.code == 9
+    for tau in (float("inf"), 0.0, -1.0, float("nan")):
+        with pytest.raises(fp.FpError) as e:
+            fp.validate(p, fp.select_args(0.3, tau))
+        assert e.value.code == 9
     with pytest.raises(fp.FpError) as e:
         fp.validate(p, None, fp.attn_args(-1.0))
     assert e.value.code == 9

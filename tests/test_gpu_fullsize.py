@@ -5,7 +5,9 @@ At these sizes the oracle computes pooling and selection for the whole layer
 (the CSR is compared bit-exactly outside the near-threshold band) and the
 attention outputs for sampled rows: the first, second, middle and last query
 block of the first and last KV head of every request (which covers ragged
-tails and the heaviest rows), plus random rows.
+tails), each KV head's row with the most kept blocks, rows that the
+near-threshold band touches, plus random rows. Each test prints one
+``[margin]`` line with the errors it measured against the bounds.
 """
 import math
 
@@ -52,7 +54,7 @@ def _check(name, alpha=None, n_random=6, **over):
     compare_pooled(gpu, orc)
     n_near = compare_csr(gpu, orc)
     # attention on sampled rows, with the CSR the GPU chose
-    rows = rows_for_sample(wl, n_random=n_random)
+    rows = rows_for_sample(wl, n_random=n_random, row_ptr=gpu["row_ptr"], near=orc.near)
     sets = sets_from_csr(gpu["row_ptr"], gpu["col_idx"], orc.blk_off, wl.num_kv_heads)
     NBt = orc.blk_off[-1]
     G = wl.num_q_heads // wl.num_kv_heads
@@ -70,11 +72,15 @@ def _check(name, alpha=None, n_random=6, **over):
         t0 = s + I * B
         o_ref[t0:t0 + o.shape[0], h * G:(h + 1) * G] = o
         lse_ref[h * G:(h + 1) * G, t0:t0 + o.shape[0]] = l.T
-    o_err, l_err = compare_outputs(gpu["out"], gpu["lse"], o_ref, lse_ref, O_TOL[wl.dtype])
+    o_err, l_rel, l_abs = compare_outputs(gpu["out"], gpu["lse"], o_ref, lse_ref, O_TOL[wl.dtype])
     nnz = int(gpu["row_ptr"][-1])
     pairs = wl.num_kv_heads * sum(nb * (nb + 1) // 2 for nb in np.diff(orc.blk_off))
-    print(f"[fullsize] ok: nnz={nnz} kept={nnz / pairs:.4f} near_rows={n_near} rows_checked={len(rows)} "
-          f"O_err={o_err:.2e} LSE_err={l_err:.2e}", flush=True)
+    max_cols = int(np.diff(gpu["row_ptr"]).max())
+    print(f"[margin] workload={name} alpha={alpha} dtype={wl.dtype} nnz={nnz} kept={nnz / pairs:.4f} "
+          f"near_pairs={len(orc.near)} near_rows={n_near} rows_checked={len(rows)} "
+          f"query_rows_checked={int((~np.isnan(lse_ref)).sum())} max_row_cols={max_cols} "
+          f"O_err={o_err:.3e} O_tol={O_TOL[wl.dtype]} LSE_rel={l_rel:.3e} LSE_abs={l_abs:.3e} LSE_tol=1e-3",
+          flush=True)
     return gpu
 
 

@@ -234,6 +234,72 @@ def test_threshold_nesting_and_limits():
             assert set(sets[h][I].tolist()) == {int(np.argmax(z)), I}
 
 
+# ---------------------------------------------------------------- P7b temperature and band
+
+def _spread_pooled(seed, tau=1.0, Hkv=2, NB=40, d=16):
+    """Pooled rows whose tempered scores tau * z spread over about 20 nats
+    below the row max whatever tau, so that alphas and temperatures move many
+    blocks across the threshold."""
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((Hkv, NB, d)), rng.standard_normal((Hkv, NB, d)) * (1.2 / tau)
+
+
+def _as_sets(sets):
+    return [[set(r.tolist()) for r in per_h] for per_h in sets]
+
+
+@pytest.mark.parametrize("tau", [1.0 / math.sqrt(128), 0.5, 2.0, 3.0])
+def test_temperature_is_a_power_of_alpha(tau):
+    """For tau > 0, exp(tau (z - m)) >= alpha  <=>  exp(z - m) >= alpha^(1/tau):
+    selection at temperature tau equals selection at tau = 1 with alpha
+    raised to 1/tau. A tau that is dropped, applied twice, applied to the
+    threshold instead of the scores, or multiplied into alpha fails this (the
+    test also checks that those readings select differently on these
+    inputs)."""
+    qbar, kbar = _spread_pooled(40, tau)
+    for alpha in (0.05, 0.3, 0.7):
+        got = _as_sets(oracle.select_blocks(qbar, kbar, alpha, sel_scale=tau)[0])
+        want = _as_sets(oracle.select_blocks(qbar, kbar, alpha ** (1.0 / tau), sel_scale=1.0)[0])
+        assert got == want
+        # the plausible slips select a different set here
+        for wrong in (alpha, alpha ** (1.0 / tau ** 2), alpha * tau, alpha ** tau):
+            assert _as_sets(oracle.select_blocks(qbar, kbar, wrong, sel_scale=1.0)[0]) != want
+
+
+def test_temperature_scales_the_pooled_dot_product():
+    """z = tau * qbar . kbar: scaling qbar by c and tau by 1/c leaves every
+    decision unchanged, while scaling qbar alone changes them."""
+    qbar, kbar = _spread_pooled(41)
+    base = _as_sets(oracle.select_blocks(qbar, kbar, 0.3, sel_scale=1.5)[0])
+    assert _as_sets(oracle.select_blocks(qbar * 4.0, kbar, 0.3, sel_scale=1.5 / 4.0)[0]) == base
+    assert _as_sets(oracle.select_blocks(qbar * 4.0, kbar, 0.3, sel_scale=1.5)[0]) != base
+
+
+@pytest.mark.parametrize("tau", [1.0, 0.25, 3.0])
+@pytest.mark.parametrize("alpha", [0.3, 0.01])
+def test_near_threshold_band_width(tau, alpha):
+    """The exclusion band: a pair is listed near iff |exp(tau (z - m)) - alpha|
+    <= 1e-4 alpha, and forced pairs are never listed. One row with scores
+    built so that the probability ratios are exactly alpha (1 +- 5e-5)
+    (inside the band: listed, kept above and pruned below) and alpha
+    (1 +- 5e-4) (outside: not listed); the diagonal is forced."""
+    d, I = 4, 5
+    ratios = {1: alpha * (1 + 5e-5), 2: alpha * (1 - 5e-5), 3: alpha * (1 + 5e-4), 4: alpha * (1 - 5e-4),
+              5: alpha * 1e-3}
+    kbar = np.zeros((1, I + 1, d))
+    for J, r in ratios.items():
+        kbar[0, J, 0] = math.log(r) / tau     # tau * qbar . kbar - m = ln r, with m = 0 at J = 0
+    qbar = np.zeros((1, I + 1, d))
+    qbar[0, I, 0] = 1.0
+    sets, near = oracle.select_blocks(qbar, kbar, alpha, sel_scale=tau)
+    assert set(sets[0][I].tolist()) == {0, 1, 3, 5}
+    assert sorted(J for (h, i, J) in near if i == I) == [1, 2]
+    # the diagonal stays unlisted when its ratio sits inside the band too
+    kbar[0, I, 0] = math.log(alpha * (1 - 2e-5)) / tau
+    sets, near = oracle.select_blocks(qbar, kbar, alpha, sel_scale=tau)
+    assert I in sets[0][I] and sorted(J for (h, i, J) in near if i == I) == [1, 2]
+
+
 # ---------------------------------------------------------------- P8 planted recovery
 
 def test_planted_recovery_tiny_workload():
