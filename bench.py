@@ -1,10 +1,11 @@
 #!/usr/bin/env python3
 """Benchmark of one mean-corrected block-sparse causal prefill layer on MI355X.
 
-One step = the whole hot path over one batch: block pooling (fp_pool_blocks),
-scoring + threshold + CSR (fp_select_blocks) and block-sparse attention with
-the fused mean correction (fp_sparse_prefill). Inputs are synthetic, seeded,
-and resident in HBM before timing starts.
+One step = the whole hot path over one batch: Stage 1 (fp_stage1: block
+pooling, then scoring + threshold + CSR) and block-sparse attention with the
+fused mean correction (fp_sparse_prefill). Inputs are synthetic, seeded, and
+resident in HBM before timing starts; L2 and MALL are flushed before every
+timed step.
 
 Default workload: the Llama-3.1-8B-shaped layer at 128K tokens (32 query / 8
 KV heads, head dim 128, block 128, bf16, alpha 0.3). Prints one JSON line.
@@ -103,6 +104,7 @@ def parse():
                     help="with --chunk: pool every key block so far in each chunk (no reuse)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--dense-reps", type=int, default=3, help="timed repetitions of the dense comparator")
     ap.add_argument("--cpu-rows", type=int, default=16, help="attention rows the CPU baseline computes")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
@@ -175,16 +177,42 @@ def stage1_bytes(wl):
         (nbq + 2 * nbk) * wl.num_kv_heads * d * 4
 
 
+def host_description():
+    """Cores this process may run on, the CPU model and the BLAS numpy calls
+    (vendor and thread count), for the CPU baseline record."""
+    info = {"affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": None, "blas": None, "blas_threads": None}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    info["cpu_model"] = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            info["blas"] = f"{blas[0].get('internal_api')} {blas[0].get('version')}"
+            info["blas_threads"] = int(blas[0].get("num_threads", 0)) or None
+    except Exception:  # pragma: no cover
+        pass
+    return info
+
+
+def timing_stats(ms):
+    """mean / median / min of a list of HIP-event times in ms."""
+    a = np.asarray(ms, dtype=np.float64)
+    return {"mean": float(a.mean()), "median": float(np.median(a)), "min": float(a.min())}
+
+
 def cpu_baseline(wl, row_ptr, n_rows, seed=0, mean_correction=True, forced=None):
     """Time the fp64 oracle on the host (pool + select for the whole layer,
     attention for a few sampled rows, extrapolated by computed key count)."""
     import torch
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+    host = host_description()
+    threads = host["blas_threads"] or host["affinity_cores"]
     t0 = time.perf_counter()
     def deq(t, s):
         x = t.to(torch.float32) if t.dtype == torch.float8_e4m3fn else t
@@ -220,7 +248,8 @@ def cpu_baseline(wl, row_ptr, n_rows, seed=0, mean_correction=True, forced=None)
     t_att = max(t_att_sample, 0.0) * total_cost / max(sample_cost, 1.0)
     sec = t_sel + t_att
     return dict(value=wl.dense_equiv_flops() / sec / 1e12, unit="TFLOP/s (dense-equivalent)", cores=threads,
-                kind="oracle", seconds_per_layer=sec,
+                kind="oracle", seconds_per_layer=sec, affinity_cores=host["affinity_cores"],
+                cpu_model=host["cpu_model"], blas=host["blas"],
                 sample=(f"fp64 numpy oracle: pool+select over all {nrows} rows ({t_sel:.1f} s), attention over "
                         f"{len(sample)} random rows ({t_att_sample:.1f} s) extrapolated by visited-key count to "
                         f"{t_att:.0f} s; input conversion {t_conv:.1f} s not counted"))
@@ -251,7 +280,6 @@ def run_chunked(args, wl, fp, torch, q, k, v, descales):
     # one k_bar / v_bar for the whole prompt: each chunk pools only its own key
     # blocks into it (unless --chunk-repool, which pools every block so far)
     k_bar, v_bar = jobs[0][3].k_bar, jobs[0][3].v_bar
-    pool = fp.pool_blocks if args.chunk_repool else fp.pool_chunk_blocks
     torch.cuda.synchronize()
 
     def step(evs=None):
@@ -260,21 +288,19 @@ def run_chunked(args, wl, fp, torch, q, k, v, descales):
             qc = q[s0:s0 + c]
             if ev is not None:
                 ev[0].record()
-            pool(prob, qc, k, v, b.q_bar, k_bar, v_bar)
+            fp.stage1(prob, sel, qc, k, v, b.q_bar, k_bar, v_bar, b.row_ptr, b.col_idx, b.workspace,
+                      chunk_only=not args.chunk_repool)
             if ev is not None:
                 ev[1].record()
-            fp.select_blocks(prob, sel, b.q_bar, k_bar, b.row_ptr, b.col_idx, b.workspace)
-            if ev is not None:
-                ev[2].record()
             fp.sparse_prefill(prob, att, qc, k, v, k_bar, v_bar, b.row_ptr, b.col_idx, b.out, b.lse,
                               b.attn_workspace)
             if ev is not None:
-                ev[3].record()
+                ev[2].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in jobs] for _ in range(args.steps)]
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in jobs] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
@@ -282,8 +308,8 @@ def run_chunked(args, wl, fp, torch, q, k, v, descales):
     wall = time.perf_counter() - t0
     def stage(a, b):
         return float(np.mean([sum(e[a].elapsed_time(e[b]) for e in se) for se in evs]))
-    pool_ms, sel_ms, att_ms = stage(0, 1), stage(1, 2), stage(2, 3)
-    ms = float(np.mean([se[0][0].elapsed_time(se[-1][3]) for se in evs]))
+    s1_ms, att_ms = stage(0, 1), stage(1, 2)
+    ms = float(np.mean([se[0][0].elapsed_time(se[-1][2]) for se in evs]))
     flops = strict = 0.0
     nnz = pairs = 0
     for s0, c, prob, b in jobs:
@@ -312,7 +338,7 @@ def run_chunked(args, wl, fp, torch, q, k, v, descales):
                    "alpha": wl.alpha, "mean_correction": not args.no_mean_correction,
                    "kept_fraction": nnz / max(pairs, 1), "nnz": nnz},
         "ms_per_layer": ms,
-        "stages_ms": {"pool": pool_ms, "select": sel_ms, "attention": att_ms},
+        "stages_ms": {"stage1": s1_ms, "attention": att_ms},
         "attn_mfma_frac_computed": achieved / peak,
         "attn_flops_computed": flops,
         "attn_flops_causal_strict": strict,
@@ -372,35 +398,52 @@ def main():
     sel = fp.select_args(wl.alpha, wl.sel_scale, wl.min_sparse_len, args.sink, args.window, args.last_n)
     torch.cuda.synchronize()
 
+    # Between timed steps a 512 MiB scratch write evicts L2 and the 256 MiB
+    # MALL, so no step starts with the previous step's data in cache; it runs
+    # outside the events.
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        fp.pool_blocks(prob, q, k, v, bufs.q_bar, bufs.k_bar, bufs.v_bar)
+        fp.stage1(prob, sel, q, k, v, bufs.q_bar, bufs.k_bar, bufs.v_bar, bufs.row_ptr, bufs.col_idx,
+                  bufs.workspace)
         if ev is not None:
             ev[1].record()
-        fp.select_blocks(prob, sel, bufs.q_bar, bufs.k_bar, bufs.row_ptr, bufs.col_idx, bufs.workspace)
-        if ev is not None:
-            ev[2].record()
         fp.sparse_prefill(prob, att, q, k, v, bufs.k_bar, bufs.v_bar, bufs.row_ptr, bufs.col_idx, bufs.out,
                           bufs.lse, bufs.attn_workspace)
         if ev is not None:
-            ev[3].record()
+            ev[2].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
+        flush.fill_(i & 1)
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    pool_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    sel_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    att_ms = [e[2].elapsed_time(e[3]) for e in evs]
-    step_ms = [e[0].elapsed_time(e[3]) for e in evs]
+    s1_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    att_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    step_ms = [e[0].elapsed_time(e[2]) for e in evs]
     ms = float(np.mean(step_ms))
+
+    # Stage 1 split into its pooling and selection calls (separate launches,
+    # timed apart from the steps above).
+    split_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(3)]
+    for i in range(len(split_ev)):
+        flush.fill_(i & 1)
+        split_ev[i][0].record()
+        fp.pool_blocks(prob, q, k, v, bufs.q_bar, bufs.k_bar, bufs.v_bar)
+        split_ev[i][1].record()
+        fp.select_blocks(prob, sel, bufs.q_bar, bufs.k_bar, bufs.row_ptr, bufs.col_idx, bufs.workspace)
+        split_ev[i][2].record()
+    torch.cuda.synchronize()
+    pool_ms = [e[0].elapsed_time(e[1]) for e in split_ev]
+    sel_ms = [e[1].elapsed_time(e[2]) for e in split_ev]
 
     row_ptr = bufs.row_ptr.cpu().numpy().astype(np.int64)
     col_idx = bufs.col_idx[: int(row_ptr[-1])].cpu().numpy()
@@ -412,18 +455,22 @@ def main():
     peak = PEAK_TFLOPS[wl.dtype]
     achieved = flops / (att_avg * 1e-3) / 1e12
 
-    dense_ms = None
+    dense = None
     if not args.no_dense:
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         dws = fp.attn_workspace_bytes(prob, False, att)
         dws = torch.empty(dws, dtype=torch.uint8, device="cuda:0") if dws else None
-        fp.dense_prefill(prob, att, q, k, v, bufs.out, bufs.lse, dws)
-        torch.cuda.synchronize()
-        e0.record()
-        fp.dense_prefill(prob, att, q, k, v, bufs.out, bufs.lse, dws)
-        e1.record()
-        torch.cuda.synchronize()
-        dense_ms = e0.elapsed_time(e1)
+        fp.dense_prefill(prob, att, q, k, v, bufs.out, bufs.lse, dws)   # warm-up
+        dense_ms = []
+        for i in range(args.dense_reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            flush.fill_(i & 1)
+            e0.record()
+            fp.dense_prefill(prob, att, q, k, v, bufs.out, bufs.lse, dws)
+            e1.record()
+            torch.cuda.synchronize()
+            dense_ms.append(e0.elapsed_time(e1))
+        dense = timing_stats(dense_ms)
+        dense["reps"] = len(dense_ms)
 
     rec = {
         "metric": METRIC,
@@ -458,15 +505,21 @@ def main():
             "csr_bytes": int(row_ptr[-1]) * 4 + len(row_ptr) * 4,
         },
         "ms_per_layer": ms,
-        "stages_ms": {"pool": float(np.mean(pool_ms)), "select": float(np.mean(sel_ms)), "attention": att_avg},
+        "ms_per_step_stats": timing_stats(step_ms),
+        "stages_ms": {"stage1": float(np.mean(s1_ms)), "attention": att_avg},
+        "stages_ms_stats": {"stage1": timing_stats(s1_ms), "attention": timing_stats(att_ms)},
+        "stage1_split_ms": {"pool": timing_stats(pool_ms), "select": timing_stats(sel_ms)},
+        "timing": "HIP events on the library's stream; L2 and MALL flushed (512 MiB write) before every timed "
+                  "step and dense repetition, outside the events",
         "attn_mfma_frac_computed": achieved / peak,
         # FP8: against the peak of its FP8 / bf16 product mix (= frac for bf16)
         "attn_mfma_frac_mixed_peak": achieved / mixed_peak(flops, exact_flops, wl.dtype),
         "attn_flops_computed": flops,
         "attn_flops_causal_strict": strict,
-        "dense_kernel_ms": dense_ms,
+        "dense_kernel_ms": None if dense is None else dense["mean"],
+        "dense_kernel_ms_stats": dense,
         "dense_equiv_flops": dense_eq,
-        "pool_hbm_gbs": stage1_bytes(wl) / (float(np.mean(pool_ms)) * 1e-3) / 1e9,
+        "pool_hbm_gbs": stage1_bytes(wl) / (float(np.median(pool_ms)) * 1e-3) / 1e9,
         "roofline": {
             "bound": "mfma",
             "achieved": achieved,

@@ -6,7 +6,7 @@ library has not been built, importing the compute functions raises at call
 time with a message that says so; there is no fallback path.
 
 Entry points mirror the C ABI in include/fpv2.h:
-  pool_blocks, pool_chunk_blocks, select_blocks, sparse_prefill, dense_prefill
+  pool_blocks, pool_chunk_blocks, select_blocks, stage1, sparse_prefill, dense_prefill
 plus the convenience ``prefill`` that allocates outputs and runs all three
 stages, and the host-only ``index_shape`` / ``select_workspace_bytes`` /
 ``attn_workspace_bytes`` / ``validate``.
@@ -93,6 +93,8 @@ def lib() -> ctypes.CDLL:
         L.fp_pool_chunk_blocks.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
         L.fp_select_blocks.argtypes = [P, ctypes.POINTER(_SelectArgs), vp, vp, vp, vp, ctypes.c_int64, vp,
                                        ctypes.c_size_t, vp]
+        L.fp_stage1.argtypes = [P, ctypes.POINTER(_SelectArgs), ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                ctypes.c_int64, vp, ctypes.c_size_t, vp]
         L.fp_attn_workspace_bytes.argtypes = [P, ctypes.POINTER(_AttnArgs), ctypes.c_int32,
                                               ctypes.POINTER(ctypes.c_size_t)]
         L.fp_attn_num_splits.argtypes = [P, ctypes.POINTER(_AttnArgs), ctypes.POINTER(ctypes.c_int32)]
@@ -101,7 +103,7 @@ def lib() -> ctypes.CDLL:
         L.fp_dense_prefill.argtypes = [P, ctypes.POINTER(_AttnArgs), vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         for f in ("fp_index_shape", "fp_select_workspace_bytes", "fp_attn_workspace_bytes", "fp_attn_num_splits",
                   "fp_validate",
-                  "fp_pool_blocks", "fp_pool_chunk_blocks", "fp_select_blocks", "fp_sparse_prefill",
+                  "fp_pool_blocks", "fp_pool_chunk_blocks", "fp_select_blocks", "fp_stage1", "fp_sparse_prefill",
                   "fp_dense_prefill"):
             getattr(L, f).restype = ctypes.c_int32
         L.fp_status_string.argtypes = [ctypes.c_int32]
@@ -383,6 +385,20 @@ def select_blocks(prob: Problem, sel: _SelectArgs, q_bar, k_bar, row_ptr, col_id
                                   _stream(stream)))
 
 
+def stage1(prob: Problem, sel: _SelectArgs, q, k, v, q_bar, k_bar, v_bar, row_ptr, col_idx, workspace,
+           chunk_only: bool = False, stream=None):
+    """fp_stage1: pooling (all key blocks, or with ``chunk_only`` only the ones
+    the chunk adds) and selection in two kernels."""
+    rows, named = _pooled_checks(prob, q_bar, k_bar, v_bar)
+    named += _qkv_checks(prob, q, k, v)
+    named += [("row_ptr", _tensor(row_ptr, "row_ptr", torch.int32, (rows + 1,))),
+              ("col_idx", _tensor(col_idx, "col_idx", torch.int32, flat_min=1))]
+    _one_gpu(named + _workspace_check(workspace))
+    _check(lib().fp_stage1(prob.ref, ctypes.byref(sel), 1 if chunk_only else 0, _ptr(q), _ptr(k), _ptr(v),
+                           _ptr(q_bar), _ptr(k_bar), _ptr(v_bar), _ptr(row_ptr), _ptr(col_idx), col_idx.numel(),
+                           _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
 def sparse_prefill(prob: Problem, attn: _AttnArgs, q, k, v, k_bar, v_bar, row_ptr, col_idx, out, lse=None,
                    workspace=None, stream=None):
     """fp_sparse_prefill; ``workspace`` (uint8 device tensor of at least
@@ -440,12 +456,18 @@ class Buffers:
 
 def run_prefill(prob: Problem, bufs: Buffers, q, k, v, alpha: float, sel_scale: float = 1.0,
                 min_sparse_len: int = 0, sm_scale: float = 0.0, mean_correction: bool = True, stream=None,
-                sink: int = 0, window: int = 0, last_n: int = 0, num_splits: int = 0):
+                sink: int = 0, window: int = 0, last_n: int = 0, num_splits: int = 0, fused_stage1: bool = True):
     """All three stages on preallocated buffers (nothing allocated here; the
-    buffers must have been sized with the same num_splits)."""
-    pool_blocks(prob, q, k, v, bufs.q_bar, bufs.k_bar, bufs.v_bar, stream)
-    select_blocks(prob, select_args(alpha, sel_scale, min_sparse_len, sink, window, last_n), bufs.q_bar, bufs.k_bar,
-                  bufs.row_ptr, bufs.col_idx, bufs.workspace, stream)
+    buffers must have been sized with the same num_splits). Stage 1 runs as
+    fp_stage1 (two kernels), or with ``fused_stage1=False`` as the separate
+    fp_pool_blocks and fp_select_blocks calls."""
+    sel = select_args(alpha, sel_scale, min_sparse_len, sink, window, last_n)
+    if fused_stage1:
+        stage1(prob, sel, q, k, v, bufs.q_bar, bufs.k_bar, bufs.v_bar, bufs.row_ptr, bufs.col_idx, bufs.workspace,
+               stream=stream)
+    else:
+        pool_blocks(prob, q, k, v, bufs.q_bar, bufs.k_bar, bufs.v_bar, stream)
+        select_blocks(prob, sel, bufs.q_bar, bufs.k_bar, bufs.row_ptr, bufs.col_idx, bufs.workspace, stream)
     sparse_prefill(prob, attn_args(sm_scale, mean_correction, num_splits), q, k, v, bufs.k_bar, bufs.v_bar,
                    bufs.row_ptr, bufs.col_idx, bufs.out, bufs.lse, bufs.attn_workspace, stream)
     return bufs

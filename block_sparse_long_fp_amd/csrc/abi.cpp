@@ -225,17 +225,33 @@ KVAddr make_kv(const fp_problem* p) {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Selection tiles: T query blocks of one (KV head, request) each.
+struct SelTiles {
+  int T;
+  int64_t per_head, total;
+};
+
+SelTiles sel_tiles(const fp_problem* p, const Shape& s) {
+  SelTiles st{};
+  st.T = select_tile_blocks((int64_t)p->num_kv_heads * s.NBq_tot);
+  for (int r = 0; r < p->num_seqs; ++r) {
+    const int64_t nbq = ((int64_t)p->cu_seqlens[r + 1] - p->cu_seqlens[r] + p->block_size - 1) / p->block_size;
+    st.per_head += (nbq + st.T - 1) / st.T;
+  }
+  st.total = st.per_head * p->num_kv_heads;
+  return st;
+}
+
+// Selection workspace: the tile ticket, then one look-back word per tile.
 struct WsLayout {
-  size_t z, rowmax, counts, total;
+  size_t ticket, status, total;
 };
 
 WsLayout ws_layout(const fp_problem* p, const Shape& s) {
   WsLayout w{};
-  const int64_t rows = (int64_t)p->num_kv_heads * s.NBq_tot;
-  w.z = 0;
-  w.rowmax = align256((size_t)p->num_kv_heads * s.pairs * sizeof(float));
-  w.counts = w.rowmax + align256((size_t)rows * sizeof(float));
-  w.total = w.counts + align256((size_t)rows * sizeof(int32_t));
+  w.ticket = 0;
+  w.status = 256;
+  w.total = w.status + align256((size_t)sel_tiles(p, s).total * sizeof(uint64_t));
   return w;
 }
 
@@ -326,11 +342,8 @@ fp_status fp_validate(const fp_problem* p, const fp_select_args* sel, const fp_a
   return ok();
 }
 
-static fp_status run_pool(const fp_problem* p, const void* q, const void* k, const void* v, float* q_bar,
-                          float* k_bar, float* v_bar, void* stream, bool chunk_only) {
-  Shape s;
-  fp_status st = check_problem(p, &s);
-  if (st) return st;
+static fp_status prep_pool(const fp_problem* p, const Shape& s, const void* q, const void* k, const void* v,
+                           float* q_bar, float* k_bar, float* v_bar, bool chunk_only, PoolParams* out) {
   if (!q || !k || !v || !q_bar || !k_bar || !v_bar) return fail(FP_ERR_NULL, "pooling: NULL buffer");
   PoolParams pp{};
   pp.q = q; pp.k = k; pp.v = v;
@@ -344,6 +357,17 @@ static fp_status run_pool(const fp_problem* p, const void* q, const void* k, con
   pp.kv = make_kv(p);
   pp.rt = make_table(p, s);
   if (pool_lds_bytes(pp.G) > 64 * 1024) return fail(FP_ERR_UNSUPPORTED, "GQA ratio %d too large for pooling", pp.G);
+  *out = pp;
+  return FP_OK;
+}
+
+static fp_status run_pool(const fp_problem* p, const void* q, const void* k, const void* v, float* q_bar,
+                          float* k_bar, float* v_bar, void* stream, bool chunk_only) {
+  Shape s;
+  fp_status st = check_problem(p, &s);
+  if (st) return st;
+  PoolParams pp;
+  if ((st = prep_pool(p, s, q, k, v, q_bar, k_bar, v_bar, chunk_only, &pp))) return st;
   return hip_status(launch_pool(pp, (hipStream_t)stream), "pool launch");
 }
 
@@ -357,14 +381,14 @@ fp_status fp_pool_chunk_blocks(const fp_problem* p, const void* q, const void* k
   return run_pool(p, q, k, v, q_bar, k_bar, v_bar, stream, true);
 }
 
-fp_status fp_select_blocks(const fp_problem* p, const fp_select_args* sel, const float* q_bar, const float* k_bar,
-                           int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity, void* workspace,
-                           size_t workspace_bytes, void* stream) {
-  Shape s;
-  fp_status st = check_problem(p, &s);
+// Validates a selection call and fills its kernel parameters (the ticket and
+// look-back states in `workspace`).
+static fp_status prep_select(const fp_problem* p, const Shape& s, const fp_select_args* sel, const float* q_bar,
+                             const float* k_bar, int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                             void* workspace, size_t workspace_bytes, SelectParams* out) {
+  fp_status st = check_select(sel);
   if (st) return st;
-  if ((st = check_select(sel))) return st;
-  if (!q_bar || !k_bar || !row_ptr || !col_idx) return fail(FP_ERR_NULL, "fp_select_blocks: NULL buffer");
+  if (!q_bar || !k_bar || !row_ptr || !col_idx) return fail(FP_ERR_NULL, "selection: NULL buffer");
   const int64_t max_nnz = (int64_t)p->num_kv_heads * s.pairs;
   if (col_capacity < max_nnz)
     return fail(FP_ERR_CAPACITY, "col_capacity=%lld < max_nnz=%lld", (long long)col_capacity, (long long)max_nnz);
@@ -372,13 +396,18 @@ fp_status fp_select_blocks(const fp_problem* p, const fp_select_args* sel, const
   if (!workspace || workspace_bytes < wl.total)
     return fail(FP_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace ? workspace_bytes : (size_t)0,
                 wl.total);
+  const SelTiles tl = sel_tiles(p, s);
+  if (tl.total > INT32_MAX) return fail(FP_ERR_UNSUPPORTED, "%lld selection tiles", (long long)tl.total);
   SelectParams sp{};
   sp.q_bar = q_bar; sp.k_bar = k_bar; sp.row_ptr = row_ptr; sp.col_idx = col_idx;
   char* ws = static_cast<char*>(workspace);
-  sp.zbuf = reinterpret_cast<float*>(ws + wl.z);
-  sp.rowmax = reinterpret_cast<float*>(ws + wl.rowmax);
-  sp.counts = reinterpret_cast<int32_t*>(ws + wl.counts);
-  sp.pairs_tot = s.pairs;
+  sp.ticket = reinterpret_cast<uint32_t*>(ws + wl.ticket);
+  sp.status = reinterpret_cast<uint64_t*>(ws + wl.status);
+  sp.tile_blocks = tl.T;
+  sp.tiles_per_head = (int32_t)tl.per_head;
+  sp.ntiles = (int32_t)tl.total;
+  sp.bit_words = (s.nb_max + 63) / 64;
+  sp.cache_scores = s.nb_max <= kCacheCols ? 1 : 0;
   sp.sel_scale = sel->sel_scale;
   sp.all_keep = sel->alpha <= 0.f;
   sp.log_alpha = sel->alpha > 0.f ? (float)std::log((double)sel->alpha) : 0.f;
@@ -390,6 +419,41 @@ fp_status fp_select_blocks(const fp_problem* p, const fp_select_args* sel, const
   sp.B = p->block_size;
   sp.kpitch = (int32_t)s.kpitch;
   sp.rt = make_table(p, s);
+  *out = sp;
+  return FP_OK;
+}
+
+fp_status fp_select_blocks(const fp_problem* p, const fp_select_args* sel, const float* q_bar, const float* k_bar,
+                           int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  Shape s;
+  fp_status st = check_problem(p, &s);
+  if (st) return st;
+  SelectParams sp;
+  if ((st = prep_select(p, s, sel, q_bar, k_bar, row_ptr, col_idx, col_capacity, workspace, workspace_bytes, &sp)))
+    return st;
+  fp_status hs = hip_status(launch_select_reset(sp, (hipStream_t)stream), "select reset launch");
+  if (hs) return hs;
+  return hip_status(launch_select(sp, (hipStream_t)stream), "select launch");
+}
+
+fp_status fp_stage1(const fp_problem* p, const fp_select_args* sel, int32_t chunk_only, const void* q, const void* k,
+                    const void* v, float* q_bar, float* k_bar, float* v_bar, int32_t* row_ptr, int32_t* col_idx,
+                    int64_t col_capacity, void* workspace, size_t workspace_bytes, void* stream) {
+  Shape s;
+  fp_status st = check_problem(p, &s);
+  if (st) return st;
+  if (chunk_only != 0 && chunk_only != 1) return fail(FP_ERR_ARG, "chunk_only=%d must be 0 or 1", chunk_only);
+  PoolParams pp;
+  if ((st = prep_pool(p, s, q, k, v, q_bar, k_bar, v_bar, chunk_only != 0, &pp))) return st;
+  SelectParams sp;
+  if ((st = prep_select(p, s, sel, q_bar, k_bar, row_ptr, col_idx, col_capacity, workspace, workspace_bytes, &sp)))
+    return st;
+  pp.sel_ticket = sp.ticket;
+  pp.sel_status = sp.status;
+  pp.sel_ntiles = sp.ntiles;
+  fp_status hs = hip_status(launch_pool(pp, (hipStream_t)stream), "pool launch");
+  if (hs) return hs;
   return hip_status(launch_select(sp, (hipStream_t)stream), "select launch");
 }
 

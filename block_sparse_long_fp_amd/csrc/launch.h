@@ -22,19 +22,27 @@ struct PoolParams {
   int32_t Hq, Hkv, G, B, NBq_tot, NBk_tot, fp8;
   int32_t kpitch;       // rows per KV head of k_bar / v_bar (>= NBk_tot)
   int32_t chunk_only;   // 1: pool only key blocks J >= qb0 (grid over query blocks)
+  uint32_t* sel_ticket; // non-NULL: workgroup 0 also clears the selection's
+  uint64_t* sel_status; //   ticket and sel_ntiles look-back states (fp_stage1)
+  int32_t sel_ntiles;
   KVAddr kv;
   ReqTable rt;
 };
+
+constexpr int kCacheCols = 1024;  // selection scores stay in LDS up to this many key blocks per request
 
 struct SelectParams {
   const float* q_bar;
   const float* k_bar;
   int32_t* row_ptr;
   int32_t* col_idx;
-  float* zbuf;        // workspace: Hkv * pairs_tot floats
-  float* rowmax;      // workspace: rows floats
-  int32_t* counts;    // workspace: rows ints
-  int64_t pairs_tot;  // causal (query block, key block) pairs per KV head
+  uint32_t* ticket;   // workspace: tile ticket (zero before the launch)
+  uint64_t* status;   // workspace: look-back state per tile (zero before the launch)
+  int32_t tile_blocks;     // T: query blocks per tile (4, 8 or 16)
+  int32_t tiles_per_head;  // sum_r ceil(NBq_r / T)
+  int32_t ntiles;          // Hkv * tiles_per_head
+  int32_t bit_words;       // 64-bit keep words per tile row: ceil(nb_max / 64)
+  int32_t cache_scores;    // nb_max <= kCacheCols: scores kept in LDS between the passes
   float sel_scale;
   float log_alpha;    // ln(alpha), fp32
   int32_t all_keep;   // alpha <= 0
@@ -80,6 +88,9 @@ struct AttnParams {
 size_t pool_lds_bytes(int G);
 hipError_t launch_pool(const PoolParams& p, hipStream_t stream);
 hipError_t launch_select(const SelectParams& p, hipStream_t stream);
+hipError_t launch_select_reset(const SelectParams& p, hipStream_t stream);
+int select_tile_blocks(int64_t rows);      // T for a launch of this many CSR rows
+size_t select_dyn_lds(int T, int nb_max);  // dynamic LDS bytes of the selection kernel
 hipError_t launch_attn(const AttnParams& p, hipStream_t stream);
 int attn_rows_per_wg();
 

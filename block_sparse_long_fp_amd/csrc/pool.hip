@@ -27,7 +27,18 @@ namespace fpv2 {
 
 namespace {
 
-constexpr int kPoolThreads = 256;
+// Threads per workgroup: 256 when the grid has enough workgroups to keep
+// every CU streaming; 1024 for small grids (pooling one short chunk), where a
+// thread would otherwise sum its share of the block's tokens in many serial
+// rounds of loads.
+constexpr int kPoolThreadsWide = 1024;
+constexpr int kPoolSmallGrid = 2048;
+// A block's tokens are split into interleaved groups, each summed by one
+// (group, slot, chunk) task in a fixed order and the partial sums reduced in
+// a fixed order: about kPairs tasks per workgroup, whatever its thread count,
+// so the pooled values do not depend on the launch shape (a chunk pooled
+// alone equals the same block pooled with the whole prompt, bit for bit).
+constexpr int kPairs = 768;
 constexpr int kChunks = kHeadDim / 8;  // 8 elements per chunk
 
 constexpr int kBatch = 8;  // loads in flight per thread
@@ -67,22 +78,22 @@ __device__ __forceinline__ void add_raw(const uint4 w, float (&acc)[8]) {
 }
 
 // acc += the chunks at elem0 + k * estride for k = 0 .. cnt-1, in that order,
-// with kBatch loads in flight.
+// kBatch loads in flight (the last batch's loads predicated).
 template <bool FP8>
 __device__ __forceinline__ void sum_strided(const void* base, int64_t elem0, int64_t estride, int cnt,
                                             float (&acc)[8]) {
-  int k = 0;
-  for (; k + kBatch <= cnt; k += kBatch) {
+  for (int k = 0; k < cnt; k += kBatch) {
     uint4 w[kBatch];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) w[u] = load_raw<FP8>(base, elem0 + (int64_t)(k + u) * estride);
+    for (int u = 0; u < kBatch; ++u)
+      w[u] = k + u < cnt ? load_raw<FP8>(base, elem0 + (int64_t)(k + u) * estride) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) add_raw<FP8>(w[u], acc);
+    for (int u = 0; u < kBatch; ++u)
+      if (k + u < cnt) add_raw<FP8>(w[u], acc);
   }
-  for (; k < cnt; ++k) add_raw<FP8>(load_raw<FP8>(base, elem0 + (int64_t)k * estride), acc);
 }
 
-template <bool FP8>
+template <bool FP8, int kPoolThreads>
 __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolParams p) {
   extern __shared__ float part[];  // [groups][slots*kChunks][8]
   // Consecutive workgroups are the KV heads of one block, so the workgroups
@@ -109,10 +120,17 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolParams p) {
   const bool has_q = qi >= 0;
   const int64_t qtok0 = (int64_t)rt.tok_off[r] + (int64_t)qi * p.B;
 
+  if (p.sel_ticket != nullptr && blockIdx.x == 0) {
+    // fp_stage1: clear the selection kernel's ticket and look-back states
+    // (the selection launch that follows on the stream reads them).
+    if (threadIdx.x == 0) *p.sel_ticket = 0u;
+    for (int j = threadIdx.x; j < p.sel_ntiles; j += kPoolThreads) p.sel_status[j] = 0ull;
+  }
+
   const int G = p.G;
   const int slots = G + 2;
   const int tasks = slots * kChunks;
-  const int groups = tasks >= kPoolThreads ? 1 : kPoolThreads / tasks;
+  const int groups = tasks >= kPairs ? 1 : kPairs / tasks;
   const int tid = threadIdx.x;
 
   for (int tk = tid; tk < groups * tasks; tk += kPoolThreads) {
@@ -136,22 +154,21 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolParams p) {
         sum_strided<FP8>(src, kv_elem_offset(p.kv, rt, r, t0 + grp, h, p.Hkv) + chunk * 8,
                          (int64_t)groups * p.Hkv * kHeadDim, cnt, acc);
       } else {
-        // Paged: a batch's page-table lookups go out together, then its loads.
-        int k = 0;
-        for (; k + kBatch <= cnt; k += kBatch) {
+        // Paged: a batch's page-table lookups go out together, then its loads
+        // (the last batch predicated).
+        for (int k = 0; k < cnt; k += kBatch) {
           int64_t off[kBatch];
 #pragma unroll
           for (int u = 0; u < kBatch; ++u)
-            off[u] = kv_elem_offset(p.kv, rt, r, t0 + grp + (k + u) * groups, h, p.Hkv) + chunk * 8;
+            off[u] = k + u < cnt ? kv_elem_offset(p.kv, rt, r, t0 + grp + (k + u) * groups, h, p.Hkv) + chunk * 8
+                                 : 0;
           uint4 w[kBatch];
 #pragma unroll
-          for (int u = 0; u < kBatch; ++u) w[u] = load_raw<FP8>(src, off[u]);
+          for (int u = 0; u < kBatch; ++u) w[u] = k + u < cnt ? load_raw<FP8>(src, off[u]) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-          for (int u = 0; u < kBatch; ++u) add_raw<FP8>(w[u], acc);
+          for (int u = 0; u < kBatch; ++u)
+            if (k + u < cnt) add_raw<FP8>(w[u], acc);
         }
-        for (; k < cnt; ++k)
-          add_raw<FP8>(load_raw<FP8>(src, kv_elem_offset(p.kv, rt, r, t0 + grp + k * groups, h, p.Hkv) + chunk * 8),
-                       acc);
       }
     }
     float* dst = part + ((int64_t)grp * tasks + task) * 8;
@@ -196,17 +213,23 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolParams p) {
 
 size_t pool_lds_bytes(int G) {
   const int tasks = (G + 2) * kChunks;
-  const int groups = tasks >= kPoolThreads ? 1 : kPoolThreads / tasks;
+  const int groups = tasks >= kPairs ? 1 : kPairs / tasks;
   return (size_t)groups * tasks * 8 * sizeof(float);
 }
 
 hipError_t launch_pool(const PoolParams& p, hipStream_t stream) {
-  dim3 grid((unsigned)p.Hkv * (unsigned)(p.chunk_only ? p.NBq_tot : p.NBk_tot));
+  const unsigned wgs = (unsigned)p.Hkv * (unsigned)(p.chunk_only ? p.NBq_tot : p.NBk_tot);
+  const int threads = wgs < (unsigned)kPoolSmallGrid ? kPoolThreadsWide : 256;
   const size_t lds = pool_lds_bytes(p.G);
-  if (p.fp8)
-    hipLaunchKernelGGL(pool_kernel<true>, grid, dim3(kPoolThreads), lds, stream, p);
-  else
-    hipLaunchKernelGGL(pool_kernel<false>, grid, dim3(kPoolThreads), lds, stream, p);
+  if (threads == 256) {
+    if (p.fp8) hipLaunchKernelGGL((pool_kernel<true, 256>), dim3(wgs), dim3(256), lds, stream, p);
+    else hipLaunchKernelGGL((pool_kernel<false, 256>), dim3(wgs), dim3(256), lds, stream, p);
+  } else {
+    if (p.fp8) hipLaunchKernelGGL((pool_kernel<true, kPoolThreadsWide>), dim3(wgs), dim3(kPoolThreadsWide), lds,
+                                  stream, p);
+    else hipLaunchKernelGGL((pool_kernel<false, kPoolThreadsWide>), dim3(wgs), dim3(kPoolThreadsWide), lds,
+                            stream, p);
+  }
   return hipGetLastError();
 }
 

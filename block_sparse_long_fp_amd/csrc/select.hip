@@ -15,18 +15,34 @@
 // iff z_J - m >= ln(alpha) (the same as exp(z_J - m) >= alpha), plus the
 // forced blocks (the diagonal, and optionally sink / window / last-n rows).
 //
-// Four kernels, no host round trip:
-//   score_kernel    one workgroup per (KV head, tile of 32 query blocks of one
-//                   request, tile of 64 key blocks): both pooled tiles staged
-//                   in LDS as fp32, each thread computes a 2 x 4 block of
-//                   scores, every score summed over the head dim in the same
-//                   order (so a score does not depend on its tile), and z goes
-//                   to the workspace. Tiles wholly above the diagonal exit.
-//   rowstat_kernel  one wave per row: row max of z, then the keep count.
-//   scan_kernel     one workgroup: exclusive prefix sum of the row counts
-//                   into row_ptr (wave shuffles, then a carry across chunks).
-//   compact_kernel  one wave per row: ballot of the keep flags of 64 columns,
-//                   mbcnt prefix, ascending column ids written at row_ptr.
+// One kernel, no score round trip through HBM and no host round trip
+// (select_kernel; a small reset kernel, or the pooling kernel of fp_stage1,
+// clears its look-back state first):
+//   * Workgroup = 1024 threads (16 waves); it takes the next tile from an
+//     atomic ticket. A tile is T consecutive query blocks of one (KV head,
+//     request), T = 16 for launches of many rows and 4 for small ones (a
+//     short chunk), so that a small launch still spreads over the CUs; tiles
+//     are numbered in CSR row order.
+//   * Scores on the fp32 matrix cores (v_mfma_f32_16x16x4_f32): every wave
+//     holds the tile's pooled queries (padded to 16 rows) as its B operand
+//     in registers and multiplies them with its 16 of every 256 key blocks,
+//     whose pooled keys it loads straight into registers as the A operand
+//     (the next 256 prefetched); lane l handles row / key block l % 16 and
+//     head dims 32 (l / 16) .. + 31. A score does not depend on the tile it
+//     falls in (the same products in the same order).
+//   * Pass 1 takes each row's max over its causal key blocks; the scores stay
+//     in LDS when the longest request has at most kCacheCols key blocks, else
+//     pass 2 computes them again, 256 key blocks at a time.
+//   * Pass 2, one wave per row: keep = z - max >= ln(alpha) or forced; one
+//     ballot per 64 key blocks gives 64 keep bits (LDS) and their count.
+//   * Decoupled look-back: the tile publishes its keep count, sums its
+//     predecessors' counts back to the nearest one that has published its
+//     inclusive prefix (64 states per round trip, one per lane), and
+//     publishes its own; the exclusive prefix places its rows in the CSR.
+//     Predecessors hold lower tickets, so they are running or done and every
+//     wait ends.
+//   * Compaction: row_ptr of each row, and the kept key-block ids from the
+//     bits, ascending (mbcnt prefix per 64-bit word).
 #include "common.h"
 #include "launch.h"
 
@@ -34,25 +50,12 @@ namespace fpv2 {
 
 namespace {
 
-constexpr int kTileI = 32;       // query blocks per score tile
-constexpr int kTileJ = 64;       // key blocks per score tile
-constexpr int kScoreThreads = 256;
-constexpr int kPad = kHeadDim + 4;
-
-// Scores of request r start at pair_offset(r) in a KV head's z slab; row i of
-// the request starts i * qb0 + i (i + 1) / 2 later (row i has qb0 + i + 1).
-__device__ __forceinline__ int64_t pair_offset(const ReqTable& rt, int r) {
-  int64_t s = 0;
-  for (int q = 0; q < r; ++q) {
-    const int64_t nb = rt.blk_off[q + 1] - rt.blk_off[q];
-    s += nb * rt.qb0[q] + nb * (nb + 1) / 2;
-  }
-  return s;
-}
-
-__device__ __forceinline__ int64_t row_pair_offset(int i, int qb0) {
-  return (int64_t)i * qb0 + (int64_t)i * (i + 1) / 2;
-}
+constexpr int kSelThreads = 1024;
+constexpr int kSelRows = 16;            // query blocks per tile, at most (the MFMA's 16 rows)
+constexpr int kSelCols = 16 * (kSelThreads / 64);  // key blocks per chunk: 16 per wave
+constexpr int kCPitch = kCacheCols + 4; // floats per cached score row
+constexpr int kBPitch = kSelCols + 4;   // floats per row of a chunk's score buffer (no cache)
+static_assert(kSelThreads / 64 >= kSelRows, "one wave per tile row in pass 2");
 
 // Blocks kept whatever their score: the diagonal, the attention sink (the
 // first p.sink blocks), the local window (p.window blocks left of the
@@ -68,210 +71,232 @@ __device__ __forceinline__ bool request_dense(const SelectParams& p, int r) {
   return p.all_keep || L < p.min_sparse_len;
 }
 
-__global__ __launch_bounds__(kScoreThreads) void score_kernel(SelectParams p) {
-  __shared__ float qs[kTileI][kPad];
-  __shared__ float ks[kTileJ][kPad];
+// Look-back state of a tile: flag in the top two bits, count below.
+constexpr uint64_t kAgg = 1ull << 62;    // the tile's own keep count
+constexpr uint64_t kIncl = 2ull << 62;   // keep count of this and every earlier tile
+constexpr uint64_t kValMask = (1ull << 62) - 1;
+constexpr int kMaxSpins = 1 << 22;       // about 0.1 s of s_sleep 1
+
+__global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
+  constexpr int kWaves = kSelThreads / 64;
+  __shared__ float s_max[kWaves][kSelRows];
+  __shared__ int s_ticket, s_excl;
+  __shared__ int s_cnt[kSelRows];
+  // [scores: T x kCPitch (cache) or two chunk buffers of T x kBPitch][bits: T x bit_words]
+  extern __shared__ __align__(16) unsigned char dyn[];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int T = p.tile_blocks;
+  if (tid == 0) s_ticket = (int)atomicAdd(p.ticket, 1u);
+  __syncthreads();
+  const int t = s_ticket;
+  // A workspace shared by overlapping calls (a misuse) could hand out tickets
+  // past the launch; such a workgroup has no tile.
+  if (t >= p.ntiles) return;
+
+  // Tile t: KV head, request and first query block.
   const ReqTable& rt = p.rt;
-  const int h = blockIdx.z;
-  // Map blockIdx.x to (request, query tile): tiles are numbered request by request.
-  int r = 0, tile = blockIdx.x;
+  const int h = t / p.tiles_per_head;
+  int rem = t - h * p.tiles_per_head, r = 0;
   for (;;) {
-    const int nb = rt.blk_off[r + 1] - rt.blk_off[r];
-    const int nt = (nb + kTileI - 1) / kTileI;
-    if (tile < nt || r + 1 >= rt.R) break;
-    tile -= nt;
+    const int nt = (rt.blk_off[r + 1] - rt.blk_off[r] + T - 1) / T;
+    if (rem < nt || r + 1 >= rt.R) break;
+    rem -= nt;
     ++r;
   }
+  const int i0 = rem * T;
   const int NBq = rt.blk_off[r + 1] - rt.blk_off[r];
   const int NB = rt.kblk_off[r + 1] - rt.kblk_off[r];
   const int qb0 = rt.qb0[r];
-  const int i0 = tile * kTileI;
-  const int J0 = blockIdx.y * kTileJ;
-  // Rows i0 .. i0 + 31 need columns J <= qb0 + i (and J < NB).
-  const int i_last = min(NBq, i0 + kTileI) - 1;
-  if (i0 >= NBq || J0 > qb0 + i_last || request_dense(p, r)) return;
-  const int tid = threadIdx.x;
+  const int nrows = min(T, NBq - i0);
+  const int ncols = qb0 + i0 + nrows;  // key blocks 0 .. the last row's diagonal
+  const bool dense = request_dense(p, r);
+  const bool cache = p.cache_scores;
+  float* const cs = reinterpret_cast<float*>(dyn);
+  uint64_t* const bits = reinterpret_cast<uint64_t*>(dyn + (cache ? T * kCPitch * 4 : 2 * T * kBPitch * 4));
+  const int ri = w;  // the row this wave ballots and compacts (if < nrows)
+  const int I = qb0 + i0 + ri;
 
-  const float* qsrc = p.q_bar + ((int64_t)h * p.NBq_tot + rt.blk_off[r]) * kHeadDim;
-  const float* ksrc = p.k_bar + ((int64_t)h * p.kpitch + rt.prow_off[r]) * kHeadDim;
-  for (int e = tid; e < kTileI * (kHeadDim / 4); e += kScoreThreads) {
-    const int rr = e / (kHeadDim / 4), c4 = e % (kHeadDim / 4);
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (i0 + rr < NBq) v = reinterpret_cast<const float4*>(qsrc + (int64_t)(i0 + rr) * kHeadDim)[c4];
-    *reinterpret_cast<float4*>(&qs[rr][c4 * 4]) = v;
-  }
-  for (int e = tid; e < kTileJ * (kHeadDim / 4); e += kScoreThreads) {
-    const int rr = e / (kHeadDim / 4), c4 = e % (kHeadDim / 4);
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (J0 + rr < NB) v = reinterpret_cast<const float4*>(ksrc + (int64_t)(J0 + rr) * kHeadDim)[c4];
-    *reinterpret_cast<float4*>(&ks[rr][c4 * 4]) = v;
-  }
-  __syncthreads();
-
-  // Thread (ri, cj) owns rows ri, ri + 16 and columns cj + 16 u, u = 0..3.
-  const int ri = tid >> 4, cj = tid & 15;
-  float acc[2][4];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int u = 0; u < 4; ++u) acc[a][u] = 0.f;
-#pragma unroll 4
-  for (int c = 0; c < kHeadDim; c += 4) {
-    float4 qv[2], kv[4];
-#pragma unroll
-    for (int a = 0; a < 2; ++a) qv[a] = *reinterpret_cast<const float4*>(&qs[ri + 16 * a][c]);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) kv[u] = *reinterpret_cast<const float4*>(&ks[cj + 16 * u][c]);
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        acc[a][u] = fmaf(qv[a].x, kv[u].x, acc[a][u]);
-        acc[a][u] = fmaf(qv[a].y, kv[u].y, acc[a][u]);
-        acc[a][u] = fmaf(qv[a].z, kv[u].z, acc[a][u]);
-        acc[a][u] = fmaf(qv[a].w, kv[u].w, acc[a][u]);
-      }
-  }
-  float* zh = p.zbuf + (int64_t)h * p.pairs_tot + pair_offset(rt, r);
-#pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    const int i = i0 + ri + 16 * a;
-    if (i >= NBq) continue;
-    float* zrow = zh + row_pair_offset(i, qb0);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int J = J0 + cj + 16 * u;
-      if (J <= qb0 + i) zrow[J] = p.sel_scale * acc[a][u];
-    }
-  }
-}
-
-constexpr int kRowThreads = 256;
-
-// Row max and keep count of every row, one wave per row, from the stored
-// scores (so the count sees exactly the values the compaction will).
-__global__ __launch_bounds__(kRowThreads) void rowstat_kernel(SelectParams p) {
-  const ReqTable& rt = p.rt;
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * (kRowThreads / 64) + (threadIdx.x >> 6);
-  const int64_t rows = (int64_t)p.Hkv * p.NBq_tot;
-  if (row >= rows) return;
-  const int h = (int)(row / p.NBq_tot);
-  const int b = (int)(row % p.NBq_tot);
-  int r = 0;
-  while (r + 1 < rt.R && rt.blk_off[r + 1] <= b) ++r;
-  const int i = b - rt.blk_off[r];
-  const int I = rt.qb0[r] + i;
-  const int NB = rt.kblk_off[r + 1] - rt.kblk_off[r];
-  if (request_dense(p, r)) {
-    if (lane == 0) p.counts[row] = I + 1;
-    return;
-  }
-  const float* zrow = p.zbuf + (int64_t)h * p.pairs_tot + pair_offset(rt, r) + row_pair_offset(i, rt.qb0[r]);
-  float m = -INFINITY;
-  for (int J = lane; J <= I; J += 64) m = fmaxf(m, zrow[J]);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
   int cnt = 0;
-  for (int J0 = 0; J0 <= I; J0 += 64) {
-    const int J = J0 + lane;
-    const bool keep = (J <= I) && (((zrow[J] - m) >= p.log_alpha) || forced_keep(p, I, J, NB));
-    cnt += __popcll(__ballot(keep));
+  if (!dense) {
+    // MFMA lane roles: row n of the tile (B operand) / key block n of the
+    // wave's 16 (A operand), k slot g: head dims 32 g .. 32 g + 31.
+    const int n = lane & 15, g = lane >> 4;
+    f32x4 qv[8];
+    {
+      const float* qsrc = p.q_bar + ((int64_t)h * p.NBq_tot + rt.blk_off[r] + i0 + n) * kHeadDim + 32 * g;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        qv[u] = n < nrows ? *reinterpret_cast<const f32x4*>(qsrc + 4 * u) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // This lane's pooled-key slice of chunk c: key block c * 256 + 16 w + n,
+    // dims 32 g .. + 31 (zeros past the tile's last column).
+    const float* ksrc = p.k_bar + ((int64_t)h * p.kpitch + rt.prow_off[r] + 16 * w + n) * kHeadDim + 32 * g;
+    f32x4 kv[8];
+    auto load_keys = [&](int c) {
+      const int J = c * kSelCols + 16 * w + n;
+      const float* src = ksrc + (int64_t)c * kSelCols * kHeadDim;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        kv[u] = J < ncols ? *reinterpret_cast<const f32x4*>(src + 4 * u) : f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    // tau * (q_bar . k_bar) of key blocks c * 256 + 16 w + 4 g + i (i = 0..3)
+    // against row n; the operands are consumed, so the next chunk's keys can
+    // be loaded into kv right after.
+    auto scores = [&]() {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[u][0], qv[u][0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[u][1], qv[u][1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[u][2], qv[u][2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[u][3], qv[u][3], acc, 0, 0, 0);
+      }
+      return acc * p.sel_scale;
+    };
+    float mx_part = -INFINITY;  // row n's max over this lane's key blocks
+    float mx = -INFINITY;       // row ri's max (after pass 1)
+    // Keep bits of the 64 key blocks c64 * 64 + lane of row ri, from scores at zrow.
+    auto decide = [&](int c64, const float* zrow) {
+      const int J = c64 * 64 + lane;
+      const bool keep = ri < nrows && J <= I && ((zrow[lane] - mx) >= p.log_alpha || forced_keep(p, I, J, NB));
+      const uint64_t word = __ballot(keep);
+      if (ri < nrows && lane == 0) bits[ri * p.bit_words + c64] = word;
+      cnt += __popcll(word);
+    };
+    const int nch = (ncols + kSelCols - 1) / kSelCols;
+    load_keys(0);
+    for (int c = 0; c < nch; ++c) {
+      const f32x4 z = scores();
+      if (c + 1 < nch) load_keys(c + 1);
+      const int J0 = c * kSelCols + 16 * w + 4 * g;  // key block of z[0]
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (n < nrows && J0 + i <= qb0 + i0 + n) mx_part = fmaxf(mx_part, z[i]);
+      if (cache && n < T) *reinterpret_cast<f32x4*>(cs + n * kCPitch + J0) = z;
+    }
+    mx_part = fmaxf(mx_part, __shfl_xor(mx_part, 16));
+    mx_part = fmaxf(mx_part, __shfl_xor(mx_part, 32));
+    if (lane < kSelRows) s_max[w][lane] = mx_part;
+    __syncthreads();
+    if (ri < nrows) {
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) mx = fmaxf(mx, s_max[v][ri]);
+    }
+    if (cache) {
+      if (ri < nrows)
+        for (int c64 = 0; c64 * 64 < ncols; ++c64) decide(c64, cs + ri * kCPitch + c64 * 64);
+    } else {
+      // Pass 2 without the cache: each chunk's scores again, through a
+      // buffer of T x 256 (two, alternating, so one barrier per chunk).
+      load_keys(0);
+      for (int c = 0; c < nch; ++c) {
+        const f32x4 z = scores();
+        if (c + 1 < nch) load_keys(c + 1);
+        float* buf = cs + (c & 1) * T * kBPitch;
+        if (n < T) *reinterpret_cast<f32x4*>(buf + n * kBPitch + 16 * w + 4 * g) = z;
+        __syncthreads();
+        if (ri < nrows)
+          for (int q = 0; q < kSelCols / 64 && c * kSelCols + q * 64 < ncols; ++q)
+            decide(c * (kSelCols / 64) + q, buf + ri * kBPitch + q * 64);
+      }
+    }
+  } else if (ri < nrows) {
+    cnt = I + 1;
   }
-  if (lane == 0) {
-    p.counts[row] = cnt;
-    p.rowmax[row] = m;
-  }
-}
+  if (ri < nrows && lane == 0) s_cnt[ri] = cnt;
+  __syncthreads();
 
-constexpr int kScanThreads = 1024;
-
-__global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __restrict__ counts,
-                                                            int32_t* __restrict__ row_ptr, int64_t rows) {
-  __shared__ int32_t wsum[kScanThreads / 64];
-  __shared__ int32_t carry_s;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  if (tid == 0) {
-    carry_s = 0;
-    row_ptr[0] = 0;
+  // Decoupled look-back over the tiles before this one, by wave 0: lane l
+  // reads the state of tile hi - l, so one round trip covers 64
+  // predecessors; the nearest one with an inclusive prefix ends the walk
+  // (tiles before the first count as inclusive zeros).
+  if (w == 0) {
+    int agg = 0;
+    for (int k = 0; k < nrows; ++k) agg += s_cnt[k];
+    int excl = 0;
+    if (t > 0) {
+      if (lane == 0)
+        __hip_atomic_store(p.status + t, kAgg | (uint64_t)agg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // Predecessors always publish; the bound only keeps a misused workspace
+      // (states not reset) from hanging the launch.
+      int spins = 0;
+      for (int hi = t - 1;;) {
+        const int j = hi - lane;
+        const uint64_t st =
+            j >= 0 ? __hip_atomic_load(p.status + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : kIncl;
+        const uint64_t f = st & ~kValMask;
+        const uint64_t incl = __ballot(f == kIncl);
+        const int first = incl ? __builtin_ctzll(incl) : 64;  // nearest inclusive prefix
+        const uint64_t need = first >= 63 ? ~0ull : ((2ull << first) - 1);
+        if ((__ballot(f == 0) & need) != 0 && ++spins <= kMaxSpins) {
+          __builtin_amdgcn_s_sleep(1);
+          continue;
+        }
+        int v = lane <= first ? (int)(st & kValMask) : 0;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+        excl += v;
+        if (first < 64 || spins > kMaxSpins) break;
+        hi -= 64;
+      }
+    }
+    if (lane == 0) {
+      __hip_atomic_store(p.status + t, kIncl | (uint64_t)(excl + agg), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_excl = excl;
+      if (t == p.ntiles - 1) p.row_ptr[(int64_t)p.Hkv * p.NBq_tot] = excl + agg;
+    }
   }
   __syncthreads();
-  for (int64_t base = 0; base < rows; base += kScanThreads) {
-    const int64_t i = base + tid;
-    int32_t x = i < rows ? counts[i] : 0;
-    // inclusive wave scan
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int32_t y = __shfl_up(x, off);
-      if (lane >= off) x += y;
+
+  // Row offset of row ri and its kept key-block ids, ascending.
+  if (ri < nrows) {
+    int base = s_excl;
+    for (int k = 0; k < ri; ++k) base += s_cnt[k];
+    if (lane == 0) p.row_ptr[(int64_t)h * p.NBq_tot + rt.blk_off[r] + i0 + ri] = base;
+    int32_t* out = p.col_idx + base;
+    if (dense) {
+      for (int J = lane; J <= I; J += 64) out[J] = J;
+    } else {
+      int pos = 0;
+      for (int c = 0; c * 64 <= I; ++c) {
+        const uint64_t word = bits[ri * p.bit_words + c];
+        if ((word >> lane) & 1ull)
+          out[pos + __builtin_amdgcn_mbcnt_hi((uint32_t)(word >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)word, 0))] =
+              c * 64 + lane;
+        pos += __popcll(word);
+      }
     }
-    if (lane == 63) wsum[w] = x;
-    __syncthreads();
-    int32_t before = 0;
-    for (int k = 0; k < w; ++k) before += wsum[k];
-    const int32_t carry = carry_s;
-    if (i < rows) row_ptr[i + 1] = carry + before + x;
-    __syncthreads();
-    if (tid == kScanThreads - 1) carry_s = carry + before + x;
-    __syncthreads();
   }
 }
 
-constexpr int kCompactThreads = 256;
-
-__global__ __launch_bounds__(kCompactThreads) void compact_kernel(SelectParams p) {
-  const ReqTable& rt = p.rt;
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * (kCompactThreads / 64) + (threadIdx.x >> 6);
-  const int64_t rows = (int64_t)p.Hkv * p.NBq_tot;
-  if (row >= rows) return;
-  const int h = (int)(row / p.NBq_tot);
-  const int b = (int)(row % p.NBq_tot);
-  int r = 0;
-  while (r + 1 < rt.R && rt.blk_off[r + 1] <= b) ++r;
-  const int i = b - rt.blk_off[r];
-  const int I = rt.qb0[r] + i;
-  const int NB = rt.kblk_off[r + 1] - rt.kblk_off[r];
-  int32_t* out = p.col_idx + p.row_ptr[row];
-  if (request_dense(p, r)) {
-    for (int J = lane; J <= I; J += 64) out[J] = J;
-    return;
-  }
-  const float* zrow = p.zbuf + (int64_t)h * p.pairs_tot + pair_offset(rt, r) + row_pair_offset(i, rt.qb0[r]);
-  const float m = p.rowmax[row];
-  int base = 0;
-  for (int J0 = 0; J0 <= I; J0 += 64) {
-    const int J = J0 + lane;
-    const bool keep = (J <= I) && (((zrow[J] - m) >= p.log_alpha) || forced_keep(p, I, J, NB));
-    const uint64_t mask = __ballot(keep);
-    const int pre = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
-    if (keep) out[base + pre] = J;
-    base += __popcll(mask);
-  }
+// Clears the ticket and the tiles' look-back states.
+__global__ __launch_bounds__(256) void select_reset_kernel(uint32_t* ticket, uint64_t* status, int ntiles) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i == 0) *ticket = 0u;
+  for (int j = i; j < ntiles; j += gridDim.x * blockDim.x) status[j] = 0ull;
 }
 
 }  // namespace
 
+int select_tile_blocks(int64_t rows) { return rows >= 4096 ? kSelRows : 4; }
+
+size_t select_dyn_lds(int T, int nb_max) {
+  const size_t words = (size_t)(nb_max + 63) / 64;
+  const size_t scores = nb_max <= kCacheCols ? (size_t)T * kCPitch * 4 : (size_t)2 * T * kBPitch * 4;
+  return scores + (size_t)T * words * 8;
+}
+
+hipError_t launch_select_reset(const SelectParams& p, hipStream_t stream) {
+  const int blocks = p.ntiles / 256 + 1 < 64 ? p.ntiles / 256 + 1 : 64;
+  hipLaunchKernelGGL(select_reset_kernel, dim3(blocks), dim3(256), 0, stream, p.ticket, p.status, p.ntiles);
+  return hipGetLastError();
+}
+
 hipError_t launch_select(const SelectParams& p, hipStream_t stream) {
-  int tiles = 0;
-  for (int r = 0; r < p.rt.R; ++r) {
-    const int nb = p.rt.blk_off[r + 1] - p.rt.blk_off[r];
-    tiles += (nb + kTileI - 1) / kTileI;
-  }
-  const int jtiles = (p.rt.nb_max + kTileJ - 1) / kTileJ;
-  hipLaunchKernelGGL(score_kernel, dim3(tiles, jtiles, p.Hkv), dim3(kScoreThreads), 0, stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t rows = (int64_t)p.Hkv * p.NBq_tot;
-  const int64_t row_wgs = (rows + (kRowThreads / 64) - 1) / (kRowThreads / 64);
-  hipLaunchKernelGGL(rowstat_kernel, dim3((unsigned)row_wgs), dim3(kRowThreads), 0, stream, p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, p.counts, p.row_ptr, rows);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t wgs = (rows + (kCompactThreads / 64) - 1) / (kCompactThreads / 64);
-  hipLaunchKernelGGL(compact_kernel, dim3((unsigned)wgs), dim3(kCompactThreads), 0, stream, p);
+  const size_t lds = select_dyn_lds(p.tile_blocks, p.rt.nb_max);
+  hipFuncSetAttribute(reinterpret_cast<const void*>(select_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                      (int)lds);
+  hipLaunchKernelGGL(select_kernel, dim3(p.ntiles), dim3(kSelThreads), lds, stream, p);
   return hipGetLastError();
 }
 

@@ -18,6 +18,8 @@
  *                         with the mean-correction surrogate of every pruned
  *                         causal block merged into the same softmax
  *                         ([digest] Figure 3 Stage 2, Figure 4).
+ * fp_stage1 runs steps 1 and 2 together in two kernels ([digest] Figure 3:
+ * Stage 1 pools and produces the CSR index in one fused pass).
  * fp_dense_prefill is the dense causal comparator built from the same kernels.
  *
  * Conventions shared by every call
@@ -79,7 +81,7 @@
 extern "C" {
 #endif
 
-#define FPV2_ABI_VERSION 7
+#define FPV2_ABI_VERSION 8
 
 /* Status codes. */
 typedef int32_t fp_status;
@@ -183,7 +185,10 @@ typedef struct fp_attn_args {
 fp_status fp_index_shape(const fp_problem* p, int64_t* num_rows, int64_t* max_nnz,
                          int64_t* num_q_blocks, int64_t* num_k_blocks);
 
-/* Bytes of DEVICE workspace fp_select_blocks needs for this problem. */
+/* Bytes of DEVICE workspace fp_select_blocks and fp_stage1 need for this
+ * problem: a tile ticket and one 8-byte look-back word per selection tile (a
+ * tile is 4, 8 or 16 query blocks of one KV head and request), a few KB at
+ * 128K tokens. */
 fp_status fp_select_workspace_bytes(const fp_problem* p, size_t* bytes);
 
 /* Bytes of DEVICE workspace fp_sparse_prefill (sparse = 1) or fp_dense_prefill
@@ -235,12 +240,25 @@ fp_status fp_pool_chunk_blocks(const fp_problem* p, const void* q, const void* k
  * room for col_capacity entries; col_capacity must be >= max_nnz of
  * fp_index_shape (checked before launch, so the kernels cannot overflow).
  * workspace: DEVICE scratch of at least fp_select_workspace_bytes bytes; its
- * contents on entry do not matter and are garbage on exit. Decisions are taken
- * in fp32 as (z_J - max) >= ln(alpha). */
+ * contents on entry do not matter and are garbage on exit; calls that share a
+ * workspace must not overlap. Scores are fp32 sums over the head dim in a
+ * fixed order, decisions (z_J - max) >= ln(alpha) in fp32; no score is written
+ * to memory. Two kernels: a small reset of the workspace, then the fused
+ * score / threshold / prefix / compaction kernel. */
 fp_status fp_select_blocks(const fp_problem* p, const fp_select_args* sel, const float* q_bar,
                            const float* k_bar, int32_t* row_ptr, int32_t* col_idx,
                            int64_t col_capacity, void* workspace, size_t workspace_bytes,
                            void* stream);
+
+/* Stage 1 in two kernels ([digest] Figure 3: PackGQA pooling and the CSR
+ * index of selected blocks produced in one fused pass): fp_pool_blocks
+ * (chunk_only = 0) or fp_pool_chunk_blocks (chunk_only = 1), whose kernel also
+ * resets the selection workspace, then the selection kernel of
+ * fp_select_blocks. Arguments, outputs and errors as in those two calls; every
+ * argument of both is validated before either kernel is enqueued. */
+fp_status fp_stage1(const fp_problem* p, const fp_select_args* sel, int32_t chunk_only, const void* q,
+                    const void* k, const void* v, float* q_bar, float* k_bar, float* v_bar, int32_t* row_ptr,
+                    int32_t* col_idx, int64_t col_capacity, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Stage 2: block-sparse attention with the fused mean correction ([digest]
  * Figure 3 Stage 2: exact path over CSR blocks and correction path merged in

@@ -36,10 +36,12 @@ def upload(wl, device="cuda:0", paged: Optional[bool] = None):
 
 
 def run_gpu(wl, alpha=None, mean_correction=True, paged=None, dense=False, min_sparse_len=None,
-            device="cuda:0", forced=None, num_splits=0):
+            device="cuda:0", forced=None, num_splits=0, fused_stage1=True):
     """Run pool -> select -> attention (or the dense kernel); return CPU results.
     ``forced``: dict(sink=, window=, last_n=) forced keeps, in blocks.
-    ``num_splits``: split-KV parts (0 = the library's automatic choice)."""
+    ``num_splits``: split-KV parts (0 = the library's automatic choice).
+    ``fused_stage1``: Stage 1 through fp_stage1 (else fp_pool_blocks and
+    fp_select_blocks)."""
     alpha = wl.alpha if alpha is None else alpha
     msl = wl.min_sparse_len if min_sparse_len is None else min_sparse_len
     prob, q, k, v = upload(wl, device, paged)
@@ -50,7 +52,7 @@ def run_gpu(wl, alpha=None, mean_correction=True, paged=None, dense=False, min_s
         fp.dense_prefill(prob, att, q, k, v, bufs.out, bufs.lse)
     else:
         fp.run_prefill(prob, bufs, q, k, v, alpha, wl.sel_scale, msl, 0.0, mean_correction, **(forced or {}),
-                       num_splits=num_splits)
+                       num_splits=num_splits, fused_stage1=fused_stage1)
     torch.cuda.synchronize()
     res = dict(out=bufs.out.float().cpu().numpy(), lse=bufs.lse.cpu().numpy())
     if not dense:

@@ -63,8 +63,16 @@ def test_index_shape_and_workspace():
     nbs = [8, 16]
     assert nb == 24 and rows == 8 * 24
     assert nnz == 8 * sum(n * (n + 1) // 2 for n in nbs)
-    ws = fp.select_workspace_bytes(p)
-    assert ws >= 4 * (nnz + 2 * rows)
+    # selection workspace: a 256-byte ticket slot, then one 8-byte look-back
+    # word per tile; 192 rows (< 2048) make tiles of 4 query blocks: 2 + 4
+    # tiles per KV head, 48 in all
+    assert fp.select_workspace_bytes(p) == 256 + 512
+    # 8192 rows (128K tokens, 8 KV heads) make tiles of 16 query blocks
+    big = _prob(cu_seqlens=[0, 131072])
+    assert fp.select_workspace_bytes(big) == 256 + (8 * 64 * 8 + 255) // 256 * 256
+    # below 4096 rows the tiles are 4 query blocks: 2048 rows make 512 tiles
+    mid = _prob(cu_seqlens=[0, 32768])
+    assert fp.select_workspace_bytes(mid) == 256 + 8 * 64 * 8
 
 
 def test_chunked_index_shape():

@@ -11,7 +11,7 @@ import torch
 
 import synth
 from gpu_common import (O_TOL, compare_csr, compare_outputs, compare_pooled, run_gpu, run_oracle,
-                        sets_from_csr, host_values)
+                        sets_from_csr, host_values, upload)
 import oracle
 
 pytestmark = pytest.mark.gpu
@@ -435,3 +435,80 @@ def test_rows_beyond_the_column_cache(num_splits, last_n):
     o_err, l_rel, l_abs = compare_outputs(gpu["out"], gpu["lse"], O, LSE, O_TOL["bf16"])
     print(f"[parity] ok: rows {rows} cols {[int(counts[I]) for I in rows]} O_err={o_err:.2e} "
           f"LSE_rel={l_rel:.2e}", flush=True)
+
+
+# ---------------------------------------------------------------- fused Stage 1
+
+def test_stage1_equals_separate_calls_and_reuses_its_workspace():
+    """fp_stage1 (pooling whose kernel also resets the selection workspace,
+    then the selection kernel) gives bitwise the results of fp_pool_blocks
+    followed by fp_select_blocks (reset kernel, then selection); and one
+    selection workspace serves several calls in a row, each starting from
+    what the previous call left (the look-back states are reset every call).
+    Ragged chunked batch, forced keeps."""
+    import block_sparse_long_fp_amd as fp
+    wl = synth.make_workload("llama_32k", lengths=[3048, 2600], Hq=8, Hkv=2, n_planted=4, kind="varlen",
+                             seeds_base=20, page_size=0, min_sparse_len=0)
+    batch = synth.chunk_of(wl, 2048, 1000)
+    forced = dict(sink=1, window=1, last_n=1)
+    a = run_gpu(batch, forced=forced, fused_stage1=True)
+    b = run_gpu(batch, forced=forced, fused_stage1=False)
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key
+    _check_full(batch, forced=forced)
+    prob, q, k, v = upload(batch)
+    bufs = fp.Buffers(prob, "cuda:0")
+    sel = fp.select_args(batch.alpha, 1.0, 0, **{"sink": 1, "window": 1, "last_n": 1})
+    for it in range(3):
+        bufs.row_ptr.fill_(-7)
+        bufs.col_idx.fill_(-7)
+        if it % 2 == 0:
+            fp.stage1(prob, sel, q, k, v, bufs.q_bar, bufs.k_bar, bufs.v_bar, bufs.row_ptr, bufs.col_idx,
+                      bufs.workspace)
+        else:
+            fp.select_blocks(prob, sel, bufs.q_bar, bufs.k_bar, bufs.row_ptr, bufs.col_idx, bufs.workspace)
+        torch.cuda.synchronize()
+        rp = bufs.row_ptr.cpu().numpy().astype(np.int64)
+        assert np.array_equal(rp, a["row_ptr"]), it
+        assert np.array_equal(bufs.col_idx[:rp[-1]].cpu().numpy().astype(np.int64), a["col_idx"]), it
+
+
+def test_selection_tiles_without_score_cache():
+    """4 KV heads x 1094 query blocks (70000 tokens, block 64): 4376 CSR rows
+    make selection tiles of 16 query blocks, and rows longer than the 1024
+    key blocks whose scores the selection keeps in LDS, so it scores every
+    chunk twice (max, then threshold). Pooled statistics and the CSR against
+    the oracle; fp_stage1 against the separate calls."""
+    wl = synth.make_workload("llama_32k", L=70000, Hq=4, Hkv=4, B=64, n_planted=30, alpha=0.3)
+    a = run_gpu(wl, fused_stage1=True)
+    b = run_gpu(wl, fused_stage1=False)
+    for key in ("row_ptr", "col_idx", "q_bar", "k_bar"):
+        assert np.array_equal(a[key], b[key]), key
+    orc = run_oracle(wl, do_attend=False)
+    compare_pooled(a, orc)
+    n_near = compare_csr(a, orc)
+    print(f"[parity] ok: nnz={a['row_ptr'][-1]} rows={len(a['row_ptr']) - 1} near_rows={n_near}", flush=True)
+
+
+def test_pooling_does_not_depend_on_the_launch_shape():
+    """A whole 32896-token prompt with 8 KV heads is 2056 pooling workgroups
+    (256 threads each); its last 1024-query chunk pooled alone is 64 (1024
+    threads each). The per-token summation order is fixed, so the chunk's
+    pooled queries and its key blocks' pooled keys and values equal the whole
+    prompt's bit for bit."""
+    import block_sparse_long_fp_amd as fp
+    wl = synth.make_workload("llama_32k", L=32896, Hq=8, Hkv=8, n_planted=8)
+    whole = run_gpu(wl, num_splits=1)
+    B, start, L = 128, 31872, 32896
+    NB, qb0 = L // B, start // B
+    dev = "cuda:0"
+    q, k, v = wl.q.to(dev), wl.k.to(dev), wl.v.to(dev)
+    prob = fp.Problem([0, L - start], 8, 8, B, cu_seqlens_k=[0, L], pooled_pitch=NB)
+    bufs = fp.Buffers(prob, dev)
+    kbar = torch.zeros(8, NB, 128, device=dev)
+    vbar = torch.zeros(8, NB, 128, device=dev)
+    fp.pool_chunk_blocks(prob, q[start:].contiguous(), k, v, bufs.q_bar, kbar, vbar)
+    torch.cuda.synchronize()
+    assert np.array_equal(kbar[:, qb0:].cpu().numpy(), whole["k_bar"][:, qb0:])
+    assert np.array_equal(vbar[:, qb0:].cpu().numpy(), whole["v_bar"][:, qb0:])
+    assert np.array_equal(bufs.q_bar.cpu().numpy(), whole["q_bar"][:, qb0:])
