@@ -93,6 +93,7 @@ def lib() -> ctypes.CDLL:
         L.fp_pool_chunk_blocks.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
         L.fp_select_blocks.argtypes = [P, ctypes.POINTER(_SelectArgs), vp, vp, vp, vp, ctypes.c_int64, vp,
                                        ctypes.c_size_t, vp]
+        L.fp_select_blocks_noalloc.argtypes = [P, ctypes.POINTER(_SelectArgs), vp, vp, vp, vp, ctypes.c_int64, vp]
         L.fp_stage1.argtypes = [P, ctypes.POINTER(_SelectArgs), ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp,
                                 ctypes.c_int64, vp, ctypes.c_size_t, vp]
         L.fp_attn_workspace_bytes.argtypes = [P, ctypes.POINTER(_AttnArgs), ctypes.c_int32,
@@ -103,7 +104,8 @@ def lib() -> ctypes.CDLL:
         L.fp_dense_prefill.argtypes = [P, ctypes.POINTER(_AttnArgs), vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         for f in ("fp_index_shape", "fp_select_workspace_bytes", "fp_attn_workspace_bytes", "fp_attn_num_splits",
                   "fp_validate",
-                  "fp_pool_blocks", "fp_pool_chunk_blocks", "fp_select_blocks", "fp_stage1", "fp_sparse_prefill",
+                  "fp_pool_blocks", "fp_pool_chunk_blocks", "fp_select_blocks", "fp_select_blocks_noalloc", "fp_stage1",
+                  "fp_sparse_prefill",
                   "fp_dense_prefill"):
             getattr(L, f).restype = ctypes.c_int32
         L.fp_status_string.argtypes = [ctypes.c_int32]
@@ -133,7 +135,7 @@ def _ptr(t: Optional[torch.Tensor]):
 # contiguity first, then all of them for being on one GPU.
 # --------------------------------------------------------------------------
 
-FP_ERR_NULL, FP_ERR_SHAPE, FP_ERR_DTYPE, FP_ERR_LAYOUT, FP_ERR_WORKSPACE = 1, 2, 5, 6, 8
+FP_ERR_NULL, FP_ERR_SHAPE, FP_ERR_DTYPE, FP_ERR_LAYOUT, FP_ERR_CAPACITY, FP_ERR_WORKSPACE = 1, 2, 5, 6, 7, 8
 _ELEM = {FP_BF16: torch.bfloat16, FP_FP8_E4M3: torch.float8_e4m3fn}
 
 
@@ -383,6 +385,20 @@ def select_blocks(prob: Problem, sel: _SelectArgs, q_bar, k_bar, row_ptr, col_id
     _check(lib().fp_select_blocks(prob.ref, ctypes.byref(sel), _ptr(q_bar), _ptr(k_bar), _ptr(row_ptr),
                                   _ptr(col_idx), col_idx.numel(), _ptr(workspace), workspace.numel(),
                                   _stream(stream)))
+
+
+def select_blocks_noalloc(prob: Problem, sel: _SelectArgs, q_bar, k_bar, row_ptr, col_idx, stream=None):
+    """fp_select_blocks_noalloc: select_blocks with the workspace in the
+    library's fixed per-GPU array (no allocation; calls on one GPU must not
+    overlap)."""
+    rows, named = _pooled_checks(prob, q_bar, k_bar)
+    if q_bar is None or k_bar is None:
+        raise FpError(FP_ERR_NULL, "q_bar and k_bar are required")
+    named += [("row_ptr", _tensor(row_ptr, "row_ptr", torch.int32, (rows + 1,))),
+              ("col_idx", _tensor(col_idx, "col_idx", torch.int32, flat_min=1))]
+    _one_gpu(named)
+    _check(lib().fp_select_blocks_noalloc(prob.ref, ctypes.byref(sel), _ptr(q_bar), _ptr(k_bar), _ptr(row_ptr),
+                                          _ptr(col_idx), col_idx.numel(), _stream(stream)))
 
 
 def stage1(prob: Problem, sel: _SelectArgs, q, k, v, q_bar, k_bar, v_bar, row_ptr, col_idx, workspace,

@@ -381,17 +381,26 @@ fp_status fp_pool_chunk_blocks(const fp_problem* p, const void* q, const void* k
   return run_pool(p, q, k, v, q_bar, k_bar, v_bar, stream, true);
 }
 
-// Validates a selection call and fills its kernel parameters (the ticket and
-// look-back states in `workspace`).
-static fp_status prep_select(const fp_problem* p, const Shape& s, const fp_select_args* sel, const float* q_bar,
-                             const float* k_bar, int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
-                             void* workspace, size_t workspace_bytes, SelectParams* out) {
+// Validates the arguments of a selection call other than its workspace.
+static fp_status check_select_call(const fp_problem* p, const Shape& s, const fp_select_args* sel,
+                                   const float* q_bar, const float* k_bar, int32_t* row_ptr, int32_t* col_idx,
+                                   int64_t col_capacity) {
   fp_status st = check_select(sel);
   if (st) return st;
   if (!q_bar || !k_bar || !row_ptr || !col_idx) return fail(FP_ERR_NULL, "selection: NULL buffer");
   const int64_t max_nnz = (int64_t)p->num_kv_heads * s.pairs;
   if (col_capacity < max_nnz)
     return fail(FP_ERR_CAPACITY, "col_capacity=%lld < max_nnz=%lld", (long long)col_capacity, (long long)max_nnz);
+  return FP_OK;
+}
+
+// Validates a selection call and fills its kernel parameters (the ticket and
+// look-back states in `workspace`).
+static fp_status prep_select(const fp_problem* p, const Shape& s, const fp_select_args* sel, const float* q_bar,
+                             const float* k_bar, int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                             void* workspace, size_t workspace_bytes, SelectParams* out) {
+  fp_status st = check_select_call(p, s, sel, q_bar, k_bar, row_ptr, col_idx, col_capacity);
+  if (st) return st;
   const WsLayout wl = ws_layout(p, s);
   if (!workspace || workspace_bytes < wl.total)
     return fail(FP_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace ? workspace_bytes : (size_t)0,
@@ -433,6 +442,31 @@ fp_status fp_select_blocks(const fp_problem* p, const fp_select_args* sel, const
   if ((st = prep_select(p, s, sel, q_bar, k_bar, row_ptr, col_idx, col_capacity, workspace, workspace_bytes, &sp)))
     return st;
   fp_status hs = hip_status(launch_select_reset(sp, (hipStream_t)stream), "select reset launch");
+  if (hs) return hs;
+  return hip_status(launch_select(sp, (hipStream_t)stream), "select launch");
+}
+
+fp_status fp_select_blocks_noalloc(const fp_problem* p, const fp_select_args* sel, const float* q_bar,
+                                   const float* k_bar, int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                                   void* stream) {
+  Shape s;
+  fp_status st = check_problem(p, &s);
+  if (st) return st;
+  const SelTiles tl = sel_tiles(p, s);
+  if (tl.total > FP_NOALLOC_MAX_SELECT_TILES)
+    return fail(FP_ERR_CAPACITY, "%lld selection tiles exceed the %d of the no-alloc workspace", (long long)tl.total,
+                FP_NOALLOC_MAX_SELECT_TILES);
+  // Every argument is checked before the first device call; then this
+  // device's array (looked up, not allocated).
+  if ((st = check_select_call(p, s, sel, q_bar, k_bar, row_ptr, col_idx, col_capacity))) return st;
+  void* ws = nullptr;
+  fp_status hs = hip_status(static_select_workspace(&ws), "no-alloc workspace lookup");
+  if (hs) return hs;
+  SelectParams sp;
+  if ((st = prep_select(p, s, sel, q_bar, k_bar, row_ptr, col_idx, col_capacity, ws,
+                        256 + (size_t)FP_NOALLOC_MAX_SELECT_TILES * 8, &sp)))
+    return st;
+  hs = hip_status(launch_select_reset(sp, (hipStream_t)stream), "select reset launch");
   if (hs) return hs;
   return hip_status(launch_select(sp, (hipStream_t)stream), "select launch");
 }

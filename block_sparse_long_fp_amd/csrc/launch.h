@@ -30,6 +30,7 @@ struct PoolParams {
 };
 
 constexpr int kCacheCols = 1024;  // selection scores stay in LDS up to this many key blocks per request
+constexpr int kStaticSelectTiles = FP_NOALLOC_MAX_SELECT_TILES;  // look-back words of the no-alloc workspace
 
 struct SelectParams {
   const float* q_bar;
@@ -90,6 +91,9 @@ hipError_t launch_pool(const PoolParams& p, hipStream_t stream);
 hipError_t launch_select(const SelectParams& p, hipStream_t stream);
 hipError_t launch_select_reset(const SelectParams& p, hipStream_t stream);
 int select_tile_blocks(int64_t rows);      // T for a launch of this many CSR rows
+// This device's copy of the selection workspace array of the no-alloc entry
+// point (looked up once per device, with that device current).
+hipError_t static_select_workspace(void** out);
 size_t select_dyn_lds(int T, int nb_max);  // dynamic LDS bytes of the selection kernel
 hipError_t launch_attn(const AttnParams& p, hipStream_t stream);
 int attn_rows_per_wg();

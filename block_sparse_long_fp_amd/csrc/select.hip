@@ -43,12 +43,25 @@
 //     wait ends.
 //   * Compaction: row_ptr of each row, and the kept key-block ids from the
 //     bits, ascending (mbcnt prefix per 64-bit word).
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 
 namespace fpv2 {
 
+// Selection workspace of fp_select_blocks_noalloc, for callers that cannot
+// allocate: the ticket (first 256 bytes), then kStaticSelectTiles look-back
+// words. One copy per GPU, held until the process ends. In host code the name
+// stands for no device address: host code uses the per-device pointer that
+// static_select_workspace() obtains with hipGetSymbolAddress.
+__device__ __align__(256) unsigned char scratch[256 + (size_t)kStaticSelectTiles * 8];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};  // device address of `scratch` per device, once looked up
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelRows = 16;            // query blocks per tile, at most (the MFMA's 16 rows)
@@ -279,6 +292,23 @@ __global__ __launch_bounds__(256) void select_reset_kernel(uint32_t* ticket, uin
 }  // namespace
 
 int select_tile_blocks(int64_t rows) { return rows >= 4096 ? kSelRows : 4; }
+
+hipError_t static_select_workspace(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    // With device `dev` current: its copy of the array.
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
 
 size_t select_dyn_lds(int T, int nb_max) {
   const size_t words = (size_t)(nb_max + 63) / 64;

@@ -81,7 +81,7 @@
 extern "C" {
 #endif
 
-#define FPV2_ABI_VERSION 8
+#define FPV2_ABI_VERSION 9
 
 /* Status codes. */
 typedef int32_t fp_status;
@@ -249,6 +249,24 @@ fp_status fp_select_blocks(const fp_problem* p, const fp_select_args* sel, const
                            const float* k_bar, int32_t* row_ptr, int32_t* col_idx,
                            int64_t col_capacity, void* workspace, size_t workspace_bytes,
                            void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * selection as fp_select_blocks, with its workspace in a fixed device array of
+ * the library instead of a caller buffer. The caller passes only inputs and
+ * outputs; the call allocates and frees nothing. The array holds the
+ * workspace of problems up to FP_NOALLOC_MAX_SELECT_TILES selection tiles
+ * (one tile per 16 query blocks of a KV head and request when the problem has
+ * 4096 CSR rows or more, else per 4; e.g. 128K tokens with 8 KV heads is 512
+ * tiles); larger problems return FP_ERR_CAPACITY before anything is enqueued.
+ * Each GPU has one copy of the array, kept until the process ends, and every
+ * call on that GPU uses it: calls that overlap on one GPU (other streams,
+ * other threads) race and must not be made. The call uses the device current
+ * on the calling thread. */
+#define FP_NOALLOC_MAX_SELECT_TILES 65536
+fp_status fp_select_blocks_noalloc(const fp_problem* p, const fp_select_args* sel, const float* q_bar,
+                                   const float* k_bar, int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                                   void* stream);
 
 /* Stage 1 in two kernels ([digest] Figure 3: PackGQA pooling and the CSR
  * index of selected blocks produced in one fused pass): fp_pool_blocks

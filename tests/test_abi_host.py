@@ -239,3 +239,22 @@ def test_compute_calls_reject_before_launch():
     assert L.fp_dense_prefill(p.ref, ctypes.byref(attn), fake, fake, fake, None, None, None, 0, None) == 1
     for code in range(12):
         assert L.fp_status_string(code)
+
+
+def test_noalloc_selection_rejects_problems_beyond_its_array():
+    """fp_select_blocks_noalloc holds the selection workspace of at most
+    FP_NOALLOC_MAX_SELECT_TILES tiles; a larger problem (128 one-block
+    requests x 1024 KV heads = 131072 tiles) is rejected on the host with
+    FP_ERR_CAPACITY before any device call."""
+    header = open(HEADER).read()
+    cap = int(re.search(r"#define FP_NOALLOC_MAX_SELECT_TILES (\d+)", header).group(1))
+    assert cap == 65536
+    cu = [64 * i for i in range(129)]
+    p = fp.Problem(cu, 1024, 1024, 64)
+    rows, nnz, nbq, nbk = fp.index_shape(p)
+    assert rows == 131072
+    sel = fp.select_args(0.3)
+    fake = ctypes.c_void_p(0x1000)
+    code = fp.lib().fp_select_blocks_noalloc(p.ref, ctypes.byref(sel), fake, fake, fake, fake, nnz, None)
+    assert code == fp.FP_ERR_CAPACITY
+    assert b"no-alloc" in fp.lib().fp_last_error()
