@@ -63,9 +63,11 @@
 //     dispatch then keeps a head's K/V in one L2 across neighbouring rows
 //     while every XCD sees every head (the heads' kept counts differ by up
 //     to 14 % at 128K, and a fixed head per XCD let the busiest one set the
-//     kernel time: 9.62 -> 8.61 ms). The period measured best at 16 query
-//     blocks with 8 KV heads (9.0 ms against 9.0-9.4 for 1 .. 128) and at 32
-//     with 4 (6.84 against 6.96 ms for 16).
+//     kernel time: 9.62 -> 8.61 ms). The period is 1024 / Hkv query blocks
+//     (128 with 8 KV heads): the kernel time is level with shorter periods
+//     (8.95 against 8.94 ms for 16 and 8.86 for 64 at 128K, interleaved), and
+//     a head stays on an XCD long enough for its kept tiles to be reused from
+//     L2 (L2 misses 7.11 -> 5.44 GB per launch against a period of 16).
 //   * Split-KV ([digest] Table 7: count-balanced CSR splits): when a launch
 //     has too few rows to fill the chip, each row's item list is cut into
 //     `splits` consecutive parts of equal cost (an exact block counts 2, a
@@ -99,7 +101,7 @@ constexpr int kSlab8 = 8 * kWaves;      // FP8 K rows one DMA instruction of eve
 
 // A work-unit slot keeps its KV head for kRotateSpan / Hkv query blocks (see
 // decode_work).
-constexpr int kRotateSpan = 128;
+constexpr int kRotateSpan = 1024;
 constexpr int kColCache = 1024;         // CSR columns cached in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
