@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(_PKG, "libfpv2.so")
 FP_BF16, FP_FP8_E4M3 = 0, 1
 FP_KV_CONTIGUOUS, FP_KV_PAGED = 0, 1
 FP_MAX_SEQS = 128
-FP_MAX_BLOCKS_PER_SEQ = 32768
+FP_MAX_BLOCKS_PER_SEQ = 16384
 
 STATUS_NAMES = {
     0: "FP_OK", 1: "FP_ERR_NULL", 2: "FP_ERR_SHAPE", 3: "FP_ERR_GQA", 4: "FP_ERR_BLOCK", 5: "FP_ERR_DTYPE",

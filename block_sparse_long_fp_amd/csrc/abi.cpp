@@ -4,6 +4,7 @@
 // failure; the library never allocates device memory and never synchronises.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -225,33 +226,99 @@ KVAddr make_kv(const fp_problem* p) {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Selection tiles: T query blocks of one (KV head, request) each.
+// Selection tiles: consecutive CSR rows of one (KV head, request) whose
+// score-cache prefixes fall in one multiple of the launch's area A. Rows go
+// in units of 16 (the matrix-core row block) when two of the widest 16-row
+// blocks fit the cache, else one by one. A is at least the widest unit (no
+// empty tiles) and at most what leaves room for it in the cache; launches
+// with enough area make about kSelTargetTiles tiles. A launch of too few
+// units for that (a chunk of a long prompt, a short prompt) makes one tile
+// per 16-row block and splits each tile's key blocks among up to
+// kSelMaxParts workgroups, unless the caller has no room for the split's
+// buffers.
 struct SelTiles {
-  int T;
+  int64_t area;
+  int gran;
   int64_t per_head, total;
+  int parts, part_cols;
+  int lds_floats;
 };
 
-SelTiles sel_tiles(const fp_problem* p, const Shape& s) {
-  SelTiles st{};
-  st.T = select_tile_blocks((int64_t)p->num_kv_heads * s.NBq_tot);
-  for (int r = 0; r < p->num_seqs; ++r) {
-    const int64_t nbq = ((int64_t)p->cu_seqlens[r + 1] - p->cu_seqlens[r] + p->block_size - 1) / p->block_size;
-    st.per_head += (nbq + st.T - 1) / st.T;
-  }
-  st.total = st.per_head * p->num_kv_heads;
-  return st;
+// First query block's key-block id of request r (chunked prefill: > 0).
+int req_qb0(const fp_problem* p, int r) {
+  const int32_t* cuk = key_offsets(p);
+  return ((cuk[r + 1] - cuk[r]) - (p->cu_seqlens[r + 1] - p->cu_seqlens[r])) / p->block_size;
 }
 
-// Selection workspace: the tile ticket, then one look-back word per tile.
+int64_t req_nbq(const fp_problem* p, int r) {
+  return ((int64_t)p->cu_seqlens[r + 1] - p->cu_seqlens[r] + p->block_size - 1) / p->block_size;
+}
+
+SelTiles sel_tiles(const fp_problem* p, const Shape& s, bool allow_split) {
+  const int gran = 2 * 16 * ((int64_t)s.nb_max + 3) <= kSelCacheFloats ? 16 : 1;
+  const int64_t wmax = (int64_t)gran * (s.nb_max + 3);  // cache floats of the widest unit
+  int64_t total = 0;
+  for (int r = 0; r < p->num_seqs; ++r) {
+    const int64_t nu = (req_nbq(p, r) + gran - 1) / gran;
+    total += sel_area_before(nu, req_qb0(p, r), gran);
+  }
+  total *= p->num_kv_heads;
+  auto tiles_for = [&](int64_t A) {
+    SelTiles st{};
+    st.area = A;
+    st.gran = gran;
+    for (int r = 0; r < p->num_seqs; ++r)
+      st.per_head += sel_tiles_in_request((int)req_nbq(p, r), req_qb0(p, r), gran, A);
+    st.total = st.per_head * p->num_kv_heads;
+    st.parts = 1;
+    st.part_cols = 0;
+    st.lds_floats = (int)(A + wmax);
+    return st;
+  };
+  const int64_t per_target = (total + kSelTargetTiles - 1) / kSelTargetTiles;
+  if (allow_split && gran == 16 && per_target < wmax) {
+    // Matrix-core units (16 rows x 16 key blocks) per tile; a tile with more
+    // than one per wave splits its key blocks, about 16 units per part.
+    const SelTiles st = tiles_for(wmax);
+    int64_t units = 0;
+    for (int r = 0; r < p->num_seqs; ++r) {
+      const int64_t nbq = req_nbq(p, r), qb0 = req_qb0(p, r);
+      for (int64_t j = 0; 16 * j < nbq; ++j) units += (qb0 + std::min(16 * j + 16, nbq) + 15) / 16;
+    }
+    units *= p->num_kv_heads;
+    const int64_t by_units = units / (16 * st.total);
+    const int64_t by_cus = (kSelTargetTiles + st.total - 1) / st.total;
+    int parts = (int)std::max<int64_t>(1, std::min<int64_t>(std::min(by_units, by_cus), kSelMaxParts));
+    const int cols = (s.nb_max + parts - 1) / parts;
+    const int part_cols = (cols + 63) / 64 * 64;
+    parts = (s.nb_max + part_cols - 1) / part_cols;
+    if (parts > 1) {
+      SelTiles sp = st;
+      sp.parts = parts;
+      sp.part_cols = part_cols;
+      return sp;
+    }
+  }
+  return tiles_for(std::min(std::max(per_target, wmax), kSelCacheFloats - wmax));
+}
+
+// Selection workspace: the tile ticket (256 bytes), one look-back word per
+// tile, and with a key-block split one arrival count per tile, each part's
+// row maxima and each tile's scores.
 struct WsLayout {
-  size_t ticket, status, total;
+  size_t ticket, status, spill_max, spill, total;
+  int reset_words;
 };
 
-WsLayout ws_layout(const fp_problem* p, const Shape& s) {
+WsLayout ws_layout(const SelTiles& st) {
   WsLayout w{};
   w.ticket = 0;
   w.status = 256;
-  w.total = w.status + align256((size_t)sel_tiles(p, s).total * sizeof(uint64_t));
+  const bool split = st.parts > 1;
+  w.reset_words = (int)(st.total * (split ? 2 : 1));
+  w.spill_max = w.status + align256((size_t)w.reset_words * sizeof(uint64_t));
+  w.spill = w.spill_max + (split ? align256((size_t)st.total * st.parts * kSelMaxRowsPerTile * 4) : 0);
+  w.total = w.spill + (split ? align256((size_t)st.total * st.lds_floats * 4) : 0);
   return w;
 }
 
@@ -310,7 +377,7 @@ fp_status fp_select_workspace_bytes(const fp_problem* p, size_t* bytes) {
   fp_status st = check_problem(p, &s);
   if (st) return st;
   if (!bytes) return fail(FP_ERR_NULL, "bytes is NULL");
-  *bytes = ws_layout(p, s).total;
+  *bytes = ws_layout(sel_tiles(p, s, true)).total;
   return ok();
 }
 
@@ -394,29 +461,36 @@ static fp_status check_select_call(const fp_problem* p, const Shape& s, const fp
   return FP_OK;
 }
 
-// Validates a selection call and fills its kernel parameters (the ticket and
-// look-back states in `workspace`).
+// Validates a selection call and fills its kernel parameters (the ticket,
+// state words and split buffers in `workspace`). allow_split = false keeps
+// every tile in one workgroup (no split buffers).
 static fp_status prep_select(const fp_problem* p, const Shape& s, const fp_select_args* sel, const float* q_bar,
                              const float* k_bar, int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
-                             void* workspace, size_t workspace_bytes, SelectParams* out) {
+                             void* workspace, size_t workspace_bytes, bool allow_split, SelectParams* out) {
   fp_status st = check_select_call(p, s, sel, q_bar, k_bar, row_ptr, col_idx, col_capacity);
   if (st) return st;
-  const WsLayout wl = ws_layout(p, s);
+  const SelTiles tl = sel_tiles(p, s, allow_split);
+  if (tl.total * tl.parts > INT32_MAX / 2)
+    return fail(FP_ERR_UNSUPPORTED, "%lld selection tiles", (long long)tl.total);
+  const WsLayout wl = ws_layout(tl);
   if (!workspace || workspace_bytes < wl.total)
     return fail(FP_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace ? workspace_bytes : (size_t)0,
                 wl.total);
-  const SelTiles tl = sel_tiles(p, s);
-  if (tl.total > INT32_MAX) return fail(FP_ERR_UNSUPPORTED, "%lld selection tiles", (long long)tl.total);
   SelectParams sp{};
   sp.q_bar = q_bar; sp.k_bar = k_bar; sp.row_ptr = row_ptr; sp.col_idx = col_idx;
   char* ws = static_cast<char*>(workspace);
   sp.ticket = reinterpret_cast<uint32_t*>(ws + wl.ticket);
   sp.status = reinterpret_cast<uint64_t*>(ws + wl.status);
-  sp.tile_blocks = tl.T;
+  sp.spill_max = tl.parts > 1 ? reinterpret_cast<int32_t*>(ws + wl.spill_max) : nullptr;
+  sp.spill = tl.parts > 1 ? reinterpret_cast<float*>(ws + wl.spill) : nullptr;
+  sp.tile_area = tl.area;
+  sp.gran = tl.gran;
   sp.tiles_per_head = (int32_t)tl.per_head;
   sp.ntiles = (int32_t)tl.total;
-  sp.bit_words = (s.nb_max + 63) / 64;
-  sp.cache_scores = s.nb_max <= kCacheCols ? 1 : 0;
+  sp.parts = tl.parts;
+  sp.part_cols = tl.part_cols;
+  sp.reset_words = wl.reset_words;
+  sp.lds_floats = tl.lds_floats;
   sp.sel_scale = sel->sel_scale;
   sp.all_keep = sel->alpha <= 0.f;
   sp.log_alpha = sel->alpha > 0.f ? (float)std::log((double)sel->alpha) : 0.f;
@@ -439,7 +513,8 @@ fp_status fp_select_blocks(const fp_problem* p, const fp_select_args* sel, const
   fp_status st = check_problem(p, &s);
   if (st) return st;
   SelectParams sp;
-  if ((st = prep_select(p, s, sel, q_bar, k_bar, row_ptr, col_idx, col_capacity, workspace, workspace_bytes, &sp)))
+  if ((st = prep_select(p, s, sel, q_bar, k_bar, row_ptr, col_idx, col_capacity, workspace, workspace_bytes, true,
+                        &sp)))
     return st;
   fp_status hs = hip_status(launch_select_reset(sp, (hipStream_t)stream), "select reset launch");
   if (hs) return hs;
@@ -452,7 +527,7 @@ fp_status fp_select_blocks_noalloc(const fp_problem* p, const fp_select_args* se
   Shape s;
   fp_status st = check_problem(p, &s);
   if (st) return st;
-  const SelTiles tl = sel_tiles(p, s);
+  const SelTiles tl = sel_tiles(p, s, false);
   if (tl.total > FP_NOALLOC_MAX_SELECT_TILES)
     return fail(FP_ERR_CAPACITY, "%lld selection tiles exceed the %d of the no-alloc workspace", (long long)tl.total,
                 FP_NOALLOC_MAX_SELECT_TILES);
@@ -464,7 +539,7 @@ fp_status fp_select_blocks_noalloc(const fp_problem* p, const fp_select_args* se
   if (hs) return hs;
   SelectParams sp;
   if ((st = prep_select(p, s, sel, q_bar, k_bar, row_ptr, col_idx, col_capacity, ws,
-                        256 + (size_t)FP_NOALLOC_MAX_SELECT_TILES * 8, &sp)))
+                        256 + (size_t)FP_NOALLOC_MAX_SELECT_TILES * 8, false, &sp)))
     return st;
   hs = hip_status(launch_select_reset(sp, (hipStream_t)stream), "select reset launch");
   if (hs) return hs;
@@ -481,11 +556,12 @@ fp_status fp_stage1(const fp_problem* p, const fp_select_args* sel, int32_t chun
   PoolParams pp;
   if ((st = prep_pool(p, s, q, k, v, q_bar, k_bar, v_bar, chunk_only != 0, &pp))) return st;
   SelectParams sp;
-  if ((st = prep_select(p, s, sel, q_bar, k_bar, row_ptr, col_idx, col_capacity, workspace, workspace_bytes, &sp)))
+  if ((st = prep_select(p, s, sel, q_bar, k_bar, row_ptr, col_idx, col_capacity, workspace, workspace_bytes, true,
+                        &sp)))
     return st;
   pp.sel_ticket = sp.ticket;
   pp.sel_status = sp.status;
-  pp.sel_ntiles = sp.ntiles;
+  pp.sel_words = sp.reset_words;
   fp_status hs = hip_status(launch_pool(pp, (hipStream_t)stream), "pool launch");
   if (hs) return hs;
   return hip_status(launch_select(sp, (hipStream_t)stream), "select launch");

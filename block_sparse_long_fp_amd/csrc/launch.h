@@ -23,14 +23,50 @@ struct PoolParams {
   int32_t kpitch;       // rows per KV head of k_bar / v_bar (>= NBk_tot)
   int32_t chunk_only;   // 1: pool only key blocks J >= qb0 (grid over query blocks)
   uint32_t* sel_ticket; // non-NULL: workgroup 0 also clears the selection's
-  uint64_t* sel_status; //   ticket and sel_ntiles look-back states (fp_stage1)
-  int32_t sel_ntiles;
+  uint64_t* sel_status; //   ticket and sel_words state words (fp_stage1)
+  int32_t sel_words;
   KVAddr kv;
   ReqTable rt;
 };
 
-constexpr int kCacheCols = 1024;  // selection scores stay in LDS up to this many key blocks per request
 constexpr int kStaticSelectTiles = FP_NOALLOC_MAX_SELECT_TILES;  // look-back words of the no-alloc workspace
+
+// Selection tiles. Row i of a request (query block i, at key block qb0 + i)
+// has qb0 + i + 1 causal key blocks; its scores take at most qb0 + i + 4
+// floats of the tile's LDS score cache (the count rounded up to 4). Rows
+// are grouped in units of `gran` rows (16: the matrix-core row block, when
+// two of the widest blocks fit the cache; else 1); unit j bounds its cache
+// need by gran * (qb0 + gran * (j + 1) + 3) floats. A tile is the units of
+// one (KV head, request) whose cache prefix sel_area_before(j) falls in
+// [k A, (k + 1) A) for a launch-wide area A: consecutive CSR rows of about
+// equal work. A launch of few units also splits each tile's key blocks into
+// `parts` ranges of `part_cols`, one workgroup each.
+constexpr int kSelCacheFloats = 39936;   // LDS score cache of a tile: A + widest unit <= this (156 KB)
+constexpr int kSelTargetTiles = 256;     // workgroups per launch to aim for (one per CU)
+constexpr int kSelMaxParts = 64;
+constexpr int kSelMaxRowsPerTile = 320;  // bound on a tile's rows (at most 279 by the cache bound)
+
+__host__ __device__ inline int64_t sel_area_before(int64_t j, int64_t qb0, int gran) {
+  return (int64_t)gran * (j * (qb0 + gran + 3) + (int64_t)gran * (j * (j - 1) / 2));
+}
+
+// Smallest j in [0, nu] with sel_area_before(j) >= a (nu if none).
+__host__ __device__ inline int sel_first_unit(int64_t a, int qb0, int gran, int nu) {
+  const double al = (double)gran * (qb0 + gran + 3), be = (double)gran * gran;
+  const double b = al - 0.5 * be;
+  int j = (int)((-b + sqrt(b * b + 2.0 * be * (double)a)) / be);
+  j = j < 0 ? 0 : (j > nu ? nu : j);
+  while (j < nu && sel_area_before(j, qb0, gran) < a) ++j;
+  while (j > 0 && sel_area_before(j - 1, qb0, gran) >= a) --j;
+  return j;
+}
+
+// Tiles of a request of nbq query blocks: one per multiple of A that the
+// cache prefixes of its units reach.
+__host__ __device__ inline int sel_tiles_in_request(int nbq, int qb0, int gran, int64_t A) {
+  const int nu = (nbq + gran - 1) / gran;
+  return nu <= 0 ? 0 : (int)(sel_area_before(nu - 1, qb0, gran) / A) + 1;
+}
 
 struct SelectParams {
   const float* q_bar;
@@ -38,12 +74,18 @@ struct SelectParams {
   int32_t* row_ptr;
   int32_t* col_idx;
   uint32_t* ticket;   // workspace: tile ticket (zero before the launch)
-  uint64_t* status;   // workspace: look-back state per tile (zero before the launch)
-  int32_t tile_blocks;     // T: query blocks per tile (4, 8 or 16)
-  int32_t tiles_per_head;  // sum_r ceil(NBq_r / T)
+  uint64_t* status;   // workspace: look-back state per tile, then (parts > 1) an
+                      // arrival count per tile; reset_words words, zero before the launch
+  int32_t* spill_max; // workspace (parts > 1): [ntiles * parts][256] row-max keys of each part
+  float* spill;       // workspace (parts > 1): [ntiles][lds_floats] the tiles' scores, cache layout
+  int64_t tile_area;       // A
+  int32_t gran;            // rows per tiling unit (16 or 1)
+  int32_t tiles_per_head;  // sum_r sel_tiles_in_request(NBq_r, qb0_r, gran, A)
   int32_t ntiles;          // Hkv * tiles_per_head
-  int32_t bit_words;       // 64-bit keep words per tile row: ceil(nb_max / 64)
-  int32_t cache_scores;    // nb_max <= kCacheCols: scores kept in LDS between the passes
+  int32_t parts;           // workgroups per tile (1: no key-block split)
+  int32_t part_cols;       // key blocks per part, a multiple of 64 (parts > 1)
+  int32_t reset_words;     // ntiles, or 2 * ntiles with parts > 1
+  int32_t lds_floats;      // dynamic LDS of the launch: A + widest row (<= kSelCacheFloats)
   float sel_scale;
   float log_alpha;    // ln(alpha), fp32
   int32_t all_keep;   // alpha <= 0
@@ -90,11 +132,9 @@ size_t pool_lds_bytes(int G);
 hipError_t launch_pool(const PoolParams& p, hipStream_t stream);
 hipError_t launch_select(const SelectParams& p, hipStream_t stream);
 hipError_t launch_select_reset(const SelectParams& p, hipStream_t stream);
-int select_tile_blocks(int64_t rows);      // T for a launch of this many CSR rows
 // This device's copy of the selection workspace array of the no-alloc entry
 // point (looked up once per device, with that device current).
 hipError_t static_select_workspace(void** out);
-size_t select_dyn_lds(int T, int nb_max);  // dynamic LDS bytes of the selection kernel
 hipError_t launch_attn(const AttnParams& p, hipStream_t stream);
 int attn_rows_per_wg();
 

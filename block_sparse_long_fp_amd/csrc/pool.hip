@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolParams p) {
     // fp_stage1: clear the selection kernel's ticket and look-back states
     // (the selection launch that follows on the stream reads them).
     if (threadIdx.x == 0) *p.sel_ticket = 0u;
-    for (int j = threadIdx.x; j < p.sel_ntiles; j += kPoolThreads) p.sel_status[j] = 0ull;
+    for (int j = threadIdx.x; j < p.sel_words; j += kPoolThreads) p.sel_status[j] = 0ull;
   }
 
   const int G = p.G;

@@ -81,7 +81,7 @@
 extern "C" {
 #endif
 
-#define FPV2_ABI_VERSION 9
+#define FPV2_ABI_VERSION 10
 
 /* Status codes. */
 typedef int32_t fp_status;
@@ -110,7 +110,7 @@ enum { FP_KV_CONTIGUOUS = 0, FP_KV_PAGED = 1 };
 
 /* Limits of this build. */
 #define FP_MAX_SEQS 128               /* requests per call                      */
-#define FP_MAX_BLOCKS_PER_SEQ 32768   /* NBk_r; 4M tokens at B = 128            */
+#define FP_MAX_BLOCKS_PER_SEQ 16384   /* NBk_r; 2M tokens at B = 128            */
 #define FP_HEAD_DIM 128
 
 /* Problem description shared by all calls. */
@@ -187,8 +187,12 @@ fp_status fp_index_shape(const fp_problem* p, int64_t* num_rows, int64_t* max_nn
 
 /* Bytes of DEVICE workspace fp_select_blocks and fp_stage1 need for this
  * problem: a tile ticket and one 8-byte look-back word per selection tile (a
- * tile is 4, 8 or 16 query blocks of one KV head and request), a few KB at
- * 128K tokens. */
+ * tile is a run of query blocks of one KV head and request, cut to about equal
+ * causal area: 256 tiles, 2.3 KB, at 128K tokens with 8 KV heads). A problem
+ * of few, long rows (a chunk of a long prompt) also splits each tile's key
+ * blocks among several workgroups, which adds an arrival count per tile, the
+ * parts' row maxima and the tiles' fp32 scores (about 4 bytes per causal
+ * block pair of the call: 0.8 MB for a 2048-token chunk at 128K). */
 fp_status fp_select_workspace_bytes(const fp_problem* p, size_t* bytes);
 
 /* Bytes of DEVICE workspace fp_sparse_prefill (sparse = 1) or fp_dense_prefill
@@ -242,9 +246,13 @@ fp_status fp_pool_chunk_blocks(const fp_problem* p, const void* q, const void* k
  * workspace: DEVICE scratch of at least fp_select_workspace_bytes bytes; its
  * contents on entry do not matter and are garbage on exit; calls that share a
  * workspace must not overlap. Scores are fp32 sums over the head dim in a
- * fixed order, decisions (z_J - max) >= ln(alpha) in fp32; no score is written
- * to memory. Two kernels: a small reset of the workspace, then the fused
- * score / threshold / prefix / compaction kernel. */
+ * fixed order, decisions (z_J - max) >= ln(alpha) in fp32, the same whatever
+ * the launch (chunked calls select exactly like a whole prefill). No score
+ * is written to memory, except within the workspace when a problem of few,
+ * long rows splits its tiles' key blocks. Two kernels: a small reset of the
+ * workspace, then the fused score / threshold / prefix / compaction kernel.
+ * Requests of more than FP_MAX_BLOCKS_PER_SEQ key blocks are rejected
+ * (FP_ERR_UNSUPPORTED) by every call. */
 fp_status fp_select_blocks(const fp_problem* p, const fp_select_args* sel, const float* q_bar,
                            const float* k_bar, int32_t* row_ptr, int32_t* col_idx,
                            int64_t col_capacity, void* workspace, size_t workspace_bytes,
@@ -256,9 +264,9 @@ fp_status fp_select_blocks(const fp_problem* p, const fp_select_args* sel, const
  * the library instead of a caller buffer. The caller passes only inputs and
  * outputs; the call allocates and frees nothing. The array holds the
  * workspace of problems up to FP_NOALLOC_MAX_SELECT_TILES selection tiles
- * (one tile per 16 query blocks of a KV head and request when the problem has
- * 4096 CSR rows or more, else per 4; e.g. 128K tokens with 8 KV heads is 512
- * tiles); larger problems return FP_ERR_CAPACITY before anything is enqueued.
+ * (tiles as for fp_select_workspace_bytes, never split among workgroups here:
+ * 256 tiles at 128K tokens with 8 KV heads, at least one per request and KV
+ * head); larger problems return FP_ERR_CAPACITY before anything is enqueued.
  * Each GPU has one copy of the array, kept until the process ends, and every
  * call on that GPU uses it: calls that overlap on one GPU (other streams,
  * other threads) race and must not be made. The call uses the device current

@@ -64,15 +64,30 @@ def test_index_shape_and_workspace():
     assert nb == 24 and rows == 8 * 24
     assert nnz == 8 * sum(n * (n + 1) // 2 for n in nbs)
     # selection workspace: a 256-byte ticket slot, then one 8-byte look-back
-    # word per tile; 192 rows (< 2048) make tiles of 4 query blocks: 2 + 4
-    # tiles per KV head, 48 in all
-    assert fp.select_workspace_bytes(p) == 256 + 512
-    # 8192 rows (128K tokens, 8 KV heads) make tiles of 16 query blocks
+    # word per tile. Rows are tiled in 16-row blocks of about equal causal
+    # area (at least one block per tile): here one tile per request and KV
+    # head, 16 in all
+    assert fp.select_workspace_bytes(p) == 256 + 256
+    # 128K tokens, 8 KV heads: 256 tiles of about 16.7K score floats
     big = _prob(cu_seqlens=[0, 131072])
-    assert fp.select_workspace_bytes(big) == 256 + (8 * 64 * 8 + 255) // 256 * 256
-    # below 4096 rows the tiles are 4 query blocks: 2048 rows make 512 tiles
+    assert fp.select_workspace_bytes(big) == 256 + 256 * 8
+    # 32K tokens: 256 query blocks per KV head make too few 16-row blocks
+    # for one tile per CU, so a tile holds the area of one widest block (8
+    # per KV head, 64 in all); with about one matrix-core unit per wave
+    # their key blocks are not split
     mid = _prob(cu_seqlens=[0, 32768])
-    assert fp.select_workspace_bytes(mid) == 256 + 8 * 64 * 8
+    assert fp.select_workspace_bytes(mid) == 256 + 64 * 8
+    # a 2048-token chunk after 129024 tokens: one 16-row block per KV head,
+    # 64 units each, so each tile's 1024 key blocks go to 4 workgroups of
+    # 256: the look-back words plus one arrival count per tile, each part's
+    # row maxima (320 int32) and each tile's scores (two widest blocks:
+    # 2 x 16 x (1024 + 3) floats)
+    def a256(x):
+        return (x + 255) // 256 * 256
+    chunk = _prob(cu_seqlens=[0, 2048], cu_seqlens_k=[0, 131072])
+    tiles, parts = 8, 4
+    assert fp.select_workspace_bytes(chunk) == (256 + a256(2 * tiles * 8) + a256(tiles * parts * 320 * 4)
+                                              + a256(tiles * 2 * 16 * 1027 * 4))
 
 
 def test_chunked_index_shape():
