@@ -125,7 +125,22 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
   // The wave index is uniform: unit and row indices derived from it stay in
   // scalar registers (and the pooled queries are read with scalar loads).
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (tid == 0) s_ticket = (int)atomicAdd(p.ticket, 1u);
+  // Wave 1 takes the ticket while wave 0 brings the launch parameters and
+  // request 0's table entries into the scalar cache: each first read of a
+  // kernel-argument line is a memory round trip, which later phases would
+  // otherwise pay one after another (the empty asm statements only need the
+  // values in registers).
+  if (tid == 64) s_ticket = (int)atomicAdd(p.ticket, 1u);
+  if (w == 0) {
+    const ReqTable& rt0 = p.rt;
+    asm volatile("" ::"s"(p.q_bar), "s"(p.k_bar), "s"(p.row_ptr), "s"(p.col_idx), "s"(p.status));
+    asm volatile("" ::"s"(p.tile_area), "s"(p.gran), "s"(p.tiles_per_head), "s"(p.ntiles), "s"(p.parts),
+                 "s"(p.part_cols), "s"(p.sel_scale), "s"(p.log_alpha));
+    asm volatile("" ::"s"(p.all_keep), "s"(p.min_sparse_len), "s"(p.sink), "s"(p.window), "s"(p.last_n),
+                 "s"(p.Hkv), "s"(p.NBq_tot), "s"(p.kpitch));
+    asm volatile("" ::"s"(rt0.R), "s"(rt0.blk_off[0]), "s"(rt0.kblk_off[0]), "s"(rt0.qb0[0]), "s"(rt0.prow_off[0]),
+                 "s"(rt0.tok_off[0]));
+  }
   __syncthreads();
   const int ticket = s_ticket;
   // A workspace shared by overlapping calls (a misuse) could hand out tickets
