@@ -473,12 +473,13 @@ def test_stage1_equals_separate_calls_and_reuses_its_workspace():
         assert np.array_equal(bufs.col_idx[:rp[-1]].cpu().numpy().astype(np.int64), a["col_idx"]), it
 
 
-def test_selection_tiles_without_score_cache():
-    """4 KV heads x 1094 query blocks (70000 tokens, block 64): 4376 CSR rows
-    make selection tiles of 16 query blocks, and rows longer than the 1024
-    key blocks whose scores the selection keeps in LDS, so it scores every
-    chunk twice (max, then threshold). Pooled statistics and the CSR against
-    the oracle; fp_stage1 against the separate calls."""
+def test_selection_splits_long_rows_among_workgroups():
+    """4 KV heads x 1094 query blocks (70000 tokens, block 64): too few 16-row
+    blocks for one selection tile per CU, so each tile's key blocks (more
+    than 1024 per row) are split among two workgroups that spill their scores
+    and row maxima to the workspace, the last to arrive finishing the tile.
+    Pooled statistics and the CSR against the oracle; fp_stage1 against the
+    separate calls."""
     wl = synth.make_workload("llama_32k", L=70000, Hq=4, Hkv=4, B=64, n_planted=30, alpha=0.3)
     a = run_gpu(wl, fused_stage1=True)
     b = run_gpu(wl, fused_stage1=False)
