@@ -1103,8 +1103,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
     for (int it = 0; it < 8; ++it) {
       // Buffer range: rows 4 it .. nvalid - 1 (bytes past the base of row 4 it).
       const int nrec = uniform(nvalid > 4 * it ? (nvalid - 1 - 4 * it) * rstride + kHeadDim * 2 : 0);
+      // Non-temporal (aux 2): the rows are read by this workgroup only, so
+      // they need not displace the kept K/V tiles that other rows reuse from
+      // L2 and MALL.
       __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(qb + (int64_t)(4 * it) * rstride, nrec),
-                                               (lds_ptr)(qs + it * kQGroup), 16, qoff, 0, 0, 0);
+                                               (lds_ptr)(qs + it * kQGroup), 16, qoff, 0, 0, 2);
     }
   }
 
@@ -1250,7 +1253,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
     for (int it = 0; it < 8; ++it) {
       const int rr = 4 * it + (lane >> 4);
       const uint4 v = *reinterpret_cast<const uint4*>(st + rr * kOStride + chunk * 16);
-      if (tq0 + rr < nI) *reinterpret_cast<uint4*>(p.out + ((tok0 + rr) * p.Hq + g) * kHeadDim + chunk * 8) = v;
+      // Non-temporal: the output is written once and read by no kernel here.
+      if (tq0 + rr < nI)
+        __builtin_nontemporal_store(
+            u32x4{v.x, v.y, v.z, v.w},
+            reinterpret_cast<u32x4*>(p.out + ((tok0 + rr) * p.Hq + g) * kHeadDim + chunk * 8));
     }
   }
   if (q_valid && p.lse != nullptr && hf == 0) p.lse[(int64_t)g * p.T + tok] = (ws.m + __log2f(l_tot)) * kLn2;

@@ -44,14 +44,18 @@ constexpr int kChunks = kHeadDim / 8;  // 8 elements per chunk
 constexpr int kBatch = 8;  // loads in flight per thread
 
 // The 8 elements at `elem` as raw words (16 bytes of bf16, or 8 bytes of
-// FP8 codes in .x/.y).
+// FP8 codes in .x/.y). Non-temporal loads: every input byte is read once, so
+// the lines need not stay in L2 or MALL (Llama 128K: 0.295 -> 0.265 ms).
 template <bool FP8>
 __device__ __forceinline__ uint4 load_raw(const void* base, int64_t elem) {
   if constexpr (FP8) {
-    const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(base) + elem);
+    const u32x2 w =
+        __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(base) + elem));
     return make_uint4(w.x, w.y, 0, 0);
   } else {
-    return *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + elem);
+    const u32x4 w =
+        __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(base) + elem));
+    return make_uint4(w.x, w.y, w.z, w.w);
   }
 }
 
