@@ -23,8 +23,9 @@
 //     product straight from registers (the PV contraction index is relabelled
 //     to match the score accumulator layout).
 //   * Work items: the CSR row's key blocks, then correction chunks of 64
-//     pooled columns whose per-column bias log2(n_J) or -inf masks selected
-//     and non-causal blocks (from an LDS bitmap of the row). The kept blocks
+//     pooled columns: the row's pruned blocks in column order, gathered by
+//     DMA from a list the waves build in LDS from a bitmap of the row, each
+//     with bias log2(n_J) (-inf for unused columns of the last chunk). The kept blocks
 //     between the row's first and last item run through a pipelined
 //     instantiation without score adjustments; the diagonal block, the last
 //     kept block and the correction chunks through a general one.
@@ -103,6 +104,7 @@ constexpr int kSlab8 = 8 * kWaves;      // FP8 K rows one DMA instruction of eve
 // decode_work).
 constexpr int kRotateSpan = 1024;
 constexpr int kColCache = 1024;         // CSR columns cached in LDS
+constexpr int kPList = 2048;            // pruned blocks listed in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegBig = -1.0e30f;
@@ -147,6 +149,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, int
 struct RowCtx {
   int r, I, h, L;
   int n_exact;          // CSR entries (key blocks) of the row
+  int n_corr;           // pruned causal blocks: one correction column each
+  bool listed;          // the pruned blocks are listed in LDS (n_corr <= kPList)
   int n_items;          // plus the correction chunks
   const int32_t* cols;  // CSR row (nullptr in dense mode)
   int64_t pooled_row0;  // row h * kpitch + prow_off[r] of k_bar / v_bar
@@ -559,35 +563,84 @@ __device__ __forceinline__ int item_block(const RowCtx& rc, const int32_t* colca
   return uniform(e - 1 < kColCache ? lload_i32(colcache + e - 1) : gload_i32(rc.cols + e - 1));
 }
 
+// Pruned blocks of a row: causal key blocks J < I whose bit in the row's
+// selection bitmap is clear, one correction column each.
+
+// Number of pruned blocks of row I (every lane of the wave gets it).
+__device__ __forceinline__ int count_pruned(const uint32_t* selbits, int I, int lane) {
+  const int nw = (I + 31) >> 5;
+  int n = 0;
+  for (int wd = lane; wd < nw; wd += 64) {
+    uint32_t pm = ~selbits[wd];
+    if (wd == (I >> 5)) pm &= (1u << (I & 31)) - 1u;
+    n += __popc(pm);
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) n += __shfl_xor(n, d);
+  return n;
+}
+
+// The pruned blocks of row I in column order into plist (the caller ensures
+// there are at most kPList). Wave w takes columns [w S, (w + 1) S), S a
+// multiple of 64 with kWaves S >= I: its entries start at the number of
+// pruned blocks before w S, and each round ranks 64 columns, one per lane,
+// by a ballot.
+__device__ __forceinline__ void list_pruned(const uint32_t* selbits, int I, int16_t* plist, int w, int lane) {
+  const int S = (I + kWaves * 64 - 1) / (kWaves * 64) * 64;
+  const int c0 = w * S, c1 = min(I, c0 + S);
+  if (c0 >= c1) return;
+  int at = 0;
+  for (int wd = lane; wd < c0 / 32; wd += 64) at += __popc(~selbits[wd]);  // words wholly below c0 < I
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) at += __shfl_xor(at, d);
+  for (int J = c0; J < c1; J += 64) {
+    const int Jl = J + lane;
+    const int Jc = min(Jl, c1 - 1);
+    const bool pr = Jl < c1 && !((selbits[Jc >> 5] >> (Jc & 31)) & 1u);
+    const uint64_t m = __ballot(pr);
+    if (pr)
+      plist[at + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] =
+          (int16_t)Jl;
+    at += __popcll(m);
+  }
+}
+
+// Block of column t of correction chunk x: with the list, the pruned block of
+// rank kPC x + t; else column kPC x + t if pruned (chunk x then spans key
+// blocks kPC x .. kPC x + kPC - 1). -1: none (past the last, or selected).
+__device__ __forceinline__ int chunk_block(const RowCtx& rc, const uint32_t* selbits, const int16_t* plist, int x,
+                                           int t) {
+  const int k = x * kPC + t;
+  if (rc.listed) return k < rc.n_corr ? (int)plist[k] : -1;
+  return k < rc.I && !((selbits[k >> 5] >> (k & 31)) & 1u) ? k : -1;
+}
+
 // Starts the DMA of item e into one K tile, one V tile and (pooled items) one
-// bias row.
+// bias row. A correction chunk gathers the bf16 pooled rows (256 bytes each)
+// of its blocks; columns without one read zeros (an offset past the range)
+// and get bias -inf.
 template <int BLK, int PAGED, bool F8>
 __device__ __forceinline__ void issue_item(const AttnParams& p, const RowCtx& rc, const int32_t* colcache,
-                                           const uint32_t* selbits, int e, uint8_t* kt, uint8_t* vt, float* bias,
-                                           int tid, int w, int lane, uint32_t voff_kv, uint32_t voff_pool) {
+                                           const uint32_t* selbits, const int16_t* plist, int e, uint8_t* kt,
+                                           uint8_t* vt, float* bias, int tid, int w, int lane, uint32_t voff_kv) {
   if (e < rc.n_exact) {
     issue_block<BLK, PAGED, F8>(p, rc, item_block(rc, colcache, e), kt, vt, w, lane, voff_kv);
   } else {
-    // Correction chunk: pooled columns c0 .. c0+63 (bf16 rows of 256 bytes);
-    // columns at or past I read zeros and get bias -inf.
-    const int c0 = (e - rc.n_exact) * kPC;
-    const int64_t row0 = (rc.pooled_row0 + c0) * (kHeadDim * 2);
-    const uint8_t* kb = reinterpret_cast<const uint8_t*>(p.kbar16) + row0;
-    const uint8_t* vb = reinterpret_cast<const uint8_t*>(p.vbar16) + row0;
+    const int x = e - rc.n_exact;
+    const int64_t row0 = rc.pooled_row0 * (kHeadDim * 2);
+    const int nrec = rc.I * (kHeadDim * 2);
+    const __amdgpu_buffer_rsrc_t kr = raw_rsrc(reinterpret_cast<const uint8_t*>(p.kbar16) + row0, nrec);
+    const __amdgpu_buffer_rsrc_t vr = raw_rsrc(reinterpret_cast<const uint8_t*>(p.vbar16) + row0, nrec);
 #pragma unroll
     for (int u = 0; u < kPC / kSlab; ++u) {
-      const int nrec = uniform(min(max(rc.I - c0 - kSlab * u, 0), kSlab) * (kHeadDim * 2));
-      const int du = kSlab * u * (kHeadDim * 2);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(kb + du, nrec), (lds_ptr)(kt + (kWaves * u + w) * kQuad),
-                                               16, voff_pool, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(vb + du, nrec), (lds_ptr)(vt + (kWaves * u + w) * kQuad),
-                                               16, voff_pool, 0, 0, 0);
+      const int J = chunk_block(rc, selbits, plist, x, kSlab * u + 4 * w + (lane & 3));
+      const uint32_t off = J >= 0 ? (uint32_t)(J * (kHeadDim * 2) + (lane >> 2) * 16) : (uint32_t)nrec;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_ptr)(kt + (kWaves * u + w) * kQuad), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_ptr)(vt + (kWaves * u + w) * kQuad), 16, off, 0, 0, 0);
     }
     if (tid < kPC) {
-      const int Jc = c0 + tid;
-      float bv = -INFINITY;
-      if (Jc < rc.I && !((selbits[Jc >> 5] >> (Jc & 31)) & 1u)) bv = __log2f((float)min(BLK, rc.L - Jc * BLK));
-      bias[tid] = bv;
+      const int J = chunk_block(rc, selbits, plist, x, tid);
+      bias[tid] = J >= 0 ? __log2f((float)min(BLK, rc.L - J * BLK)) : -INFINITY;
     }
   }
 }
@@ -941,10 +994,11 @@ struct ItemLoop {
   const RowCtx& rc;
   const int32_t* colcache;
   const uint32_t* selbits;
+  const int16_t* plist;
   uint8_t *kt0, *kt1, *vt0, *vt1;
   float *bias0, *bias1;
   int N, tid, w, lane;
-  uint32_t voff_kv, voff_pool;
+  uint32_t voff_kv;
   bool wave_active;
   int tq0, tq;
   float sl2;
@@ -989,8 +1043,8 @@ struct ItemLoop {
       }
     }
     if (e + 1 < N)
-      issue_item<BLK, PAGED, F8>(p, rc, colcache, selbits, e + 1, SET ? kt0 : kt1, SET ? vt0 : vt1,
-                                 SET ? bias0 : bias1, tid, w, lane, voff_kv, voff_pool);
+      issue_item<BLK, PAGED, F8>(p, rc, colcache, selbits, plist, e + 1, SET ? kt0 : kt1, SET ? vt0 : vt1,
+                                 SET ? bias0 : bias1, tid, w, lane, voff_kv);
     if (wave_active) {
       if (EXACT)
         attend_exact<BLK, F8>(ws, (SET ? kt1 : kt0) + lkx(), SET ? vt1 : vt0, sl2, lv);
@@ -1024,6 +1078,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   __shared__ float bias0[kPC], bias1[kPC];
   __shared__ uint32_t selbits[FP_MAX_BLOCKS_PER_SEQ / 32];
   __shared__ int32_t colcache[kColCache];
+  __shared__ int16_t plist[kPList];
   uint8_t* const kt0 = reinterpret_cast<uint8_t*>(k_lds0);
   uint8_t* const kt1 = reinterpret_cast<uint8_t*>(k_lds1);
   uint8_t* const vt0 = reinterpret_cast<uint8_t*>(v_lds0);
@@ -1067,7 +1122,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   const int lv = (gq >> 1) * kQuad + (gq & 1) * 128 + ((j16 & 3) >> 1) * 64 + (j16 >> 2) * 16 + (j16 & 1) * 8;
   // DMA offsets: chunk lane/4 of row 4w + lane%4 of a 32-row slab.
   const uint32_t voff_kv = (uint32_t)((4 * w + (lane & 3)) * p.Hkv * kHeadDim * 2 + (lane >> 2) * 16);
-  const uint32_t voff_pool = (uint32_t)((4 * w + (lane & 3)) * kHeadDim * 2 + (lane >> 2) * 16);
 
   // Logit scale in log2 units. FP8 folds the Q and K descales into it (K, V
   // and the pooled rows are staged in code units) and multiplies the output
@@ -1117,7 +1171,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   rc.n_exact = p.dense ? I + 1 : sload_i32(p.row_ptr + row + 1) - rp0;
   rc.cols = p.dense ? nullptr : p.col_idx + rp0;
   const bool do_corr = p.mean_correction && !p.dense && I > 0;
-  rc.n_items = rc.n_exact + (do_corr ? (I + kPC - 1) / kPC : 0);
   rc.pooled_row0 = (int64_t)rc.h * p.kpitch + rt.prow_off[rc.r];
 
   WaveState<BLK> ws;
@@ -1171,6 +1224,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
     }
     __syncthreads();
   }
+  // Correction chunks: the row's pruned blocks, kPC per chunk, from a list
+  // the waves build now (the next barrier publishes it); a row with more
+  // than kPList of them takes its chunks over consecutive key blocks instead.
+  rc.n_corr = do_corr ? uniform(count_pruned(selbits, I, lane)) : 0;
+  rc.listed = rc.n_corr <= kPList;
+  if (rc.listed && rc.n_corr > 0) list_pruned(selbits, I, plist, w, lane);
+  rc.n_items = rc.n_exact + (rc.listed ? (rc.n_corr + kPC - 1) / kPC : (I + kPC - 1) / kPC);
 
   // Items [e0, e1) of this split (all items without split-KV): the diagonal
   // block, the other kept blocks, the correction chunks. The kept blocks
@@ -1182,12 +1242,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
     int e0, e1;
     split_range(rc.n_exact, rc.n_items, split, p.splits, e0, e1);
     if (e0 < e1) {
+      if (e0 >= rc.n_exact) __syncthreads();  // the list, for the first item
       const bool odd = e0 & 1;
-      issue_item<BLK, PAGED, F8>(p, rc, colcache, selbits, e0, odd ? kt1 : kt0, odd ? vt1 : vt0,
-                                 odd ? bias1 : bias0, tid, w, lane, voff_kv, voff_pool);
+      issue_item<BLK, PAGED, F8>(p, rc, colcache, selbits, plist, e0, odd ? kt1 : kt0, odd ? vt1 : vt0,
+                                 odd ? bias1 : bias0, tid, w, lane, voff_kv);
       tiles_ready();
-      ItemLoop<BLK, PAGED, F8> L{p, rc, colcache, selbits, kt0, kt1, vt0, vt1, bias0, bias1, e1, tid, w, lane,
-                                 voff_kv, voff_pool, wave_active, tq0, tq, sl2, lk, lk8, lv, hf};
+      ItemLoop<BLK, PAGED, F8> L{p, rc, colcache, selbits, plist, kt0, kt1, vt0, vt1, bias0, bias1, e1, tid, w,
+                                 lane, voff_kv, wave_active, tq0, tq, sl2, lk, lk8, lv, hf};
       L.template run<false>(ws, e0, min(e1, 1));
       L.template run<true>(ws, max(e0, 1), min(e1, rc.n_exact - 1));
       L.template run<false>(ws, max(e0, max(1, rc.n_exact - 1)), e1);
@@ -1195,8 +1256,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   } else {
     const int N = rc.n_items;
     tiles_ready();
-    ItemLoop<BLK, PAGED, F8> L{p, rc, colcache, selbits, kt0, kt1, vt0, vt1, bias0, bias1, N, tid, w, lane,
-                               voff_kv, voff_pool, wave_active, tq0, tq, sl2, lk, lk8, lv, hf};
+    ItemLoop<BLK, PAGED, F8> L{p, rc, colcache, selbits, plist, kt0, kt1, vt0, vt1, bias0, bias1, N, tid, w,
+                               lane, voff_kv, wave_active, tq0, tq, sl2, lk, lk8, lv, hf};
     L.template run<false>(ws, 0, 1);
     L.template run<true>(ws, 1, rc.n_exact - 1);
     L.template run<false>(ws, max(1, rc.n_exact - 1), N);

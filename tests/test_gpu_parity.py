@@ -437,6 +437,41 @@ def test_rows_beyond_the_column_cache(num_splits, last_n):
           f"LSE_rel={l_rel:.2e}", flush=True)
 
 
+def test_rows_with_more_pruned_blocks_than_the_list():
+    """140000 tokens of one KV head (4 query heads) in 64-token blocks: 2188
+    key blocks. At alpha = 0.5 the late rows prune more than the 2048 blocks
+    whose list the attention kernel keeps in LDS, so their correction chunks
+    span consecutive key blocks (selected ones masked) instead of the listed
+    pruned blocks; rows just below that count use the list."""
+    import math
+    wl = synth.make_workload("llama_32k", L=140000, Hq=4, Hkv=1, B=64, n_planted=30)
+    Q, K, V = host_values(wl)
+    alpha = 0.5
+    print(f"[parity] pruned-list overflow L=140000 B=64 alpha={alpha}", flush=True)
+    gpu = run_gpu(wl, alpha)
+    orc = run_oracle(wl, alpha, do_attend=False, Qkv=(Q, K, V))
+    compare_pooled(gpu, orc)
+    compare_csr(gpu, orc)
+    counts = np.diff(gpu["row_ptr"])
+    NB = len(counts)
+    pruned = np.arange(NB) - (counts - 1)
+    assert NB == 2188 and (pruned > 2048).sum() >= 20 and (pruned <= 2048).sum() >= 20
+    over = np.nonzero(pruned > 2048)[0]
+    under = np.nonzero(pruned <= 2048)[0]
+    rows = sorted({NB - 1, int(over[0]), int(under[-1]), int(np.argmax(pruned))})
+    sets = sets_from_csr(gpu["row_ptr"], gpu["col_idx"], orc.blk_off, 1)[0][0]
+    O = np.full_like(Q, np.nan)
+    LSE = np.full((4, Q.shape[0]), np.nan)
+    for I in rows:
+        o, l = oracle.attend_row(Q, K, V, orc.kbar, orc.vbar, np.asarray(sets[I]), 0, I, 64, 4,
+                                 1.0 / math.sqrt(128), True)
+        O[I * 64:I * 64 + o.shape[0]] = o
+        LSE[:, I * 64:I * 64 + o.shape[0]] = l.T
+    o_err, l_rel, l_abs = compare_outputs(gpu["out"], gpu["lse"], O, LSE, O_TOL["bf16"])
+    print(f"[parity] ok: rows {rows} pruned {[int(pruned[I]) for I in rows]} O_err={o_err:.2e} "
+          f"LSE_rel={l_rel:.2e}", flush=True)
+
+
 # ---------------------------------------------------------------- fused Stage 1
 
 def test_stage1_equals_separate_calls_and_reuses_its_workspace():
