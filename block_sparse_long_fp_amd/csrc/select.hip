@@ -117,6 +117,7 @@ constexpr int kMaxSpins = 1 << 22;       // about 0.1 s of s_sleep 1
 template <bool kSplit>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
   __shared__ int s_ticket, s_excl, s_arrived;
+  __shared__ int s_tile[3];  // the tile's request, first row and row count
   __shared__ int s_wsum[kSelWaves];
   __shared__ int s_off[kSelMaxRowsPerTile + 1];  // cache offset (floats) of each tile row
   __shared__ int s_cnt[kSelMaxRowsPerTile];      // kept blocks of each row, then its offset in the tile's CSR part
@@ -148,23 +149,38 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
   if (ticket >= p.ntiles * p.parts) return;
   const int t = ticket / p.parts, part = ticket - t * p.parts;
 
-  // Tile t: KV head, request, and its rows i0 .. i0 + nr - 1.
+  // Tile t: KV head, request, and its rows i0 .. i0 + nr - 1. Wave 0 alone
+  // decodes it (a chain of 64-bit scalar products: run by all 16 waves it
+  // queued on the CU's scalar unit, the last wave done 3 us after the first)
+  // and hands the result to the others through LDS.
   const ReqTable& rt = p.rt;
-  const int64_t A = p.tile_area;
   const int h = t / p.tiles_per_head;
-  int k = t - h * p.tiles_per_head, r = 0;
-  for (;;) {
-    const int nt = sel_tiles_in_request(rt.blk_off[r + 1] - rt.blk_off[r], rt.qb0[r], p.gran, A);
-    if (k < nt || r + 1 >= rt.R) break;
-    k -= nt;
-    ++r;
+  if (w == 0) {
+    const int64_t A = p.tile_area;
+    int k = t - h * p.tiles_per_head, r = 0;
+    for (;;) {
+      const int nt = sel_tiles_in_request(rt.blk_off[r + 1] - rt.blk_off[r], rt.qb0[r], p.gran, A);
+      if (k < nt || r + 1 >= rt.R) break;
+      k -= nt;
+      ++r;
+    }
+    const int nbq = rt.blk_off[r + 1] - rt.blk_off[r];
+    const int nu = (nbq + p.gran - 1) / p.gran;
+    const int j0 = p.gran * sel_first_unit((int64_t)k * A, rt.qb0[r], p.gran, nu);
+    const int j1 = p.gran * sel_first_unit((int64_t)(k + 1) * A, rt.qb0[r], p.gran, nu);
+    if (lane == 0) {
+      s_tile[0] = r;
+      s_tile[1] = j0;
+      s_tile[2] = min(min(j1, nbq) - j0, kSelMaxRowsPerTile);
+    }
   }
+  __syncthreads();
+  const int r = __builtin_amdgcn_readfirstlane(s_tile[0]);
+  const int i0 = __builtin_amdgcn_readfirstlane(s_tile[1]);
+  const int nr = __builtin_amdgcn_readfirstlane(s_tile[2]);
   const int NBq = rt.blk_off[r + 1] - rt.blk_off[r];
   const int NB = rt.kblk_off[r + 1] - rt.kblk_off[r];
   const int qb0 = rt.qb0[r];
-  const int gran = p.gran, nu = (NBq + gran - 1) / gran;
-  const int i0 = gran * sel_first_unit((int64_t)k * A, qb0, gran, nu);
-  const int nr = min(min(gran * sel_first_unit((int64_t)(k + 1) * A, qb0, gran, nu), NBq) - i0, kSelMaxRowsPerTile);
   const int I0 = qb0 + i0;  // key block of the tile's first row; row j has I0 + j + 1 causal blocks
   const bool dense = request_dense(p, r);
   if (dense && part != 0) return;  // a dense tile is written by its first part alone
