@@ -105,7 +105,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--dense-reps", type=int, default=3, help="timed repetitions of the dense comparator")
-    ap.add_argument("--cpu-rows", type=int, default=16, help="attention rows the CPU baseline computes")
+    ap.add_argument("--cpu-rows", type=int, default=96,
+                    help="attention rows the CPU baseline computes (96: about 10 s of oracle work at 128K)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
     return ap.parse_args()
