@@ -102,11 +102,12 @@ def lib() -> ctypes.CDLL:
         L.fp_sparse_prefill.argtypes = [P, ctypes.POINTER(_AttnArgs), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                         ctypes.c_size_t, vp]
         L.fp_dense_prefill.argtypes = [P, ctypes.POINTER(_AttnArgs), vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.fp_check_index.argtypes = [P, vp, vp, ctypes.c_int64, vp, vp]
         for f in ("fp_index_shape", "fp_select_workspace_bytes", "fp_attn_workspace_bytes", "fp_attn_num_splits",
                   "fp_validate",
                   "fp_pool_blocks", "fp_pool_chunk_blocks", "fp_select_blocks", "fp_select_blocks_noalloc", "fp_stage1",
                   "fp_sparse_prefill",
-                  "fp_dense_prefill"):
+                  "fp_dense_prefill", "fp_check_index"):
             getattr(L, f).restype = ctypes.c_int32
         L.fp_status_string.argtypes = [ctypes.c_int32]
         L.fp_status_string.restype = ctypes.c_char_p
@@ -446,6 +447,36 @@ def dense_prefill(prob: Problem, attn: _AttnArgs, q, k, v, out, lse=None, worksp
     nbytes = 0 if workspace is None else workspace.numel()
     _check(lib().fp_dense_prefill(prob.ref, ctypes.byref(attn), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                                   _ptr(workspace), nbytes, _stream(stream)))
+
+
+FP_CHECK_ROWPTR, FP_CHECK_ORDER, FP_CHECK_RANGE, FP_CHECK_DIAG, FP_CHECK_PAGE = 1, 2, 4, 8, 16
+
+
+def check_index(prob: Problem, row_ptr=None, col_idx=None, err=None, stream=None):
+    """fp_check_index: device check of a CSR index (and, for paged K / V, the
+    page table) before fp_sparse_prefill, which trusts both. Returns ``err``
+    (an int32 device tensor of one element, allocated here if None), which
+    holds the OR of the FP_CHECK_* bits found once the stream reaches it."""
+    named = []
+    if (row_ptr is None) != (col_idx is None):
+        raise FpError(FP_ERR_NULL, "give both row_ptr and col_idx, or neither")
+    if row_ptr is not None:
+        rows, nnz, nbq, nbk = index_shape(prob)
+        named += [("row_ptr", _tensor(row_ptr, "row_ptr", torch.int32, (rows + 1,))),
+                  ("col_idx", _tensor(col_idx, "col_idx", torch.int32, flat_min=1))]
+    if prob.s.kv_layout == FP_KV_PAGED:
+        named.append(("page_table", _tensor(prob.page_table, "page_table", torch.int32,
+                                            (prob.num_seqs, prob.s.max_pages_per_seq), min_rows=prob.num_seqs)))
+    if err is None:
+        dev = _one_gpu(named)
+        if dev is None:
+            raise FpError(FP_ERR_NULL, "nothing to check on a GPU (no CSR, and K / V are not paged)")
+        err = torch.empty(1, dtype=torch.int32, device=dev)
+    named.append(("err", _tensor(err, "err", torch.int32, flat_min=1)))
+    _one_gpu(named)
+    cap = 0 if col_idx is None else col_idx.numel()
+    _check(lib().fp_check_index(prob.ref, _ptr(row_ptr), _ptr(col_idx), cap, _ptr(err), _stream(stream)))
+    return err
 
 
 class Buffers:

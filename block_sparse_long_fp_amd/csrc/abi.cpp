@@ -631,6 +631,29 @@ fp_status fp_dense_prefill(const fp_problem* p, const fp_attn_args* attn, const 
                        stream, true);
 }
 
+fp_status fp_check_index(const fp_problem* p, const int32_t* row_ptr, const int32_t* col_idx, int64_t col_capacity,
+                         int32_t* err, void* stream) {
+  Shape s;
+  fp_status st = check_problem(p, &s);
+  if (st) return st;
+  if (!err) return fail(FP_ERR_NULL, "fp_check_index: err is NULL");
+  if ((row_ptr == nullptr) != (col_idx == nullptr))
+    return fail(FP_ERR_NULL, "fp_check_index: give both row_ptr and col_idx, or neither");
+  if (row_ptr && col_capacity < 0)
+    return fail(FP_ERR_ARG, "fp_check_index: col_capacity=%lld is negative", (long long)col_capacity);
+  CheckParams cp{};
+  cp.row_ptr = row_ptr;
+  cp.col_idx = col_idx;
+  cp.cap = col_capacity;
+  cp.err = err;
+  cp.rows = (int32_t)((int64_t)p->num_kv_heads * s.NBq_tot);
+  cp.NBq_tot = (int32_t)s.NBq_tot;
+  cp.num_pages = p->kv_layout == FP_KV_PAGED ? p->num_pages : 0;
+  cp.kv = make_kv(p);
+  cp.rt = make_table(p, s);
+  return hip_status(launch_check(cp, (hipStream_t)stream), "fp_check_index");
+}
+
 const char* fp_status_string(fp_status s) {
   switch (s) {
     case FP_OK: return "FP_OK";

@@ -128,6 +128,17 @@ struct AttnParams {
   ReqTable rt;
 };
 
+struct CheckParams {
+  const int32_t* row_ptr;  // NULL: page table only
+  const int32_t* col_idx;
+  int64_t cap;             // entries of col_idx
+  int32_t* err;
+  int32_t rows;            // Hkv * NBq_tot
+  int32_t NBq_tot, num_pages;
+  KVAddr kv;
+  ReqTable rt;
+};
+
 size_t pool_lds_bytes(int G);
 hipError_t launch_pool(const PoolParams& p, hipStream_t stream);
 hipError_t launch_select(const SelectParams& p, hipStream_t stream);
@@ -137,5 +148,6 @@ hipError_t launch_select_reset(const SelectParams& p, hipStream_t stream);
 hipError_t static_select_workspace(void** out);
 hipError_t launch_attn(const AttnParams& p, hipStream_t stream);
 int attn_rows_per_wg();
+hipError_t launch_check(const CheckParams& p, hipStream_t stream);
 
 }  // namespace fpv2

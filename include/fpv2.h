@@ -81,7 +81,7 @@
 extern "C" {
 #endif
 
-#define FPV2_ABI_VERSION 10
+#define FPV2_ABI_VERSION 11
 
 /* Status codes. */
 typedef int32_t fp_status;
@@ -307,6 +307,27 @@ fp_status fp_sparse_prefill(const fp_problem* p, const fp_attn_args* attn, const
 fp_status fp_dense_prefill(const fp_problem* p, const fp_attn_args* attn, const void* q,
                            const void* k, const void* v, void* out, float* lse, void* workspace,
                            size_t workspace_bytes, void* stream);
+
+/* Device check of the inputs that fp_sparse_prefill trusts: the CSR of
+ * selected blocks per KV head ([digest] Table 7; Figure 3, Stage 1 output)
+ * and, for paged K / V, the page table ([digest] "What they did", Fix 3).
+ * The prefill reads them without checks (none would be free at its rate);
+ * a caller that builds its own CSR or page table can run this first.
+ * row_ptr, col_idx: DEVICE CSR as for fp_sparse_prefill, col_idx holding
+ * col_capacity entries (both NULL: check the page table only). err: DEVICE
+ * int32, set to 0 and then to the OR of the FP_CHECK_* bits of every
+ * problem found, in stream order (read it after the stream reaches this
+ * point). Every read is bounded by the problem's sizes and col_capacity, so
+ * a malformed index cannot make the check itself read out of range. */
+enum {
+  FP_CHECK_ROWPTR = 1,  /* row_ptr[0] != 0, an entry below its predecessor or past col_capacity */
+  FP_CHECK_ORDER = 2,   /* a row's columns not strictly ascending                              */
+  FP_CHECK_RANGE = 4,   /* a column outside [0, I] (I: the row's own key block)                */
+  FP_CHECK_DIAG = 8,    /* a row with no columns, or whose last column is not I                */
+  FP_CHECK_PAGE = 16    /* paged: a page id outside [0, num_pages) among the pages in use     */
+};
+fp_status fp_check_index(const fp_problem* p, const int32_t* row_ptr, const int32_t* col_idx,
+                         int64_t col_capacity, int32_t* err, void* stream);
 
 /* Static text for a status code; never NULL. */
 const char* fp_status_string(fp_status s);

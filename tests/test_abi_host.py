@@ -273,3 +273,18 @@ def test_noalloc_selection_rejects_problems_beyond_its_array():
     code = fp.lib().fp_select_blocks_noalloc(p.ref, ctypes.byref(sel), fake, fake, fake, fake, nnz, None)
     assert code == fp.FP_ERR_CAPACITY
     assert b"no-alloc" in fp.lib().fp_last_error()
+
+
+def test_check_index_rejects_bad_arguments_on_the_host():
+    """fp_check_index validates before launching: a NULL error word, one of
+    row_ptr / col_idx without the other, or a negative capacity (fake
+    non-NULL device pointers; nothing is dereferenced)."""
+    L = fp.lib()
+    p = _prob()
+    fake = ctypes.c_void_p(0x1000)
+    assert L.fp_check_index(p.ref, fake, fake, 10, None, None) == fp.FP_ERR_NULL
+    assert L.fp_check_index(p.ref, fake, None, 10, fake, None) == fp.FP_ERR_NULL
+    assert L.fp_check_index(p.ref, None, fake, 10, fake, None) == fp.FP_ERR_NULL
+    assert L.fp_check_index(p.ref, fake, fake, -1, fake, None) == 9  # FP_ERR_ARG
+    bad = _prob(num_q_heads=30)  # GQA mismatch is caught by the problem check first
+    assert L.fp_check_index(bad.ref, fake, fake, 10, fake, None) == 3
