@@ -103,11 +103,12 @@ def lib() -> ctypes.CDLL:
                                         ctypes.c_size_t, vp]
         L.fp_dense_prefill.argtypes = [P, ctypes.POINTER(_AttnArgs), vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.fp_check_index.argtypes = [P, vp, vp, ctypes.c_int64, vp, vp]
+        L.fp_workspace_bytes.argtypes = [P, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
         for f in ("fp_index_shape", "fp_select_workspace_bytes", "fp_attn_workspace_bytes", "fp_attn_num_splits",
                   "fp_validate",
                   "fp_pool_blocks", "fp_pool_chunk_blocks", "fp_select_blocks", "fp_select_blocks_noalloc", "fp_stage1",
                   "fp_sparse_prefill",
-                  "fp_dense_prefill", "fp_check_index"):
+                  "fp_dense_prefill", "fp_check_index", "fp_workspace_bytes"):
             getattr(L, f).restype = ctypes.c_int32
         L.fp_status_string.argtypes = [ctypes.c_int32]
         L.fp_status_string.restype = ctypes.c_char_p
@@ -327,6 +328,17 @@ def attn_workspace_bytes(prob: Problem, sparse: bool = True, attn: Optional["_At
     n = ctypes.c_size_t()
     _check(lib().fp_attn_workspace_bytes(prob.ref, ctypes.byref(attn) if attn is not None else None,
                                          1 if sparse else 0, ctypes.byref(n)))
+    return n.value
+
+
+FP_CALL_SELECT, FP_CALL_SPARSE, FP_CALL_DENSE = 0, 1, 2
+
+
+def workspace_bytes(prob: Problem, which_call: int) -> int:
+    """fp_workspace_bytes: the workspace of FP_CALL_SELECT, FP_CALL_SPARSE or
+    FP_CALL_DENSE (attention with the default arguments)."""
+    n = ctypes.c_size_t()
+    _check(lib().fp_workspace_bytes(prob.ref, which_call, ctypes.byref(n)))
     return n.value
 
 

@@ -391,6 +391,16 @@ fp_status fp_attn_workspace_bytes(const fp_problem* p, const fp_attn_args* attn,
   return ok();
 }
 
+fp_status fp_workspace_bytes(const fp_problem* p, int32_t which_call, size_t* bytes) {
+  switch (which_call) {
+    case FP_CALL_SELECT: return fp_select_workspace_bytes(p, bytes);
+    case FP_CALL_SPARSE: return fp_attn_workspace_bytes(p, nullptr, 1, bytes);
+    case FP_CALL_DENSE: return fp_attn_workspace_bytes(p, nullptr, 0, bytes);
+    default: return fail(FP_ERR_ARG, "fp_workspace_bytes: which_call=%d is not FP_CALL_SELECT, _SPARSE or _DENSE",
+                         which_call);
+  }
+}
+
 fp_status fp_attn_num_splits(const fp_problem* p, const fp_attn_args* attn, int32_t* splits) {
   Shape s;
   fp_status st = check_problem(p, &s);

@@ -203,6 +203,14 @@ fp_status fp_select_workspace_bytes(const fp_problem* p, size_t* bytes);
 fp_status fp_attn_workspace_bytes(const fp_problem* p, const fp_attn_args* attn, int32_t sparse,
                                   size_t* bytes);
 
+/* The same sizes through one call: which_call FP_CALL_SELECT (fp_select_blocks
+ * and fp_stage1: fp_select_workspace_bytes), FP_CALL_SPARSE (fp_sparse_prefill)
+ * or FP_CALL_DENSE (fp_dense_prefill), the last two with the default attention
+ * arguments (automatic split; fp_attn_workspace_bytes takes explicit ones).
+ * Host only. Unknown which_call: FP_ERR_ARG. */
+enum { FP_CALL_SELECT = 0, FP_CALL_SPARSE = 1, FP_CALL_DENSE = 2 };
+fp_status fp_workspace_bytes(const fp_problem* p, int32_t which_call, size_t* bytes);
+
 /* The split-KV part count the attention calls will use for these args
  * (resolves num_splits = 0). */
 fp_status fp_attn_num_splits(const fp_problem* p, const fp_attn_args* attn, int32_t* splits);

@@ -288,3 +288,20 @@ def test_check_index_rejects_bad_arguments_on_the_host():
     assert L.fp_check_index(p.ref, fake, fake, -1, fake, None) == 9  # FP_ERR_ARG
     bad = _prob(num_q_heads=30)  # GQA mismatch is caught by the problem check first
     assert L.fp_check_index(bad.ref, fake, fake, 10, fake, None) == 3
+
+
+def test_workspace_bytes_by_call_matches_the_specific_sizes():
+    """fp_workspace_bytes(which_call) returns what the per-call sizing
+    functions return (attention with its default arguments), for a batch, a
+    single long prompt, a chunk and an FP8 paged problem; an unknown call is
+    FP_ERR_ARG."""
+    ds = [torch.ones(1) for _ in range(3)]
+    table = torch.zeros((2, 40), dtype=torch.int32)
+    probs = [_prob(), _prob(cu_seqlens=[0, 131072]), _prob(cu_seqlens=[0, 2048], cu_seqlens_k=[0, 131072]),
+             _prob(dtype=fp.FP_FP8_E4M3, descales=ds, page_table=table, page_size=128, num_pages=80)]
+    for p in probs:
+        assert fp.workspace_bytes(p, fp.FP_CALL_SELECT) == fp.select_workspace_bytes(p)
+        assert fp.workspace_bytes(p, fp.FP_CALL_SPARSE) == fp.attn_workspace_bytes(p, True)
+        assert fp.workspace_bytes(p, fp.FP_CALL_DENSE) == fp.attn_workspace_bytes(p, False)
+    n = ctypes.c_size_t()
+    assert fp.lib().fp_workspace_bytes(probs[0].ref, 7, ctypes.byref(n)) == 9  # FP_ERR_ARG
