@@ -232,7 +232,8 @@ __device__ __forceinline__ void softmax_half(WaveState<BLK>& ws, const f32x16 (&
 // diagonal block (causal mask from tile kt_lim on), or a chunk of pooled
 // columns (logit s*sl2 + bias[col]; columns past the chunk end have bias
 // -inf).
-enum ItemKind { kExact = 0, kDiag = 1, kPooled = 2 };
+enum ItemKind { kExact = 0, kDiag = 1, kPooled = 2, kDiagFirst = 3 };  // kDiagFirst: the diagonal of a
+                                                                    // request's first query block
 
 // V^T operand for PV job j of a half (tile 2hh + (j >> 3), MFMA s2 = (j >> 2) & 1,
 // dims 32 (j & 3) ..): keys 16 s2 + 4 hf + 0..3 and + 8..11 of the tile, each
@@ -295,9 +296,45 @@ __device__ __forceinline__ i32x8 k8_operand(const uint8_t* kh, int j) {
   return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// bf16 K operand of QK job j of a half, read from an FP8 K tile and widened
+// exactly: the 8 codes of row c at the dims widen_q gives the lane's Q
+// operand of step ks = j >> 1, 64 (ks / 4) + 32 hf + 8 (ks % 4) .. + 7, lie
+// in one 16-byte chunk of the row (the lane's hf part is in its base).
+__device__ __forceinline__ bf16x8 k8w_operand(const uint8_t* kh, int j) {
+  const int ks = j >> 1;
+  const uint2 w = *reinterpret_cast<const uint2*>(kh + (j & 1) * 4 * kOct + (4 * (ks >> 2) + ((ks & 3) >> 1)) * 128 +
+                                                  8 * (ks & 1));
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// QK^T of one half from an FP8 K tile on the bf16 matrix cores (Q and K
+// widened exactly): the sums are those of fp32 arithmetic, where the FP8
+// matrix cores keep about 12 bits below each 64-term step's largest product
+// (an in-bounds probe measured errors up to 2^-12.1 of it, 15 code units on
+// a sum of 1e5, against 0.02 for the bf16 products of the same codes).
+template <int DEPTH>
+__device__ __forceinline__ void qk_half8w(const bf16x8 (&qw)[kHeadDim / 16], const uint8_t* kh, f32x16 (&s)[2]) {
+  constexpr int NJ = 2 * (kHeadDim / 16);
+  bf16x8 kf[DEPTH];
+#pragma unroll
+  for (int j = 0; j < DEPTH; ++j) kf[j] = k8w_operand(kh, j);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    s[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j % DEPTH], qw[j >> 1], j < 2 ? f32x16{} : s[j & 1], 0, 0, 0);
+    if (j + DEPTH < NJ) kf[j % DEPTH] = k8w_operand(kh, j + DEPTH);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // S^T += K Q^T over 64 dims on E4M3 codes (v_mfma_f32_32x32x64_f8f6f4, both
-// operands FP8, no block scales): the products of two codes are exact in
-// fp32, so the scores equal those of the codes widened to bf16.
+// operands FP8, no block scales). The products of two codes are exact, but
+// the instruction sums them with about 12 bits below the largest (see
+// qk_half8w), which the kept blocks off the diagonal accept for the FP8 rate.
 __device__ __forceinline__ f32x16 mfma_f8(const i32x8& a, const i32x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
@@ -350,6 +387,8 @@ __device__ __forceinline__ void attend_item(WaveState<BLK>& ws, const uint8_t* k
                                             int lk8, int lv, int hf) {
   constexpr int kDepth = 4;  // operand reads in flight
   if (EXACT) kind = kExact;
+  const bool first = kind == kDiagFirst;
+  if (first) kind = kDiag;
   const int nh = kind == kPooled ? 1 : BLK / 64;
   // Pooled scores are turned into log2-unit logits with their bias before
   // the max; exact scores are scaled after it.
@@ -360,8 +399,17 @@ __device__ __forceinline__ void attend_item(WaveState<BLK>& ws, const uint8_t* k
     // QK^T of tiles 2hh, 2hh+1 (rows 32kt + c of a tile).
     f32x16 s[2];
     if constexpr (F8) {
-      if (kind != kPooled) {
+      if (kind != kPooled && !first) {
         qk_half8(ws.q8, kb + lk8 + (2 * hh) * 4 * kOct, s);
+      } else if (first) {
+        // The diagonal of a request's first query block on the bf16 matrix
+        // cores: those queries see no other keys, so their log-sum-exp is
+        // this block's scores alone and can lie near 0, where a relative
+        // bound needs the scores to fp32 accuracy. Later rows sum over at
+        // least one more block.
+        bf16x8 qw[kHeadDim / 16];
+        widen_q(ws.q8, qw);
+        qk_half8w<kDepth>(qw, kb + lk8 + (2 * hh) * 4 * kOct, s);
       } else {
         // The pooled rows are bf16: Q widened for this chunk (not kept, to
         // leave the registers to the kept blocks' pipeline).
@@ -671,7 +719,8 @@ template <int BLK, bool EXACT, bool F8>
 __device__ __forceinline__ void compute_item(WaveState<BLK>& ws, const RowCtx& rc, int e, const uint8_t* kt,
                                              const uint8_t* vt, const float* bias, int tq0, int tq, float sl2,
                                              int lk, int lk8, int lv, int hf) {
-  const int kind = EXACT ? kExact : (e == 0 ? kDiag : (e < rc.n_exact ? kExact : kPooled));
+  const int kind =
+      EXACT ? kExact : (e == 0 ? (F8 && rc.I == 0 ? kDiagFirst : kDiag) : (e < rc.n_exact ? kExact : kPooled));
   attend_item<BLK, EXACT, F8>(ws, kt, vt, bias, kind, tq0 >> 5, tq, sl2, lk, lk8, lv, hf);
 }
 

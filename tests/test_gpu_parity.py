@@ -78,6 +78,25 @@ def test_fp8_gqa8():
     _check_full(wl)
 
 
+@pytest.mark.parametrize("Hq,Hkv,B,fp8,splits", [
+    (6, 2, 128, False, 0),    # G = 3: 384 packed rows, the second 256-row sub-tile half empty
+    (10, 2, 128, False, 0),   # G = 5 (40 / 8 heads): 640 rows, third sub-tile half empty
+    (14, 2, 64, False, 0),    # G = 7 (28 / 4 heads), 64-key blocks: 448 rows
+    (10, 2, 128, True, 0),    # G = 5 with FP8 products
+    (6, 2, 128, False, 3),    # G = 3, split-KV
+])
+def test_gqa_ratios_that_leave_waves_without_rows(Hq, Hkv, B, fp8, splits):
+    """GQA ratios whose G B packed rows do not fill whole 256-row sub-tiles:
+    the last sub-tile of every row has waves without rows (which still issue
+    their share of each block's DMA and take part in every barrier), and
+    pooling sums an odd number of query heads per group. Ragged requests,
+    paged K / V with 16-token pages for the bf16 cases."""
+    wl = synth.make_workload("qwen4b_varlen_paged", lengths=[1500, 700], Hq=Hq, Hkv=Hkv, min_sparse_len=0,
+                             n_planted=3, B=B, fp8=fp8, page_size=0 if fp8 else 16)
+    assert wl.num_q_heads // wl.num_kv_heads * B % 256 != 0
+    _check_full(wl, num_splits=splits)
+
+
 @pytest.mark.parametrize("page_size", [0, 64, 6])
 def test_fp8_block64_varlen(page_size):
     # FP8 products with 64-key blocks (one FP8 K DMA instruction per wave) on
