@@ -84,6 +84,7 @@ def test_fp8_gqa8():
     (14, 2, 64, False, 0),    # G = 7 (28 / 4 heads), 64-key blocks: 448 rows
     (10, 2, 128, True, 0),    # G = 5 with FP8 products
     (6, 2, 128, False, 3),    # G = 3, split-KV
+    (12, 4, 64, True, 3),     # G = 3, 64-key blocks: 192 rows (two waves idle), FP8, split-KV
 ])
 def test_gqa_ratios_that_leave_waves_without_rows(Hq, Hkv, B, fp8, splits):
     """GQA ratios whose G B packed rows do not fill whole 256-row sub-tiles:
