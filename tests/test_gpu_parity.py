@@ -191,6 +191,22 @@ def test_single_token_and_one_block_requests(fp8):
     _check_full(wl, paged=False, num_splits=1)
 
 
+@pytest.mark.parametrize("num_splits", [1, 3])
+def test_batch_of_the_most_requests(num_splits):
+    """FP_MAX_SEQS = 128 requests of seeded lengths 1 .. 399 (one- and
+    two-token requests, block-boundary lengths, ragged tails), 64-key blocks,
+    paged K / V: the attention kernel's multi-request decode holds request q
+    in lane q and, past 64 requests, in lane q + 64 as well; pooling,
+    selection tiles and the CSR offsets walk the whole request table."""
+    rng = np.random.default_rng(128)
+    lengths = [int(x) for x in rng.integers(1, 400, 128)]
+    lengths[:6] = [1, 2, 63, 64, 65, 128]
+    wl = synth.make_workload("qwen4b_varlen_paged", lengths=lengths, Hq=4, Hkv=1, B=64, min_sparse_len=0,
+                             n_planted=0, page_size=16)
+    assert len(wl.seqlens) == 128
+    _check_full(wl, num_splits=num_splits)
+
+
 @pytest.mark.parametrize("forced", [dict(sink=2, window=4, last_n=8), dict(sink=1, window=0, last_n=0),
                                     dict(sink=0, window=2, last_n=3)])
 def test_forced_keeps_sink_window_last_n(forced):
