@@ -192,6 +192,34 @@ def test_single_token_and_one_block_requests(fp8):
 
 
 @pytest.mark.parametrize("num_splits", [1, 3])
+def test_lse_buffer_is_optional(num_splits):
+    """lse = NULL skips the log-sum-exp: the sparse and dense calls, unsplit
+    and split (whose merge kernel writes the LSE), give bitwise the same
+    output with and without it. Ragged GQA-4 batch, FP8."""
+    import block_sparse_long_fp_amd as fp
+    wl = synth.make_workload("qwen4b_varlen_paged", lengths=[1300, 500], Hq=8, Hkv=2, min_sparse_len=0,
+                             n_planted=3, fp8=True, page_size=0)
+    prob, q, k, v = upload(wl)
+    att = fp.attn_args(0.0, True, num_splits)
+    bufs = fp.Buffers(prob, "cuda:0", attn=att)
+    fp.run_prefill(prob, bufs, q, k, v, wl.alpha, wl.sel_scale, 0, 0.0, True, num_splits=num_splits)
+    for dense in (False, True):
+        outs = []
+        for with_lse in (True, False):
+            out = torch.full_like(bufs.out, 7.0)
+            lse = torch.full_like(bufs.lse, 7.0) if with_lse else None
+            if dense:
+                fp.dense_prefill(prob, att, q, k, v, out, lse)
+            else:
+                fp.sparse_prefill(prob, att, q, k, v, bufs.k_bar, bufs.v_bar, bufs.row_ptr, bufs.col_idx, out, lse)
+            torch.cuda.synchronize()
+            outs.append(out.cpu())
+            if with_lse:
+                assert torch.isfinite(lse).all() and not (lse == 7.0).any()
+        assert torch.equal(outs[0], outs[1]), f"dense={dense}"
+
+
+@pytest.mark.parametrize("num_splits", [1, 3])
 def test_batch_of_the_most_requests(num_splits):
     """FP_MAX_SEQS = 128 requests of seeded lengths 1 .. 399 (one- and
     two-token requests, block-boundary lengths, ragged tails), 64-key blocks,
