@@ -36,22 +36,22 @@ def upload(wl, device="cuda:0", paged: Optional[bool] = None):
 
 
 def run_gpu(wl, alpha=None, mean_correction=True, paged=None, dense=False, min_sparse_len=None,
-            device="cuda:0", forced=None, num_splits=0, fused_stage1=True):
+            device="cuda:0", forced=None, num_splits=0, fused_stage1=True, sm_scale=0.0):
     """Run pool -> select -> attention (or the dense kernel); return CPU results.
     ``forced``: dict(sink=, window=, last_n=) forced keeps, in blocks.
     ``num_splits``: split-KV parts (0 = the library's automatic choice).
     ``fused_stage1``: Stage 1 through fp_stage1 (else fp_pool_blocks and
-    fp_select_blocks)."""
+    fp_select_blocks). ``sm_scale``: softmax scale (0 = 1 / sqrt(d))."""
     alpha = wl.alpha if alpha is None else alpha
     msl = wl.min_sparse_len if min_sparse_len is None else min_sparse_len
     prob, q, k, v = upload(wl, device, paged)
-    att = fp.attn_args(0.0, mean_correction, num_splits)
+    att = fp.attn_args(sm_scale, mean_correction, num_splits)
     print(f"[gpu] splits={fp.attn_num_splits(prob, att)}", flush=True)
     bufs = fp.Buffers(prob, device, attn=att)
     if dense:
         fp.dense_prefill(prob, att, q, k, v, bufs.out, bufs.lse)
     else:
-        fp.run_prefill(prob, bufs, q, k, v, alpha, wl.sel_scale, msl, 0.0, mean_correction, **(forced or {}),
+        fp.run_prefill(prob, bufs, q, k, v, alpha, wl.sel_scale, msl, sm_scale, mean_correction, **(forced or {}),
                        num_splits=num_splits, fused_stage1=fused_stage1)
     torch.cuda.synchronize()
     res = dict(out=bufs.out.float().cpu().numpy(), lse=bufs.lse.cpu().numpy())

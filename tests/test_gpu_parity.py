@@ -17,12 +17,13 @@ import oracle
 pytestmark = pytest.mark.gpu
 
 
-def _check_full(wl, alpha=None, mean_correction=True, paged=None, min_sparse_len=None, forced=None, num_splits=0):
+def _check_full(wl, alpha=None, mean_correction=True, paged=None, min_sparse_len=None, forced=None, num_splits=0,
+                sm_scale=0.0):
     print(f"[parity] {wl.name} L={wl.seqlens} Lk={wl.key_seqlens} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} B={wl.block_size} "
           f"dtype={wl.dtype} alpha={alpha if alpha is not None else wl.alpha} mc={mean_correction} "
           f"paged={paged if paged is not None else wl.paged} forced={forced}", flush=True)
     gpu = run_gpu(wl, alpha, mean_correction, paged, min_sparse_len=min_sparse_len, forced=forced,
-                  num_splits=num_splits)
+                  num_splits=num_splits, sm_scale=sm_scale)
     orc = run_oracle(wl, alpha, mean_correction, do_attend=False, paged=paged, min_sparse_len=min_sparse_len,
                      forced=forced)
     compare_pooled(gpu, orc)
@@ -40,7 +41,7 @@ def _check_full(wl, alpha=None, mean_correction=True, paged=None, min_sparse_len
         ks, ke = cuk[r], cuk[r + 1]
         a, b = orc.kblk_off[r], orc.kblk_off[r + 1]
         o, l = oracle.attend(Q[s:e], K[ks:ke], V[ks:ke], orc.kbar[:, a:b], orc.vbar[:, a:b], sets[r],
-                             wl.block_size, G, 1.0 / math.sqrt(wl.head_dim), mean_correction,
+                             wl.block_size, G, sm_scale or 1.0 / math.sqrt(wl.head_dim), mean_correction,
                              q_off=(ke - ks) - (e - s))
         O[s:e], LSE[:, s:e] = o, l
     o_err, l_rel, l_abs = compare_outputs(gpu["out"], gpu["lse"], O, LSE, O_TOL[wl.dtype])
@@ -71,6 +72,16 @@ def test_gqa1_block128():
 def test_mean_correction_off():
     wl = synth.make_workload("llama_32k", L=2200, Hq=8, Hkv=2, n_planted=5)
     _check_full(wl, mean_correction=False)
+
+
+@pytest.mark.parametrize("sm_scale,fp8,mc", [(0.05, False, True), (0.2, False, True), (0.15, True, False)])
+def test_softmax_scale_and_fp8_without_correction(sm_scale, fp8, mc):
+    """A caller's softmax scale instead of 1 / sqrt(d) (on exact and pooled
+    logits alike; the pooled logit's ln n_J does not scale), and FP8 inputs
+    with the mean correction off. Ragged GQA-4 batch."""
+    wl = synth.make_workload("qwen4b_varlen_paged", lengths=[1300, 500], Hq=8, Hkv=2, min_sparse_len=0,
+                             n_planted=3, fp8=fp8, page_size=0)
+    _check_full(wl, mean_correction=mc, sm_scale=sm_scale)
 
 
 def test_fp8_gqa8():
