@@ -109,6 +109,17 @@ def test_gqa_ratios_that_leave_waves_without_rows(Hq, Hkv, B, fp8, splits):
     _check_full(wl, num_splits=splits)
 
 
+@pytest.mark.parametrize("Hq,Hkv,B,fp8", [
+    (32, 2, 128, False),   # G = 16: 2048 packed rows, 8 sub-tiles per row
+    (32, 1, 128, False),   # one KV head (multi-query), G = 32: 16 sub-tiles, 32 heads pooled per group
+    (32, 1, 64, True),     # multi-query with 64-key blocks and FP8
+])
+def test_large_gqa_ratios(Hq, Hkv, B, fp8):
+    wl = synth.make_workload("qwen4b_varlen_paged", lengths=[1000, 380], Hq=Hq, Hkv=Hkv, min_sparse_len=0,
+                             n_planted=2, B=B, fp8=fp8, page_size=0 if fp8 else 64)
+    _check_full(wl)
+
+
 @pytest.mark.parametrize("page_size", [0, 64, 6])
 def test_fp8_block64_varlen(page_size):
     # FP8 products with 64-key blocks (one FP8 K DMA instruction per wave) on
