@@ -113,8 +113,10 @@ def test_gqa_ratios_that_leave_waves_without_rows(Hq, Hkv, B, fp8, splits):
     (32, 2, 128, False),   # G = 16: 2048 packed rows, 8 sub-tiles per row
     (32, 1, 128, False),   # one KV head (multi-query), G = 32: 16 sub-tiles, 32 heads pooled per group
     (32, 1, 64, True),     # multi-query with 64-key blocks and FP8
+    (32, 32, 128, False),  # multi-head, 32 KV heads (the KV head of a work slot rotates every 32 query blocks)
+    (48, 16, 128, True),   # 16 KV heads, G = 3, FP8
 ])
-def test_large_gqa_ratios(Hq, Hkv, B, fp8):
+def test_head_counts(Hq, Hkv, B, fp8):
     wl = synth.make_workload("qwen4b_varlen_paged", lengths=[1000, 380], Hq=Hq, Hkv=Hkv, min_sparse_len=0,
                              n_planted=2, B=B, fp8=fp8, page_size=0 if fp8 else 64)
     _check_full(wl)
