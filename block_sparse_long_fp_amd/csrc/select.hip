@@ -221,7 +221,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
     auto units_of = [&](int b) { return max(cb_hi(b) - cb_lo(b), 0); };
     int U = 0;
     for (int b = 0; b < nrb; ++b) U += units_of(b);
-    const int u_begin = (int)((int64_t)U * w / kSelWaves), u_end = (int)((int64_t)U * (w + 1) / kSelWaves);
+    // Contiguous runs of units per wave; with no more units than waves, unit
+    // k goes to wave 15 - k, so consecutive units run on different SIMDs
+    // (wave w is on SIMD w % 4) rather than queueing on one matrix core, and
+    // wave 0, which decodes the tile, gets one last.
+    const int wr = kSelWaves - 1 - w;
+    const int u_begin = U <= kSelWaves ? min(wr, U) : (int)((int64_t)U * w / kSelWaves);
+    const int u_end = U <= kSelWaves ? min(wr + 1, U) : (int)((int64_t)U * (w + 1) / kSelWaves);
     if (u_begin < u_end) {
       // Buffer loads, no branches: lanes past the tile's rows or the
       // request's key blocks read zeros (the descriptors' record bounds).

@@ -78,14 +78,14 @@ def test_index_shape_and_workspace():
     mid = _prob(cu_seqlens=[0, 32768])
     assert fp.select_workspace_bytes(mid) == 256 + 64 * 8
     # a 2048-token chunk after 129024 tokens: one 16-row block per KV head,
-    # 64 units each, so each tile's 1024 key blocks go to 4 workgroups of
-    # 256: the look-back words plus one arrival count per tile, each part's
-    # row maxima (320 int32) and each tile's scores (two widest blocks:
-    # 2 x 16 x (1024 + 3) floats)
+    # 64 units each, so each tile's 1024 key blocks go to 16 workgroups of
+    # 64 (4 units, one per SIMD): the look-back words plus one arrival count
+    # per tile, each part's row maxima (320 int32) and each tile's scores
+    # (two widest blocks: 2 x 16 x (1024 + 3) floats)
     def a256(x):
         return (x + 255) // 256 * 256
     chunk = _prob(cu_seqlens=[0, 2048], cu_seqlens_k=[0, 131072])
-    tiles, parts = 8, 4
+    tiles, parts = 8, 16
     assert fp.select_workspace_bytes(chunk) == (256 + a256(2 * tiles * 8) + a256(tiles * parts * 320 * 4)
                                               + a256(tiles * 2 * 16 * 1027 * 4))
 
