@@ -259,6 +259,21 @@ def test_batch_of_the_most_requests(num_splits):
     _check_full(wl, num_splits=num_splits)
 
 
+@pytest.mark.parametrize("num_splits", [1, 3])
+def test_chunk_of_the_most_requests(num_splits):
+    """A chunked-prefill call over 128 requests: each request's queries are
+    its positions 128 .. 383 (fewer where it ends sooner) against every key
+    before them, so every request's first query block is key block 2 and the
+    chunks end raggedly. Paged K / V, 64-key blocks."""
+    rng = np.random.default_rng(129)
+    lengths = [int(x) for x in rng.integers(150, 900, 128)]
+    wl = synth.make_workload("qwen4b_varlen_paged", lengths=lengths, Hq=4, Hkv=1, B=64, min_sparse_len=0,
+                             n_planted=0, page_size=16)
+    batch = synth.chunk_of(wl, 128, 256)
+    assert len(batch.seqlens) == 128 and batch.cu_seqlens_k is not None
+    _check_full(batch, num_splits=num_splits)
+
+
 @pytest.mark.parametrize("forced", [dict(sink=2, window=4, last_n=8), dict(sink=1, window=0, last_n=0),
                                     dict(sink=0, window=2, last_n=3)])
 def test_forced_keeps_sink_window_last_n(forced):
