@@ -680,7 +680,7 @@ const char* fp_status_string(fp_status s) {
     case FP_ERR_CAPACITY: return "FP_ERR_CAPACITY: col_idx capacity below worst-case nnz";
     case FP_ERR_WORKSPACE: return "FP_ERR_WORKSPACE: workspace missing or too small";
     case FP_ERR_ARG: return "FP_ERR_ARG: bad scalar argument";
-    case FP_ERR_UNSUPPORTED: return "FP_ERR_UNSUPPORTED: outside what this build implements";
+    case FP_ERR_UNSUPPORTED: return "FP_ERR_UNSUPPORTED: outside what this library implements";
     case FP_ERR_HIP: return "FP_ERR_HIP: HIP runtime error";
     default: return "unknown fp_status";
   }

@@ -96,7 +96,7 @@ enum {
   FP_ERR_CAPACITY = 7,    /* col_idx capacity below the worst-case nnz           */
   FP_ERR_WORKSPACE = 8,   /* workspace NULL or below fp_*_workspace_bytes      */
   FP_ERR_ARG = 9,         /* bad scalar argument (NaN alpha, sel_scale, sm_scale) */
-  FP_ERR_UNSUPPORTED = 10,/* valid request outside this build (head_dim != 128,  */
+  FP_ERR_UNSUPPORTED = 10,/* valid request outside this library (head_dim != 128, */
                           /* more than FP_MAX_SEQS requests, too many blocks)    */
   FP_ERR_HIP = 11         /* a HIP runtime call or kernel launch failed          */
 };
@@ -108,7 +108,7 @@ enum { FP_BF16 = 0, FP_FP8_E4M3 = 1 };
 /* K/V storage. */
 enum { FP_KV_CONTIGUOUS = 0, FP_KV_PAGED = 1 };
 
-/* Limits of this build. */
+/* Limits of this library. */
 #define FP_MAX_SEQS 128               /* requests per call                      */
 #define FP_MAX_BLOCKS_PER_SEQ 16384   /* NBk_r; 2M tokens at B = 128            */
 #define FP_HEAD_DIM 128
