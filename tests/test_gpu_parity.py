@@ -575,6 +575,53 @@ def test_rows_with_more_pruned_blocks_than_the_list():
           f"LSE_rel={l_rel:.2e}", flush=True)
 
 
+_FP8_LONG = {}
+
+
+@pytest.mark.parametrize("L,alpha,num_splits", [(70000, 0.04, 1), (140000, 0.5, 1), (140000, 0.5, 3)])
+def test_fp8_rows_beyond_the_column_cache_and_the_pruned_list(L, alpha, num_splits):
+    """The two long-row branches of the attention kernel with FP8 inputs:
+    70000 tokens at alpha = 0.04 give rows of more than 1025 kept blocks (CSR
+    columns past the LDS cache read from global memory); 140000 tokens at
+    alpha = 0.5 give rows of more than 2048 pruned blocks (correction chunks
+    over consecutive key blocks, the selected ones masked), unsplit and split.
+    One KV head, 4 query heads, 64-token blocks."""
+    import math
+    if L not in _FP8_LONG:  # FP8 encoding of 140000 tokens takes about 17 s on the host
+        w = synth.make_workload("llama_32k", L=L, Hq=4, Hkv=1, B=64, n_planted=30, fp8=True)
+        _FP8_LONG.clear()
+        _FP8_LONG[L] = (w, host_values(w))
+    wl, (Q, K, V) = _FP8_LONG[L]
+    assert wl.dtype == "fp8"
+    print(f"[parity] fp8 long rows L={L} B=64 alpha={alpha} splits={num_splits}", flush=True)
+    gpu = run_gpu(wl, alpha, num_splits=num_splits)
+    orc = run_oracle(wl, alpha, do_attend=False, Qkv=(Q, K, V))
+    compare_pooled(gpu, orc)
+    compare_csr(gpu, orc)
+    counts = np.diff(gpu["row_ptr"])
+    NB = len(counts)
+    pruned = np.arange(NB) - (counts - 1)
+    if L == 70000:
+        assert NB == 1094 and (counts > 1025).sum() >= 20
+        rows = {NB - 1, int(np.argmax(counts)), int(np.nonzero(counts > 1025)[0][0])}
+    else:
+        assert NB == 2188 and (pruned > 2048).sum() >= 20 and (pruned <= 2048).sum() >= 20
+        rows = {NB - 1, int(np.nonzero(pruned > 2048)[0][0]), int(np.nonzero(pruned <= 2048)[0][-1]),
+                int(np.argmax(pruned))}
+    rows = sorted(rows)
+    sets = sets_from_csr(gpu["row_ptr"], gpu["col_idx"], orc.blk_off, 1)[0][0]
+    O = np.full_like(Q, np.nan)
+    LSE = np.full((4, Q.shape[0]), np.nan)
+    for I in rows:
+        o, l = oracle.attend_row(Q, K, V, orc.kbar, orc.vbar, np.asarray(sets[I]), 0, I, 64, 4,
+                                 1.0 / math.sqrt(128), True)
+        O[I * 64:I * 64 + o.shape[0]] = o
+        LSE[:, I * 64:I * 64 + o.shape[0]] = l.T
+    o_err, l_rel, l_abs = compare_outputs(gpu["out"], gpu["lse"], O, LSE, O_TOL["fp8"])
+    print(f"[parity] ok: rows {rows} kept {[int(counts[I]) for I in rows]} pruned "
+          f"{[int(pruned[I]) for I in rows]} O_err={o_err:.2e} LSE_rel={l_rel:.2e}", flush=True)
+
+
 # ---------------------------------------------------------------- fused Stage 1
 
 def test_stage1_equals_separate_calls_and_reuses_its_workspace():
