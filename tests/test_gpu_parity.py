@@ -575,6 +575,31 @@ def test_rows_with_more_pruned_blocks_than_the_list():
           f"LSE_rel={l_rel:.2e}", flush=True)
 
 
+@pytest.mark.parametrize("page_size,L,alpha", [(16, 70000, 0.04), (6, 140000, 0.5)])
+def test_paged_long_rows_equal_contiguous_bitwise(page_size, L, alpha):
+    """The long-row branches (CSR columns past the LDS cache at 70000 tokens
+    and alpha = 0.04; correction chunks over consecutive key blocks at 140000
+    tokens and alpha = 0.5) through the paged kernels, with page sizes that
+    are (16) and are not (6) multiples of 4: every output equals the
+    contiguous layout's bit for bit, and the CSR the oracle's."""
+    wl = synth.make_workload("llama_32k", L=L, Hq=4, Hkv=1, B=64, n_planted=30, page_size=page_size)
+    print(f"[parity] paged long rows L={L} page_size={page_size} alpha={alpha}", flush=True)
+    a = run_gpu(wl, alpha, paged=True)
+    b = run_gpu(wl, alpha, paged=False)
+    for key in ("q_bar", "k_bar", "v_bar", "row_ptr", "col_idx", "out", "lse"):
+        assert np.array_equal(a[key], b[key]), key
+    orc = run_oracle(wl, alpha, do_attend=False, paged=False)
+    compare_pooled(a, orc)
+    compare_csr(a, orc)
+    counts = np.diff(a["row_ptr"])
+    pruned = np.arange(len(counts)) - (counts - 1)
+    if L == 70000:
+        assert (counts > 1025).sum() >= 20
+    else:
+        assert (pruned > 2048).sum() >= 20
+    print(f"[parity] ok: max kept {int(counts.max())} max pruned {int(pruned.max())}", flush=True)
+
+
 _FP8_LONG = {}
 
 
