@@ -105,6 +105,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--dense-reps", type=int, default=3, help="timed repetitions of the dense comparator")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="without the dense comparator: untimed steps for this long before the warm-up, "
+                         "so the engine clock has settled")
     ap.add_argument("--cpu-rows", type=int, default=96,
                     help="attention rows the CPU baseline computes (96: about 10 s of oracle work at 128K)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -403,8 +406,10 @@ def main():
     # MiB MALL, so no step starts with the previous step's data in cache; it
     # runs outside the events. A read leaves clean lines behind: the step does
     # not pay for writing back someone else's dirty lines (a 512 MiB write
-    # before the step made the first kernel, pooling, 20 % slower).
-    flush_buf = torch.ones(128 << 20, dtype=torch.int32, device=dev)
+    # before the step made the first kernel, pooling, 20 % slower). The buffer
+    # is fp32 so that the sum reads it in place (an int32 sum first widens
+    # the whole buffer to int64, a 1 GiB write).
+    flush_buf = torch.ones(128 << 20, dtype=torch.float32, device=dev)
 
     def evict():
         flush_buf.sum()
@@ -424,7 +429,8 @@ def main():
     # The dense comparator runs first (its repetitions also bring the engine
     # clock up to its sustained level: a sparse step that starts from an idle
     # GPU measured 10.9 ms against 9.3 once the clock had settled, over the
-    # first four steps). Warm-up steps then run exactly as the timed ones.
+    # first four steps); without it, untimed steps run for --settle-ms.
+    # Warm-up steps then run exactly as the timed ones.
     dense = None
     if not args.no_dense:
         dws = fp.attn_workspace_bytes(prob, False, att)
@@ -441,6 +447,12 @@ def main():
             dense_ms.append(e0.elapsed_time(e1))
         dense = timing_stats(dense_ms)
         dense["reps"] = len(dense_ms)
+    else:
+        t_end = time.perf_counter() + args.settle_ms * 1e-3
+        while time.perf_counter() < t_end:
+            evict()
+            step()
+            torch.cuda.synchronize()
     for _ in range(args.warmup):
         evict()
         step()
