@@ -106,8 +106,8 @@ def parse():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--dense-reps", type=int, default=3, help="timed repetitions of the dense comparator")
     ap.add_argument("--settle-ms", type=float, default=300.0,
-                    help="without the dense comparator: untimed steps for this long before the warm-up, "
-                         "so the engine clock has settled")
+                    help="without the dense comparator (and in --chunk mode): untimed steps for this long "
+                         "before the warm-up, so the engine clock has settled")
     ap.add_argument("--cpu-rows", type=int, default=96,
                     help="attention rows the CPU baseline computes (96: about 10 s of oracle work at 128K)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -301,6 +301,11 @@ def run_chunked(args, wl, fp, torch, q, k, v, descales):
             if ev is not None:
                 ev[2].record()
 
+    # Untimed passes for --settle-ms first, so the engine clock has settled.
+    t_end = time.perf_counter() + args.settle_ms * 1e-3
+    while time.perf_counter() < t_end:
+        step()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
