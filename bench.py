@@ -106,8 +106,8 @@ def parse():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--dense-reps", type=int, default=3, help="timed repetitions of the dense comparator")
     ap.add_argument("--settle-ms", type=float, default=300.0,
-                    help="without the dense comparator (and in --chunk mode): untimed steps for this long "
-                         "before the warm-up, so the engine clock has settled")
+                    help="untimed steps for this long before the dense comparator and the warm-up, so the "
+                         "engine clock has settled")
     ap.add_argument("--cpu-rows", type=int, default=96,
                     help="attention rows the CPU baseline computes (96: about 10 s of oracle work at 128K)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -431,33 +431,16 @@ def main():
         if ev is not None:
             ev[2].record()
 
-    # The dense comparator runs first (its repetitions also bring the engine
-    # clock up to its sustained level: a sparse step that starts from an idle
-    # GPU measured 10.9 ms against 9.3 once the clock had settled, over the
-    # first four steps); without it, untimed steps run for --settle-ms.
-    # Warm-up steps then run exactly as the timed ones.
-    dense = None
-    if not args.no_dense:
-        dws = fp.attn_workspace_bytes(prob, False, att)
-        dws = torch.empty(dws, dtype=torch.uint8, device="cuda:0") if dws else None
-        fp.dense_prefill(prob, att, q, k, v, bufs.out, bufs.lse, dws)   # warm-up
-        dense_ms = []
-        for i in range(args.dense_reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            evict()
-            e0.record()
-            fp.dense_prefill(prob, att, q, k, v, bufs.out, bufs.lse, dws)
-            e1.record()
-            torch.cuda.synchronize()
-            dense_ms.append(e0.elapsed_time(e1))
-        dense = timing_stats(dense_ms)
-        dense["reps"] = len(dense_ms)
-    else:
-        t_end = time.perf_counter() + args.settle_ms * 1e-3
-        while time.perf_counter() < t_end:
-            evict()
-            step()
-            torch.cuda.synchronize()
+    # Untimed steps for --settle-ms first, so the engine clock has settled (a
+    # sparse step that starts from an idle GPU measured 10.9 ms against 9.3
+    # once the clock had settled, over the first four steps); warm-up steps
+    # then run exactly as the timed ones. The dense comparator runs after the
+    # timed steps.
+    t_end = time.perf_counter() + args.settle_ms * 1e-3
+    while time.perf_counter() < t_end:
+        evict()
+        step()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         evict()
         step()
@@ -498,6 +481,23 @@ def main():
     dense_eq = wl.dense_equiv_flops()
     peak = PEAK_TFLOPS[wl.dtype]
     achieved = flops / (att_avg * 1e-3) / 1e12
+
+    dense = None
+    if not args.no_dense:
+        dws = fp.attn_workspace_bytes(prob, False, att)
+        dws = torch.empty(dws, dtype=torch.uint8, device="cuda:0") if dws else None
+        fp.dense_prefill(prob, att, q, k, v, bufs.out, bufs.lse, dws)   # warm-up
+        dense_ms = []
+        for i in range(args.dense_reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            evict()
+            e0.record()
+            fp.dense_prefill(prob, att, q, k, v, bufs.out, bufs.lse, dws)
+            e1.record()
+            torch.cuda.synchronize()
+            dense_ms.append(e0.elapsed_time(e1))
+        dense = timing_stats(dense_ms)
+        dense["reps"] = len(dense_ms)
 
     rec = {
         "metric": METRIC,
