@@ -90,6 +90,8 @@ def parse():
                     help="override the sequence length of a single-request workload (same recipe and seed)")
     ap.add_argument("--alpha", type=float, default=None)
     ap.add_argument("--block-size", type=int, default=None, help="override the workload's block size (64 or 128)")
+    ap.add_argument("--page-size", type=int, default=None,
+                    help="override the KV page size in tokens (0: contiguous K / V)")
     ap.add_argument("--kv-heads", type=int, default=None,
                     help="one GPU's share under head sharding: this many KV heads (same GQA ratio)")
     ap.add_argument("--sink", type=int, default=0, help="forced keep: first key blocks of each request")
@@ -381,6 +383,8 @@ def main():
         base = synth.CONFIGS[args.workload]
         over["Hkv"] = args.kv_heads
         over["Hq"] = args.kv_heads * (base["Hq"] // base["Hkv"])
+    if args.page_size is not None:
+        over["page_size"] = args.page_size
     if args.seq_len is not None:
         over["L"] = args.seq_len
         over["n_planted"] = max(1, args.seq_len // 2048)  # the recipe's one planted block per 2048 tokens
