@@ -1117,8 +1117,10 @@ struct ItemLoop {
 };
 
 // F8: Q and K are E4M3 codes (QK^T on the FP8 matrix cores), V a bf16 copy
-// of its codes.
-template <int BLK, int PAGED, bool SPLIT, bool F8>
+// of its codes. DENSE only names the instantiation the dense comparator
+// (p.dense) launches, so that a kernel trace keeps its dispatches apart from
+// the sparse launches'; the code does not read it.
+template <int BLK, int PAGED, bool SPLIT, bool F8, bool DENSE>
 __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   // Two tile sets, each its own LDS object, so the compiler can tell the
   // in-flight DMA into one set from the operand reads of the other.
@@ -1443,17 +1445,25 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnParams p) {
   }
 }
 
+template <int BLK, int PAGED, bool SPLIT, bool F8>
+void launch_attn_v(const AttnParams& p, dim3 grid, hipStream_t stream) {
+  if (p.dense)
+    hipLaunchKernelGGL((attn_kernel<BLK, PAGED, SPLIT, F8, true>), grid, dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_kernel<BLK, PAGED, SPLIT, F8, false>), grid, dim3(kThreads), 0, stream, p);
+}
+
 template <int BLK, bool SPLIT>
 void launch_attn_t(const AttnParams& p, dim3 grid, hipStream_t stream) {
   if (p.fp8) {
-    if (!p.kv.paged) hipLaunchKernelGGL((attn_kernel<BLK, kContig, SPLIT, true>), grid, dim3(kThreads), 0, stream, p);
-    else hipLaunchKernelGGL((attn_kernel<BLK, kPagedAny, SPLIT, true>), grid, dim3(kThreads), 0, stream, p);
+    if (!p.kv.paged) launch_attn_v<BLK, kContig, SPLIT, true>(p, grid, stream);
+    else launch_attn_v<BLK, kPagedAny, SPLIT, true>(p, grid, stream);
   } else if (!p.kv.paged) {
-    hipLaunchKernelGGL((attn_kernel<BLK, kContig, SPLIT, false>), grid, dim3(kThreads), 0, stream, p);
+    launch_attn_v<BLK, kContig, SPLIT, false>(p, grid, stream);
   } else if (p.kv.page_size % 4 == 0) {
-    hipLaunchKernelGGL((attn_kernel<BLK, kPaged4, SPLIT, false>), grid, dim3(kThreads), 0, stream, p);
+    launch_attn_v<BLK, kPaged4, SPLIT, false>(p, grid, stream);
   } else {
-    hipLaunchKernelGGL((attn_kernel<BLK, kPagedAny, SPLIT, false>), grid, dim3(kThreads), 0, stream, p);
+    launch_attn_v<BLK, kPagedAny, SPLIT, false>(p, grid, stream);
   }
 }
 
